@@ -1,0 +1,148 @@
+/*
+ * mxfp4.h -- C ABI of libmxfp4: microscaling FP4 quantization and the
+ * block-scaled FP4 GEMM on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes, and where the method comes from (web pages on
+ * microscaling FP4, cited by title and section):
+ *   - "FP4 All the Way: Fully Quantized Training of LLMs", abstract:
+ *     E2M1 elements; NVFP4 = blocks of 16 E2M1 values sharing an E4M3
+ *     scale; round-to-nearest on the forward pass and stochastic rounding on
+ *     the backward and update passes; weights, activations and gradients
+ *     are all quantized, so all three GEMMs of a linear layer run in FP4.
+ *   - "Oscillation-Reduced MXFP4 Training for Vision Transformers", abstract:
+ *     the MX format quantizes per group with one shared scale per group.
+ *   - "Bridging the Gap Between Promise and Performance for Microscaling FP4
+ *     Quantization", abstract (and the digest of it, step 3): MXFP4 scales
+ *     are powers of two; block-wise (block-diagonal) Hadamard rotations are
+ *     fused into the weights offline and applied online to activations;
+ *     FP4 GEMM kernels consume the packed operands.
+ *
+ * Conventions shared by every entry point
+ *   - Formats: MXFP4 = blocks of 32 E2M1 codes + one E8M0 byte (2^(b-127));
+ *     NVFP4 = blocks of 16 E2M1 codes + one E4M3 byte, plus one FP32 tensor
+ *     scale.
+ *   - A quantized matrix is contraction-major: [rows, k], row-major.
+ *     codes: rows * k/2 bytes, element k of a row in bits 4*(k&1)+3..4*(k&1)
+ *     of byte k/2 (even k in the low nibble).  scales: rows * k/bs bytes,
+ *     row-major.  NVFP4 tensor_scale: one float.
+ *   - Memory: every pointer argument marked "device" is device memory owned
+ *     by the caller; the library never allocates, frees or synchronizes, and
+ *     keeps no state between calls (all entry points are reentrant).
+ *   - Streams: work is enqueued on the caller's stream and is asynchronous;
+ *     a fault during execution surfaces at the caller's next synchronization.
+ *   - Errors: every entry point returns an mxfp4_status.  Arguments are
+ *     checked before anything is launched; a rejected call has no effect.
+ *     MXFP4_ERR_HIP reports a failed kernel launch (hipGetLastError).
+ */
+#ifndef MXFP4_H
+#define MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MXFP4_OK = 0,
+    MXFP4_ERR_INVALID_ARG = -1,       /* null pointer, bad enum, negative size, ld too small */
+    MXFP4_ERR_UNSUPPORTED_SHAPE = -2, /* contraction length not a multiple of the needed block */
+    MXFP4_ERR_FORMAT_MISMATCH = -3,   /* GEMM operands differ in fmt, k or hadamard */
+    MXFP4_ERR_WORKSPACE = -4,         /* workspace missing or smaller than required */
+    MXFP4_ERR_HIP = -5                /* a HIP launch failed */
+} mxfp4_status;
+
+typedef enum { MXFP4_FMT_MX = 0, MXFP4_FMT_NV = 1 } mxfp4_fmt;
+typedef enum { MXFP4_RTN = 0, MXFP4_SR = 1 } mxfp4_rounding;
+
+/* A contraction-major quantized matrix [rows, k] (layout above). */
+typedef struct {
+    int32_t fmt;          /* mxfp4_fmt */
+    int32_t hadamard;     /* 1 if the rows were rotated by the 32x32 block Hadamard */
+    int64_t rows;
+    int64_t k;            /* contraction length */
+    uint8_t *codes;       /* device, rows * k/2 bytes */
+    uint8_t *scales;      /* device, rows * k/bs bytes */
+    float *tensor_scale;  /* device, 1 float for NVFP4; ignored (may be NULL) for MXFP4 */
+} mxfp4_tensor;
+
+/* Byte sizes of the codes and scales of a [rows, k] quantized matrix.
+ * Fails with UNSUPPORTED_SHAPE if k is not a multiple of the block size
+ * (32 for MXFP4, 16 for NVFP4). */
+mxfp4_status mxfp4_tensor_bytes(int fmt, int64_t rows, int64_t k,
+                                size_t *codes_bytes, size_t *scales_bytes);
+
+/* Workspace needed by mxfp4_quantize for an [R, C] input (0 for MXFP4;
+ * NVFP4 needs room for the per-workgroup partial maxima of the tensor-amax
+ * pass).  The workspace holds no state between calls. */
+mxfp4_status mxfp4_quantize_workspace_bytes(int fmt, int64_t R, int64_t C, int axis,
+                                            size_t *bytes);
+
+/* Quantize a bf16 matrix X [R, C] (device, row-major, leading dimension
+ * ldx >= C, elements given as raw bf16 bit patterns).
+ *
+ * Steps (sources as in the file header):
+ *   1. (hadamard = 1) rotate each aligned block of 32 along the contraction
+ *      axis by the normalised Sylvester Hadamard matrix H/sqrt(32), in FP32
+ *      -- "block-wise Hadamard transforms" of the MR-GPTQ paper's abstract;
+ *   2. (NVFP4) tensor scale s_t = max|y| / (6 * 448) over the whole tensor;
+ *   3. per block absmax and shared scale: MXFP4 E8M0 2^e with e the smallest
+ *      integer such that 6 * 2^e >= absmax; NVFP4 E4M3 = the smallest E4M3
+ *      value >= absmax / (6 * s_t);
+ *   4. scaled element rounded to E2M1: round-to-nearest-even (rounding =
+ *      MXFP4_RTN, forward pass) or stochastic rounding with 16 bits of a
+ *      Philox4x32-10 stream keyed by seed (rounding = MXFP4_SR, backward and
+ *      update passes) -- "FP4 All the Way", abstract;
+ *   5. nibble-pack codes and write the scale bytes contiguously.
+ *
+ * axis = 1: contraction along C; out is [R, C] (rows = R, k = C).
+ * axis = 0: contraction along R; out is the transpose [C, R] (rows = C,
+ *           k = R).  This is how the backward GEMMs get each operand
+ *           quantized along its own contraction axis.
+ * out: caller-filled descriptor; out->rows, out->k and out->fmt must match the
+ *      call, and out->hadamard is compared with hadamard; codes/scales (and
+ *      tensor_scale for NVFP4) must be non-NULL device buffers of the sizes
+ *      mxfp4_tensor_bytes reports.
+ * k must be a multiple of the block size, and of 32 when hadamard = 1.
+ * Blocks holding a NaN or infinity get the format's NaN scale byte (0xFF for
+ * E8M0, 0x7F for E4M3) and all-zero codes.
+ * workspace: device, at least mxfp4_quantize_workspace_bytes (may be NULL
+ * when that is 0). */
+mxfp4_status mxfp4_quantize(const uint16_t *x, int64_t R, int64_t C, int64_t ldx,
+                            int fmt, int rounding, int hadamard, int axis, uint64_t seed,
+                            mxfp4_tensor *out, void *workspace, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* Dequantize q into y [q->rows, q->k] FP32 (device, leading dimension ldy >=
+ * q->k): value = E2M1(code) * scale (NVFP4: * tensor_scale).  A rotated
+ * tensor stays in the rotated domain. */
+mxfp4_status mxfp4_dequantize(const mxfp4_tensor *q, float *y, int64_t ldy,
+                              hipStream_t stream);
+
+/* Workspace needed by mxfp4_gemm for these operands (split-K partial sums
+ * for long contractions; 0 otherwise). */
+mxfp4_status mxfp4_gemm_workspace_bytes(const mxfp4_tensor *A, const mxfp4_tensor *B,
+                                        size_t *bytes);
+
+/* C[M, N] = A * B^T, FP32, over the dequantized operands: A is [M, k], B is
+ * [N, k], both quantized along k (the three GEMMs of a linear layer -- XW^T,
+ * dY.W and dY^T.X -- are all this call on operands quantized with the axis
+ * that puts their contraction last).  MXFP4 runs on the CDNA4 block-scaled
+ * FP4 matrix cores; NVFP4 dequantizes exactly to bf16 in registers and
+ * applies both tensor scales in the epilogue.
+ * C: device, row-major, ldc >= N.  k must be a multiple of 128 (MXFP4) or
+ * 64 (NVFP4); fmt, k and hadamard of A and B must agree (FORMAT_MISMATCH).
+ * workspace: device, at least mxfp4_gemm_workspace_bytes (NULL if 0). */
+mxfp4_status mxfp4_gemm(const mxfp4_tensor *A, const mxfp4_tensor *B, float *C, int64_t ldc,
+                        void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* A static, human-readable description of a status code. */
+const char *mxfp4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_H */

@@ -1,0 +1,201 @@
+"""CPU oracle for microscaling FP4 quantization and the block-scaled FP4 GEMM.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  The HIP library never imports,
+links or calls it, and it shares no code with the HIP library.
+
+The arithmetic lives in ``mxfp4_oracle.c`` (plain scalar C, binary32 for the
+steps that decide codes, binary64 for the GEMM); this module only builds it
+and marshals numpy arrays through ctypes.  See the C file's header for the
+pages each step follows and the readings taken where the pages are silent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mxfp4_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libmxfp4_oracle.so")
+
+FMT = {"mx": 0, "nv": 1}
+ROUNDING = {"rtn": 0, "sr": 1}
+BLOCK = {"mx": 32, "nv": 16}
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle (always; a few seconds)."""
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+           "-fPIC", "-shared", "-std=c11", "-Wall", "-o", _LIB_PATH + ".tmp", _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, i32, u64, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p
+    lib.mxo_e2m1_value.restype = ctypes.c_double
+    lib.mxo_e2m1_value.argtypes = [i32]
+    lib.mxo_e8m0_value.restype = ctypes.c_double
+    lib.mxo_e8m0_value.argtypes = [i32]
+    lib.mxo_e4m3_value.restype = ctypes.c_double
+    lib.mxo_e4m3_value.argtypes = [i32]
+    lib.mxo_e4m3_round_up.restype = i32
+    lib.mxo_e4m3_round_up.argtypes = [ctypes.c_float]
+    lib.mxo_mx_scale_exponent.restype = i32
+    lib.mxo_mx_scale_exponent.argtypes = [ctypes.c_float]
+    lib.mxo_rtn_code.restype = i32
+    lib.mxo_rtn_code.argtypes = [ctypes.c_double]
+    lib.mxo_sr_code.restype = i32
+    lib.mxo_sr_code.argtypes = [ctypes.c_double, ctypes.c_uint32]
+    lib.mxo_philox4x32_10.restype = None
+    lib.mxo_philox4x32_10.argtypes = [vp, vp, vp]
+    lib.mxo_rnd16.restype = ctypes.c_uint32
+    lib.mxo_rnd16.argtypes = [u64, u64, i32]
+    lib.mxo_hadamard_scale.restype = ctypes.c_float
+    lib.mxo_hadamard_scale.argtypes = []
+    lib.mxo_fwht32.restype = None
+    lib.mxo_fwht32.argtypes = [vp]
+    lib.mxo_nv_tensor_scale.restype = ctypes.c_float
+    lib.mxo_nv_tensor_scale.argtypes = [ctypes.c_float]
+    lib.mxo_quantize.restype = i32
+    lib.mxo_quantize.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, u64, vp, vp, vp]
+    lib.mxo_dequantize.restype = i32
+    lib.mxo_dequantize.argtypes = [i32, i64, i64, vp, vp, vp, vp, i64]
+    lib.mxo_gemm.restype = i32
+    lib.mxo_gemm.argtypes = [i32, i64, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64, vp, vp]
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ---- scalar pieces (exposed for the pins) ----------------------------------
+def e2m1_value(code: int) -> float:
+    return _load().mxo_e2m1_value(int(code))
+
+
+def e8m0_value(byte: int) -> float:
+    return _load().mxo_e8m0_value(int(byte))
+
+
+def e4m3_value(byte: int) -> float:
+    return _load().mxo_e4m3_value(int(byte))
+
+
+def e4m3_round_up(r: float) -> int:
+    return _load().mxo_e4m3_round_up(float(r))
+
+
+def mx_scale_exponent(amax: float) -> int:
+    return _load().mxo_mx_scale_exponent(float(amax))
+
+
+def rtn_code(xs: float) -> int:
+    return _load().mxo_rtn_code(float(xs))
+
+
+def sr_code(xs: float, rnd16: int) -> int:
+    return _load().mxo_sr_code(float(xs), int(rnd16))
+
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    c = np.ascontiguousarray(np.asarray(ctr, dtype=np.uint32))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint32))
+    out = np.zeros(4, dtype=np.uint32)
+    _load().mxo_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def rnd16(seed: int, L: int, axis: int) -> int:
+    return _load().mxo_rnd16(int(seed), int(L), int(axis))
+
+
+def hadamard_scale() -> float:
+    return _load().mxo_hadamard_scale()
+
+
+def fwht32(x) -> np.ndarray:
+    v = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).copy()
+    assert v.shape == (32,)
+    _load().mxo_fwht32(_ptr(v))
+    return v
+
+
+def nv_tensor_scale(amax_t: float) -> float:
+    return _load().mxo_nv_tensor_scale(float(amax_t))
+
+
+# ---- tensor-level entry points ---------------------------------------------
+def quantize(x_bits: np.ndarray, fmt: str = "mx", rounding: str = "rtn",
+             hadamard: bool = False, axis: int = 1, seed: int = 0):
+    """Quantize a [R, C] bf16 tensor given as its uint16 bit patterns.
+
+    Returns (codes [rows, K/2] uint8, scales [rows, K/bs] uint8, tensor_scale
+    float or None), with (rows, K) = (R, C) for axis 1 and (C, R) for axis 0.
+    """
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    R, C = x.shape
+    rows, K = (R, C) if axis == 1 else (C, R)
+    bs = BLOCK[fmt]
+    codes = np.zeros((rows, K // 2), dtype=np.uint8)
+    scales = np.zeros((rows, K // bs), dtype=np.uint8)
+    ts = np.zeros(1, dtype=np.float32) if fmt == "nv" else None
+    rc = _load().mxo_quantize(_ptr(x), R, C, C, FMT[fmt], ROUNDING[rounding], int(bool(hadamard)),
+                              int(axis), int(seed), _ptr(codes), _ptr(scales), _ptr(ts))
+    if rc != 0:
+        raise ValueError("oracle quantize rejected its arguments")
+    return codes, scales, (float(ts[0]) if ts is not None else None)
+
+
+def dequantize(fmt: str, codes: np.ndarray, scales: np.ndarray, tensor_scale=None) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows, K = codes.shape[0], codes.shape[1] * 2
+    ts = np.array([tensor_scale if tensor_scale is not None else 1.0], dtype=np.float32)
+    y = np.zeros((rows, K), dtype=np.float32)
+    rc = _load().mxo_dequantize(FMT[fmt], rows, K, _ptr(codes), _ptr(scales), _ptr(ts), _ptr(y), K)
+    if rc != 0:
+        raise ValueError("oracle dequantize rejected its arguments")
+    return y
+
+
+def gemm(fmt: str, a, b, rows=None, cols=None):
+    """C = A B^T in binary64 over the exactly dequantized operands.
+
+    a, b: (codes, scales, tensor_scale) as returned by quantize().  rows / cols
+    select a sub-matrix (default: all).  Returns (C, S) float64 arrays of shape
+    [len(rows), len(cols)], S = sum_k |a_ik b_jk|.
+    """
+    ac, asc, ats = a
+    bc, bsc, bts = b
+    ac = np.ascontiguousarray(ac, dtype=np.uint8)
+    bc = np.ascontiguousarray(bc, dtype=np.uint8)
+    asc = np.ascontiguousarray(asc, dtype=np.uint8)
+    bsc = np.ascontiguousarray(bsc, dtype=np.uint8)
+    K = ac.shape[1] * 2
+    assert bc.shape[1] * 2 == K
+    ri = np.arange(ac.shape[0], dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    cj = np.arange(bc.shape[0], dtype=np.int64) if cols is None else np.ascontiguousarray(cols, dtype=np.int64)
+    ta = np.array([ats if ats is not None else 1.0], dtype=np.float32)
+    tb = np.array([bts if bts is not None else 1.0], dtype=np.float32)
+    Cm = np.zeros((len(ri), len(cj)), dtype=np.float64)
+    Sm = np.zeros((len(ri), len(cj)), dtype=np.float64)
+    rc = _load().mxo_gemm(FMT[fmt], K, _ptr(ac), _ptr(asc), _ptr(ta), _ptr(bc), _ptr(bsc), _ptr(tb),
+                          _ptr(ri), len(ri), _ptr(cj), len(cj), _ptr(Cm), _ptr(Sm))
+    if rc != 0:
+        raise ValueError("oracle gemm rejected its arguments")
+    return Cm, Sm

@@ -1,0 +1,453 @@
+/*
+ * mxfp4_oracle.c -- plain, slow CPU oracle for microscaling FP4 quantization
+ * and the block-scaled FP4 GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or calls
+ * this file; it exists so tests (and the CPU baseline of the benchmark) can
+ * check the HIP library against an independent, obviously correct definition.
+ * It shares no source, header, table or constant generator with the HIP code.
+ *
+ * Sources of the method (web pages on microscaling FP4, cited by title and
+ * section):
+ *   [TJ]  "Oscillation-Reduced MXFP4 Training for Vision Transformers",
+ *         abstract: MX = per-group quantization with one shared scale per group.
+ *   [FQT] "FP4 All the Way: Fully Quantized Training of LLMs", abstract:
+ *         E2M1 elements; NVFP4 = blocks of 16 E2M1 values sharing an E4M3 scale;
+ *         round-to-nearest on the forward pass, stochastic rounding on the
+ *         backward and update passes.
+ *   [MRG] "Bridging the Gap Between Promise and Performance for Microscaling
+ *         FP4 Quantization", abstract: MXFP4 scales are powers of two;
+ *         block-wise Hadamard transforms, fused into the weights and computed
+ *         online for activations.
+ *   [DIG] the Russian-language digest of [MRG] (channel post), numbered
+ *         steps 1 and 3: scales exist per block and per tensor; activations
+ *         are rotated with block-diagonal Hadamard rotations.
+ *
+ * The pages fix formats and roles, not the arithmetic.  Every step the pages
+ * leave open is taken with the plainest reading that the rest supports; each
+ * such reading is marked READING below.  Floating-point steps that decide an
+ * integer code are taken in IEEE binary32 (the kernel's precision); the
+ * GEMM is evaluated in binary64 on the exactly dequantized operands.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp (no fast-math), so every float
+ * operation below is one IEEE-754 binary32 round-to-nearest-even operation.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#include <stdlib.h>
+
+#define FMT_MX 0
+#define FMT_NV 1
+#define RND_RTN 0
+#define RND_SR 1
+
+/* ------------------------------------------------------------------ */
+/* Bit helpers                                                          */
+/* ------------------------------------------------------------------ */
+static float f32_from_bits(uint32_t b) { float f; memcpy(&f, &b, 4); return f; }
+
+/* bf16 -> fp32 is exact: a bf16 pattern is the top half of an fp32 pattern. */
+static float bf16_to_f32(uint16_t h) { return f32_from_bits((uint32_t)h << 16); }
+
+/* ------------------------------------------------------------------ */
+/* E2M1 element [FQT abstract: "FP4 values (E2M1)"]                      */
+/* READING: OCP bit layout -- bit 3 sign, bits 2:1 exponent (bias 1),   */
+/* bit 0 mantissa; exponent 0 is subnormal (0 or 0.5).                  */
+/* ------------------------------------------------------------------ */
+double mxo_e2m1_value(int code)
+{
+    int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -mag : mag;
+}
+
+/* ------------------------------------------------------------------ */
+/* E8M0 shared scale of MXFP4 [MRG abstract: power-of-two scale]        */
+/* byte b encodes 2^(b-127); 0xFF is NaN.                               */
+/* ------------------------------------------------------------------ */
+double mxo_e8m0_value(int byte)
+{
+    if (byte == 0xFF) return NAN;
+    return ldexp(1.0, byte - 127);
+}
+
+/* READING: the exponent e of a block is the smallest integer with
+ * 6 * 2^e >= amax (so the block maximum lands inside the E2M1 range
+ * [-6, 6] without clipping), clamped to the E8M0 range [-127, 127];
+ * an all-zero block takes e = -127.  Written as the search it is. */
+int mxo_mx_scale_exponent(float amax)
+{
+    if (!(amax > 0.0f)) return -127;
+    for (int e = -127; e <= 127; e++)
+        if (6.0 * ldexp(1.0, e) >= (double)amax) return e;
+    return 127;
+}
+
+/* ------------------------------------------------------------------ */
+/* E4M3 block scale of NVFP4 [FQT abstract: "shares a scale in E4M3"]  */
+/* Bias 7, no infinities, S.1111.111 is NaN, exponent 0 is subnormal.   */
+/* ------------------------------------------------------------------ */
+double mxo_e4m3_value(int byte)
+{
+    int s = (byte >> 7) & 1, e = (byte >> 3) & 15, m = byte & 7;
+    double mag;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) mag = ldexp((double)m, -9);           /* m/8 * 2^-6 */
+    else mag = ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/* READING: the block scale is the smallest non-negative finite E4M3 value
+ * that is >= r (round up, so the scaled block maximum stays within the
+ * E2M1 range); r above 448 saturates to 448.  Brute force over the codes
+ * in increasing order (0x00..0x7E are increasing for non-negative E4M3). */
+int mxo_e4m3_round_up(float r)
+{
+    for (int b = 0x00; b <= 0x7E; b++)
+        if (mxo_e4m3_value(b) >= (double)r) return b;
+    return 0x7E;
+}
+
+/* ------------------------------------------------------------------ */
+/* Round-to-nearest of a scaled element [FQT abstract: round-to-nearest */
+/* on the forward pass].                                                */
+/* READING: magnitude saturates at 6; the nearest of the 8 magnitudes   */
+/* is chosen, ties going to the code with an even (zero) mantissa bit;  */
+/* the sign bit is the sign bit of the input (so -0 and small negative  */
+/* values give code 0x8).                                               */
+/* xs must not be NaN (callers handle non-finite blocks).              */
+/* ------------------------------------------------------------------ */
+int mxo_rtn_code(double xs)
+{
+    int sign = signbit(xs) ? 8 : 0;
+    double a = fabs(xs);
+    if (a > 6.0) a = 6.0;
+    int best = 0;
+    double bestd = INFINITY;
+    for (int c = 0; c < 8; c++) {
+        double d = fabs(a - mxo_e2m1_value(c));
+        if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) == 1)) {
+            bestd = d;
+            best = c;
+        }
+    }
+    return sign | best;
+}
+
+/* ------------------------------------------------------------------ */
+/* Stochastic rounding [FQT abstract: stochastic rounding on backward   */
+/* and update passes].                                                  */
+/* READING: a = min(|xs|, 6).  A grid magnitude is kept as is.  Else    */
+/* lo < a < hi are the neighbouring magnitudes, t = floor((a-lo)/(hi-lo)*2^16)
+ * and the magnitude rounds up to hi iff rnd16 < t, so that the chance
+ * of rounding up is t/2^16, within 2^-16 of (a-lo)/(hi-lo).  Sign as RTN. */
+/* ------------------------------------------------------------------ */
+int mxo_sr_code(double xs, uint32_t rnd16)
+{
+    int sign = signbit(xs) ? 8 : 0;
+    double a = fabs(xs);
+    if (a > 6.0) a = 6.0;
+    for (int c = 0; c < 8; c++)
+        if (a == mxo_e2m1_value(c)) return sign | c;
+    int lo = 0;
+    while (mxo_e2m1_value(lo + 1) < a) lo++;        /* grid[lo] < a < grid[lo+1] */
+    double glo = mxo_e2m1_value(lo), ghi = mxo_e2m1_value(lo + 1);
+    uint32_t t = (uint32_t)floor((a - glo) / (ghi - glo) * 65536.0);
+    return sign | ((rnd16 < t) ? lo + 1 : lo);
+}
+
+/* ------------------------------------------------------------------ */
+/* Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers:  */
+/* As Easy as 1, 2, 3", SC'11): 4x32-bit counter, 2x32-bit key, ten     */
+/* rounds, each multiplying words 0 and 2 by the two Philox multipliers, */
+/* the key bumped by the two Weyl constants between rounds.              */
+/* ------------------------------------------------------------------ */
+void mxo_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4])
+{
+    const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+    const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+    uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+    uint32_t k0 = key_in[0], k1 = key_in[1];
+    for (int round = 0; round < 10; round++) {
+        uint64_t p0 = (uint64_t)M0 * c0, p1 = (uint64_t)M1 * c2;
+        uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        uint32_t n0 = hi1 ^ c1 ^ k0, n1 = lo1, n2 = hi0 ^ c3 ^ k1, n3 = lo0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+        k0 += W0; k1 += W1;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* READING (random stream of stochastic rounding): element with output
+ * logical index L = i*K + k (row i, contraction index k of the quantized,
+ * contraction-major output) takes 16 bits of Philox4x32-10 with
+ * key = (seed low, seed high) and counter = (g low, g high, axis, 0),
+ * g = L / 8; element L uses 16-bit half (L & 1) of word (L & 7) / 2. */
+uint32_t mxo_rnd16(uint64_t seed, uint64_t L, int axis)
+{
+    uint64_t g = L >> 3;
+    uint32_t ctr[4] = {(uint32_t)g, (uint32_t)(g >> 32), (uint32_t)axis, 0u};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t w[4];
+    mxo_philox4x32_10(ctr, key, w);
+    return (w[(L & 7) >> 1] >> (16 * (L & 1))) & 0xFFFFu;
+}
+
+/* ------------------------------------------------------------------ */
+/* Block-wise Hadamard rotation [MRG abstract: block-wise Hadamard      */
+/* transforms; DIG step 3: block-diagonal Hadamard rotations].          */
+/* READING: blocks of 32 along the contraction axis, Sylvester order    */
+/* H[i][j] = (-1)^popcount(i & j), normalised by 1/sqrt(32) so the      */
+/* rotation is orthonormal.  Evaluated in binary32 as the fast          */
+/* Walsh-Hadamard butterfly with strides 1, 2, 4, 8, 16 -- each pair     */
+/* (x[i], x[i+h]), i & h == 0, becomes (x[i] + x[i+h], x[i] - x[i+h]) -- */
+/* then every entry is multiplied by c = RN_f32(1/sqrt(32)).            */
+/* ------------------------------------------------------------------ */
+float mxo_hadamard_scale(void) { return (float)(1.0 / sqrt(32.0)); }
+
+void mxo_fwht32(float x[32])
+{
+    for (int h = 1; h < 32; h <<= 1) {
+        for (int i = 0; i < 32; i++) {
+            if (i & h) continue;
+            float a = x[i], b = x[i + h];
+            x[i] = a + b;
+            x[i + h] = a - b;
+        }
+    }
+    const float c = mxo_hadamard_scale();
+    for (int i = 0; i < 32; i++) x[i] = x[i] * c;
+}
+
+/* ------------------------------------------------------------------ */
+/* Whole-tensor quantization                                            */
+/* ------------------------------------------------------------------ */
+/* Logical input X is [R, C] bf16, row-major with leading dimension ldx.
+ * axis = 1: the output is [R, C] (contraction along C); axis = 0: the output
+ * is [C, R], the transpose (contraction along R).  Output row i holds the
+ * contraction vector v_i[k] = X[i][k] (axis 1) or X[k][i] (axis 0).
+ * codes:  rows x K/2 bytes, code of k in bits 4*(k&1)+3 .. 4*(k&1).
+ * scales: rows x K/bs bytes (E8M0 for MX, E4M3 for NV).
+ * tensor_scale: one float (NV only).
+ * Returns 0, or -1 on an invalid argument. */
+
+static void load_contraction_row(const uint16_t *x, int64_t ldx, int axis,
+                                 int64_t i, int64_t K, int hadamard, float *v)
+{
+    for (int64_t k = 0; k < K; k++)
+        v[k] = bf16_to_f32(axis == 1 ? x[i * ldx + k] : x[k * ldx + i]);
+    if (hadamard)
+        for (int64_t k0 = 0; k0 < K; k0 += 32) mxo_fwht32(v + k0);
+}
+
+/* NVFP4 per-tensor scale.  READING: s_t = RN_f32(amax_t / (6 * 448)) so the
+ * largest block scale lands on the largest E4M3 value; amax_t is the largest
+ * finite |v| over the tensor (after the rotation, if any); s_t = 1 for an
+ * all-zero tensor, and s_t is kept at or above 2^-117 so that the per-block
+ * product s_b * s_t (s_b >= 2^-9) stays a normal binary32 number. */
+float mxo_nv_tensor_scale(float amax_t)
+{
+    if (!(amax_t > 0.0f)) return 1.0f;
+    float st = amax_t / 2688.0f;
+    const float floor_st = ldexpf(1.0f, -117);
+    return st < floor_st ? floor_st : st;
+}
+
+int mxo_quantize(const uint16_t *x, int64_t R, int64_t C, int64_t ldx,
+                 int fmt, int rounding, int hadamard, int axis, uint64_t seed,
+                 uint8_t *codes, uint8_t *scales, float *tensor_scale)
+{
+    if (!x || !codes || !scales || R < 0 || C < 0 || ldx < C) return -1;
+    if (fmt != FMT_MX && fmt != FMT_NV) return -1;
+    if (rounding != RND_RTN && rounding != RND_SR) return -1;
+    if (axis != 0 && axis != 1) return -1;
+    if (fmt == FMT_NV && !tensor_scale) return -1;
+    const int bs = (fmt == FMT_MX) ? 32 : 16;
+    const int64_t rows = (axis == 1) ? R : C;
+    const int64_t K = (axis == 1) ? C : R;
+    if (K % bs != 0 || (hadamard && K % 32 != 0)) return -1;
+    if (rows == 0 || K == 0) {
+        if (fmt == FMT_NV) *tensor_scale = 1.0f;
+        return 0;
+    }
+
+    /* NVFP4: the tensor scale needs the whole tensor's amax first. */
+    float st = 1.0f;
+    if (fmt == FMT_NV) {
+        float amax_t = 0.0f;
+        #pragma omp parallel
+        {
+            float *v = (float *)malloc(sizeof(float) * K);
+            float local = 0.0f;
+            #pragma omp for
+            for (int64_t i = 0; i < rows; i++) {
+                load_contraction_row(x, ldx, axis, i, K, hadamard, v);
+                for (int64_t k = 0; k < K; k++) {
+                    float a = fabsf(v[k]);
+                    if (isfinite(a) && a > local) local = a;
+                }
+            }
+            #pragma omp critical
+            if (local > amax_t) amax_t = local;
+            free(v);
+        }
+        st = mxo_nv_tensor_scale(amax_t);
+        *tensor_scale = st;
+    }
+
+    #pragma omp parallel
+    {
+        float *v = (float *)malloc(sizeof(float) * K);
+        #pragma omp for
+        for (int64_t i = 0; i < rows; i++) {
+            load_contraction_row(x, ldx, axis, i, K, hadamard, v);
+            for (int64_t b = 0; b < K / bs; b++) {
+                const float *blk = v + b * bs;
+                /* block absmax; a non-finite entry makes the block NaN */
+                float amax = 0.0f;
+                int finite = 1;
+                for (int j = 0; j < bs; j++) {
+                    if (!isfinite(blk[j])) finite = 0;
+                    else if (fabsf(blk[j]) > amax) amax = fabsf(blk[j]);
+                }
+                int scale_byte;
+                double mx_step = 0.0;   /* MX: 2^-e */
+                float nv_inv = 0.0f;    /* NV: RN(1 / RN(s_b * s_t)), 0 if s_b = 0 */
+                if (!finite) {
+                    scale_byte = (fmt == FMT_MX) ? 0xFF : 0x7F;
+                } else if (fmt == FMT_MX) {
+                    int e = mxo_mx_scale_exponent(amax);
+                    scale_byte = e + 127;
+                    mx_step = ldexp(1.0, -e);
+                } else {
+                    float den = 6.0f * st;
+                    float r = amax / den;
+                    scale_byte = mxo_e4m3_round_up(r);
+                    if (scale_byte != 0) {
+                        float sb = (float)mxo_e4m3_value(scale_byte);
+                        float d = sb * st;
+                        nv_inv = 1.0f / d;
+                    }
+                }
+                scales[i * (K / bs) + b] = (uint8_t)scale_byte;
+                for (int j = 0; j < bs; j++) {
+                    int64_t k = b * bs + j;
+                    int code;
+                    if (!finite) {
+                        code = 0;
+                    } else {
+                        double xs;
+                        if (fmt == FMT_MX) {
+                            xs = (double)blk[j] * mx_step;          /* exact */
+                        } else if (scale_byte == 0) {
+                            xs = copysign(0.0, (double)blk[j]);
+                        } else {
+                            float q = blk[j] * nv_inv;              /* one binary32 multiply */
+                            xs = (double)q;
+                        }
+                        if (rounding == RND_RTN)
+                            code = mxo_rtn_code(xs);
+                        else
+                            code = mxo_sr_code(xs, mxo_rnd16(seed, (uint64_t)(i * K + k), axis));
+                    }
+                    uint8_t *byte = &codes[i * (K / 2) + k / 2];
+                    if ((k & 1) == 0) *byte = (uint8_t)((*byte & 0xF0) | code);
+                    else *byte = (uint8_t)((*byte & 0x0F) | (code << 4));
+                }
+            }
+        }
+        free(v);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Dequantization: value = E2M1(code) * scale (NV: * tensor scale).     */
+/* MX in binary32 is exact unless it leaves the binary32 range.  NV is  */
+/* RN(RN(E2M1 * s_b) * s_t); the inner product is exact.                */
+/* Rotated tensors stay in the rotated domain (READING).               */
+/* ------------------------------------------------------------------ */
+int mxo_dequantize(int fmt, int64_t rows, int64_t K, const uint8_t *codes,
+                   const uint8_t *scales, const float *tensor_scale, float *y, int64_t ldy)
+{
+    if (fmt != FMT_MX && fmt != FMT_NV) return -1;
+    const int bs = (fmt == FMT_MX) ? 32 : 16;
+    if (K % bs != 0 || ldy < K) return -1;
+    #pragma omp parallel for
+    for (int64_t i = 0; i < rows; i++) {
+        for (int64_t k = 0; k < K; k++) {
+            int code = (codes[i * (K / 2) + k / 2] >> (4 * (k & 1))) & 0xF;
+            int sbyte = scales[i * (K / bs) + k / bs];
+            float v;
+            if (fmt == FMT_MX) {
+                v = (float)(mxo_e2m1_value(code) * mxo_e8m0_value(sbyte));
+            } else {
+                float g_sb = (float)(mxo_e2m1_value(code) * mxo_e4m3_value(sbyte));
+                v = g_sb * tensor_scale[0];
+            }
+            y[i * ldy + k] = v;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Block-scaled GEMM, C = A * B^T over the contraction axis, evaluated  */
+/* in binary64 on the exactly dequantized operands (E2M1 * scale, NV:   */
+/* * tensor scale -- at most 30 significant bits, exact in binary64).   */
+/* S = sum of |a*b|, the scale of the admissible error.                 */
+/* Computes the sub-matrix rows ri[0..nr) x columns cj[0..nc).           */
+/* ------------------------------------------------------------------ */
+static double exact_operand(int fmt, const uint8_t *codes, const uint8_t *scales,
+                            const float *ts, int64_t K, int64_t i, int64_t k)
+{
+    const int bs = (fmt == FMT_MX) ? 32 : 16;
+    int code = (codes[i * (K / 2) + k / 2] >> (4 * (k & 1))) & 0xF;
+    int sbyte = scales[i * (K / bs) + k / bs];
+    if (fmt == FMT_MX) return mxo_e2m1_value(code) * mxo_e8m0_value(sbyte);
+    return mxo_e2m1_value(code) * mxo_e4m3_value(sbyte) * (double)ts[0];
+}
+
+int mxo_gemm(int fmt, int64_t K,
+             const uint8_t *a_codes, const uint8_t *a_scales, const float *a_ts,
+             const uint8_t *b_codes, const uint8_t *b_scales, const float *b_ts,
+             const int64_t *ri, int64_t nr, const int64_t *cj, int64_t nc,
+             double *Cout, double *Sout)
+{
+    if (fmt != FMT_MX && fmt != FMT_NV) return -1;
+    const int bs = (fmt == FMT_MX) ? 32 : 16;
+    if (K % bs != 0) return -1;
+    if (nr == 0 || nc == 0) return 0;
+    /* the selected rows of A, dequantized once */
+    double *arows = (double *)malloc(sizeof(double) * (size_t)nr * (size_t)(K > 0 ? K : 1));
+    if (!arows) return -1;
+    #pragma omp parallel for
+    for (int64_t p = 0; p < nr; p++)
+        for (int64_t k = 0; k < K; k++)
+            arows[p * K + k] = exact_operand(fmt, a_codes, a_scales, a_ts, K, ri[p], k);
+    #pragma omp parallel
+    {
+        double *brow = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+        #pragma omp for
+        for (int64_t q = 0; q < nc; q++) {
+            for (int64_t k = 0; k < K; k++)
+                brow[k] = exact_operand(fmt, b_codes, b_scales, b_ts, K, cj[q], k);
+            for (int64_t p = 0; p < nr; p++) {
+                const double *arow = arows + p * K;
+                double c = 0.0, s = 0.0;
+                for (int64_t k = 0; k < K; k++) {
+                    double prod = arow[k] * brow[k];
+                    c += prod;
+                    s += fabs(prod);
+                }
+                Cout[p * nc + q] = c;
+                Sout[p * nc + q] = s;
+            }
+        }
+        free(brow);
+    }
+    free(arows);
+    return 0;
+}
