@@ -1,0 +1,162 @@
+// fp4_device.h -- device helpers shared by the libmxfp4 kernels (gfx950).
+//
+// Formats (web pages on microscaling FP4, cited by title and section):
+//   E2M1 elements and the NVFP4 block of 16 with an E4M3 scale:
+//     "FP4 All the Way: Fully Quantized Training of LLMs", abstract.
+//   MXFP4's power-of-two (E8M0) shared scale per group:
+//     "Bridging the Gap Between Promise and Performance for Microscaling FP4
+//     Quantization", abstract; "Oscillation-Reduced MXFP4 Training for Vision
+//     Transformers", abstract (per-group scaling).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxfp4 {
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32v4 __attribute__((ext_vector_type(4)));
+
+constexpr int FMT_MX = 0;
+constexpr int FMT_NV = 1;
+constexpr int RND_RTN = 0;
+constexpr int RND_SR = 1;
+
+// ---------------------------------------------------------------------------
+// Cross-lane helpers (DPP within a quad of 4 lanes).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) {
+  // quad_perm [1,0,3,2]
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) {
+  // quad_perm [2,3,0,1]
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+}
+__device__ __forceinline__ float dpp_xor1f(float v) {
+  return __uint_as_float(dpp_xor1(__float_as_uint(v)));
+}
+__device__ __forceinline__ float dpp_xor2f(float v) {
+  return __uint_as_float(dpp_xor2(__float_as_uint(v)));
+}
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  u16x2 x = __builtin_bit_cast(u16x2, a), y = __builtin_bit_cast(u16x2, b);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, y));
+}
+
+// ---------------------------------------------------------------------------
+// MXFP4 shared scale: the smallest e with 6 * 2^e >= amax, clamped to
+// [-127, 127]; returned as the E8M0 byte e + 127.  `abits` is the IEEE
+// binary32 pattern of amax >= 0 (finite).  For a normal amax = (1 + f) 2^E:
+// e = E - 2 when f <= 1/2, else E - 1; zero and subnormal amax give -127.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t mx_scale_byte_from_f32bits(uint32_t abits) {
+  int ef = (int)(abits >> 23);                    // biased exponent (sign is 0)
+  int inc = (abits & 0x7FFFFFu) > 0x400000u ? 1 : 0;
+  int b = ef - 2 + inc;                           // (E - 2 + inc) + 127
+  if (ef == 0) b = 0;
+  return (uint32_t)(b < 0 ? 0 : b);
+}
+
+// The binary32 number whose exponent field is the E8M0 byte: the scale
+// operand format of the gfx950 FP4 conversion instructions (only the
+// exponent bits are used; byte 0 stands for 2^-127).
+__device__ __forceinline__ float e8m0_as_cvt_scale(uint32_t byte) {
+  return __uint_as_float(byte << 23);
+}
+
+// Exact binary32 value 2^(127 - byte) = 1 / 2^(byte - 127), byte in [0, 254].
+__device__ __forceinline__ float mx_inv_scale(uint32_t byte) {
+  int ef = 254 - (int)byte;                       // exponent field of 2^(127-byte)
+  // byte 254 -> 2^-127 is subnormal: 0x00400000
+  return ef > 0 ? __uint_as_float((uint32_t)ef << 23) : __uint_as_float(0x00400000u);
+}
+
+// Exact binary32 value of an E8M0 byte (0xFF -> NaN); 2^-127 is subnormal.
+__device__ __forceinline__ float e8m0_value(uint32_t byte) {
+  if (byte == 0xFFu) return __uint_as_float(0x7FC00000u);
+  return byte > 0 ? __uint_as_float(byte << 23) : __uint_as_float(0x00400000u);
+}
+
+// ---------------------------------------------------------------------------
+// E4M3 (bias 7, no infinities, 0x7F NaN).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float e4m3_value(uint32_t byte) {
+  byte &= 0x7Fu;
+  if (byte == 0x7Fu) return __uint_as_float(0x7FC00000u);
+  if (byte < 8u) return (float)byte * 0x1p-9f;    // subnormal m * 2^-9 (exact)
+  return __uint_as_float((((byte >> 3) + 120u) << 23) | ((byte & 7u) << 20));
+}
+
+// Smallest non-negative E4M3 value >= r (r >= 0, finite), saturating at 448.
+//   r < 2^-6 : subnormal range, byte = ceil(r * 2^9) (8 means 2^-6, which is
+//              also the byte of the smallest normal);
+//   else     : r = (1 + f) 2^E, byte = ((E + 7) << 3) + ceil(8 f), where a
+//              mantissa of 8 carries into the exponent.
+__device__ __forceinline__ uint32_t e4m3_round_up_byte(float r) {
+  if (!(r > 0.0f)) return 0u;
+  if (r > 448.0f) return 0x7Eu;
+  uint32_t b;
+  if (r < 0x1p-6f) {
+    b = (uint32_t)__builtin_ceilf(r * 512.0f);
+  } else {
+    uint32_t bits = __float_as_uint(r);
+    int E = (int)(bits >> 23) - 127;
+    uint32_t m = ((bits & 0x7FFFFFu) + 0xFFFFFu) >> 20;
+    b = (uint32_t)((E + 7) << 3) + m;
+  }
+  return b > 0x7Eu ? 0x7Eu : b;
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11).  The key schedule is
+// uniform across a wavefront, so key words live in scalar registers.
+// ---------------------------------------------------------------------------
+struct u32x4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; r++) {
+    uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return {c0, c1, c2, c3};
+}
+
+// ---------------------------------------------------------------------------
+// Stochastic rounding of one scaled element xs to a 4-bit code.
+// a = min(|xs|, 6); for a >= 1 the E2M1 neighbours below a are the binary32
+// value truncated to one mantissa bit, and the position between the two
+// neighbours is the remaining 22 mantissa bits: t = bits[21:6] =
+// floor(frac * 2^16), low code = (bits >> 22) - 252.  For a < 1 the grid step
+// is 1/2: q = floor(a * 2^17) (exact), low code = q >> 16, t = q & 0xFFFF.
+// Round up iff rnd16 < t.  The sign bit is the input's.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t sr_code(float xs, uint32_t rnd16) {
+  uint32_t sign = (__float_as_uint(xs) >> 28) & 8u;
+  float a = __builtin_fminf(__builtin_fabsf(xs), 6.0f);
+  uint32_t ab = __float_as_uint(a);
+  uint32_t lo, t;
+  if (a >= 1.0f) {
+    lo = (ab >> 22) - 252u;
+    t = (ab >> 6) & 0xFFFFu;
+  } else {
+    uint32_t q = (uint32_t)(a * 131072.0f);
+    lo = q >> 16;
+    t = q & 0xFFFFu;
+  }
+  return sign | (lo + (rnd16 < t ? 1u : 0u));
+}
+
+}  // namespace mxfp4

@@ -1,0 +1,136 @@
+// mxfp4_abi.cpp -- the C ABI of libmxfp4: argument checks, sizes, dispatch.
+//
+// Every entry point validates its arguments before anything is launched and
+// reports problems as an mxfp4_status; nothing is allocated, freed or
+// synchronized here.  The operations themselves are described in mxfp4.h.
+#include "mxfp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include "mxfp4_internal.h"
+
+namespace {
+
+int block_of(int fmt) { return fmt == MXFP4_FMT_MX ? 32 : 16; }
+bool fmt_ok(int fmt) { return fmt == MXFP4_FMT_MX || fmt == MXFP4_FMT_NV; }
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Largest element count the kernels index (R * C and rows * k): the 64-bit
+// index math is exact well beyond any tensor that fits in device memory.
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+}  // namespace
+
+extern "C" {
+
+const char* mxfp4_status_string(int status) {
+  switch (status) {
+    case MXFP4_OK: return "MXFP4_OK";
+    case MXFP4_ERR_INVALID_ARG: return "MXFP4_ERR_INVALID_ARG: null pointer, bad enum, negative size or leading dimension too small";
+    case MXFP4_ERR_UNSUPPORTED_SHAPE: return "MXFP4_ERR_UNSUPPORTED_SHAPE: contraction length is not a multiple of the required block";
+    case MXFP4_ERR_FORMAT_MISMATCH: return "MXFP4_ERR_FORMAT_MISMATCH: GEMM operands differ in format, contraction length or rotation";
+    case MXFP4_ERR_WORKSPACE: return "MXFP4_ERR_WORKSPACE: workspace missing or too small";
+    case MXFP4_ERR_HIP: return "MXFP4_ERR_HIP: a HIP kernel launch failed";
+    default: return "unknown mxfp4_status";
+  }
+}
+
+mxfp4_status mxfp4_tensor_bytes(int fmt, int64_t rows, int64_t k, size_t* codes_bytes, size_t* scales_bytes) {
+  if (!fmt_ok(fmt) || rows < 0 || k < 0 || !codes_bytes || !scales_bytes) return MXFP4_ERR_INVALID_ARG;
+  if (k % block_of(fmt) != 0) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  *codes_bytes = (size_t)rows * (size_t)(k / 2);
+  *scales_bytes = (size_t)rows * (size_t)(k / block_of(fmt));
+  return MXFP4_OK;
+}
+
+mxfp4_status mxfp4_quantize_workspace_bytes(int fmt, int64_t R, int64_t C, int axis, size_t* bytes) {
+  if (!fmt_ok(fmt) || R < 0 || C < 0 || (axis != 0 && axis != 1) || !bytes) return MXFP4_ERR_INVALID_ARG;
+  *bytes = (fmt == MXFP4_FMT_NV) ? (size_t)mxfp4::kAmaxPartials * sizeof(uint32_t) : 0;
+  return MXFP4_OK;
+}
+
+mxfp4_status mxfp4_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int fmt, int rounding,
+                            int hadamard, int axis, uint64_t seed, mxfp4_tensor* out, void* workspace,
+                            size_t ws_bytes, hipStream_t stream) {
+  if (!fmt_ok(fmt) || (rounding != MXFP4_RTN && rounding != MXFP4_SR) || (hadamard != 0 && hadamard != 1) ||
+      (axis != 0 && axis != 1) || !out)
+    return MXFP4_ERR_INVALID_ARG;
+  if (R < 0 || C < 0 || ldx < C || ldx < 1) return MXFP4_ERR_INVALID_ARG;
+  const int64_t rows = axis == 1 ? R : C, k = axis == 1 ? C : R;
+  if (k % block_of(fmt) != 0 || (hadamard && k % 32 != 0)) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  if (R > 0 && C > kMaxElems / R) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  if (out->fmt != fmt || out->rows != rows || out->k != k || out->hadamard != hadamard)
+    return MXFP4_ERR_INVALID_ARG;
+  if (rows == 0 || k == 0) return MXFP4_OK;
+  if (!x || !out->codes || !out->scales) return MXFP4_ERR_INVALID_ARG;
+  // the kernels store codes as aligned 32-bit (rows) or 8/16-byte (transposed) words
+  if (!aligned(out->codes, 16)) return MXFP4_ERR_INVALID_ARG;
+  uint32_t* partials = nullptr;
+  if (fmt == MXFP4_FMT_NV) {
+    if (!out->tensor_scale) return MXFP4_ERR_INVALID_ARG;
+    if (!workspace || ws_bytes < (size_t)mxfp4::kAmaxPartials * sizeof(uint32_t) || !aligned(workspace, 4))
+      return MXFP4_ERR_WORKSPACE;
+    partials = (uint32_t*)workspace;
+  }
+  hipError_t e = mxfp4::launch_quantize(x, R, C, ldx, fmt, rounding, hadamard, axis, seed, out->codes,
+                                        out->scales, out->tensor_scale, partials, stream);
+  return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
+}
+
+mxfp4_status mxfp4_dequantize(const mxfp4_tensor* q, float* y, int64_t ldy, hipStream_t stream) {
+  if (!q || !fmt_ok(q->fmt) || q->rows < 0 || q->k < 0) return MXFP4_ERR_INVALID_ARG;
+  if (q->k % block_of(q->fmt) != 0) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  if (ldy < q->k) return MXFP4_ERR_INVALID_ARG;
+  if (q->rows == 0 || q->k == 0) return MXFP4_OK;
+  if (!y || !q->codes || !q->scales || (q->fmt == MXFP4_FMT_NV && !q->tensor_scale)) return MXFP4_ERR_INVALID_ARG;
+  if (!aligned(q->codes, 4)) return MXFP4_ERR_INVALID_ARG;
+  hipError_t e = mxfp4::launch_dequantize(q->fmt, q->rows, q->k, q->codes, q->scales, q->tensor_scale, y, ldy,
+                                          stream);
+  return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
+}
+
+static mxfp4_status check_gemm_operands(const mxfp4_tensor* A, const mxfp4_tensor* B) {
+  if (!A || !B || !fmt_ok(A->fmt) || !fmt_ok(B->fmt) || A->rows < 0 || B->rows < 0 || A->k < 0 || B->k < 0)
+    return MXFP4_ERR_INVALID_ARG;
+  if (A->fmt != B->fmt || A->k != B->k || A->hadamard != B->hadamard) return MXFP4_ERR_FORMAT_MISMATCH;
+  const int kmul = A->fmt == MXFP4_FMT_MX ? 128 : 64;
+  if (A->k % kmul != 0) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  return MXFP4_OK;
+}
+
+mxfp4_status mxfp4_gemm_workspace_bytes(const mxfp4_tensor* A, const mxfp4_tensor* B, size_t* bytes) {
+  if (!bytes) return MXFP4_ERR_INVALID_ARG;
+  mxfp4_status s = check_gemm_operands(A, B);
+  if (s != MXFP4_OK) return s;
+  mxfp4::GemmPlan pl = mxfp4::plan_gemm(A->fmt, A->rows, B->rows, A->k);
+  *bytes = pl.splits > 1 ? (size_t)pl.splits * (size_t)A->rows * (size_t)B->rows * sizeof(float) : 0;
+  return MXFP4_OK;
+}
+
+mxfp4_status mxfp4_gemm(const mxfp4_tensor* A, const mxfp4_tensor* B, float* C, int64_t ldc, void* workspace,
+                        size_t ws_bytes, hipStream_t stream) {
+  mxfp4_status s = check_gemm_operands(A, B);
+  if (s != MXFP4_OK) return s;
+  const int64_t M = A->rows, N = B->rows, K = A->k;
+  if (ldc < N || ldc < 1) return MXFP4_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return MXFP4_OK;
+  if (!C || !A->codes || !A->scales || !B->codes || !B->scales) return MXFP4_ERR_INVALID_ARG;
+  if (A->fmt == MXFP4_FMT_NV && (!A->tensor_scale || !B->tensor_scale)) return MXFP4_ERR_INVALID_ARG;
+  if (!aligned(A->codes, 16) || !aligned(B->codes, 16) || !aligned(A->scales, 4) || !aligned(B->scales, 4))
+    return MXFP4_ERR_INVALID_ARG;
+  mxfp4::GemmPlan pl = mxfp4::plan_gemm(A->fmt, M, N, K);
+  if (pl.splits > 1) {
+    const size_t need = (size_t)pl.splits * (size_t)M * (size_t)N * sizeof(float);
+    if (!workspace || ws_bytes < need || !aligned(workspace, 4)) return MXFP4_ERR_WORKSPACE;
+  }
+  hipError_t e;
+  if (A->fmt == MXFP4_FMT_MX)
+    e = mxfp4::launch_gemm_mx(A->codes, A->scales, B->codes, B->scales, M, N, K, C, ldc, (float*)workspace, pl,
+                              stream);
+  else
+    e = mxfp4::launch_gemm_nv(A->codes, A->scales, A->tensor_scale, B->codes, B->scales, B->tensor_scale, M, N, K,
+                              C, ldc, (float*)workspace, pl, stream);
+  return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
+}
+
+}  // extern "C"

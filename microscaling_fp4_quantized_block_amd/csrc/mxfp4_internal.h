@@ -1,0 +1,36 @@
+// mxfp4_internal.h -- launchers shared between the C ABI and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxfp4 {
+
+// Upper bound on the tensor-amax partials (one per workgroup of the amax
+// pass); the NVFP4 quantize workspace holds this many 32-bit words.
+constexpr int kAmaxPartials = 1024;
+
+hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int fmt, int rounding,
+                           int hadamard, int axis, uint64_t seed, uint8_t* codes, uint8_t* scales,
+                           float* tensor_scale, uint32_t* partials, hipStream_t stream);
+
+hipError_t launch_dequantize(int fmt, int64_t rows, int64_t K, const uint8_t* codes, const uint8_t* scales,
+                             const float* ts, float* y, int64_t ldy, hipStream_t stream);
+
+// GEMM planning: how many K-splits a launch uses (1 = none).  The workspace
+// holds splits * M * N floats when splits > 1.
+struct GemmPlan {
+  int splits;
+  int64_t k_tiles;     // contraction tiles of the kernel's K step
+};
+GemmPlan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K);
+
+hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                          const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, float* C, int64_t ldc,
+                          float* workspace, const GemmPlan& plan, hipStream_t stream);
+
+hipError_t launch_gemm_nv(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
+                          const uint8_t* b_codes, const uint8_t* b_scales, const float* b_ts, int64_t M,
+                          int64_t N, int64_t K, float* C, int64_t ldc, float* workspace, const GemmPlan& plan,
+                          hipStream_t stream);
+
+}  // namespace mxfp4

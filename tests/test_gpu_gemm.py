@@ -1,0 +1,151 @@
+"""GPU parity of the block-scaled FP4 GEMM against the binary64 oracle:
+|C_gpu - C| <= 1e-5 * sum_k |a_ik b_jk| per element."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_common import need_gpu, say, to_device_bf16, q_to_host, assert_gemm_within
+
+pytestmark = pytest.mark.gpu
+
+
+def _quant_pair(mx, oracle_mod, A_bits, B_bits, fmt, had=False, rnd="rtn", axis_a=1, axis_b=1, seeds=(0, 1)):
+    qa = mx.mxfp4_quantize(to_device_bf16(A_bits), fmt, rnd, had, axis_a, seeds[0])
+    qb = mx.mxfp4_quantize(to_device_bf16(B_bits), fmt, rnd, had, axis_b, seeds[1])
+    oa = oracle_mod.quantize(A_bits, fmt, rnd, had, axis_a, seeds[0])
+    ob = oracle_mod.quantize(B_bits, fmt, rnd, had, axis_b, seeds[1])
+    # the GEMM test relies on identical operands on both sides
+    ga, gb = q_to_host(qa), q_to_host(qb)
+    assert np.array_equal(ga[0], oa[0]) and np.array_equal(ga[1], oa[1])
+    assert np.array_equal(gb[0], ob[0]) and np.array_equal(gb[1], ob[1])
+    return qa, qb, oa, ob
+
+
+@pytest.mark.parametrize("fmt", ["mx", "nv"])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 1024), (300, 200, 384), (17, 529, 256), (512, 768, 2048),
+                                   (64, 96, 8192), (1, 1, 128)])
+def test_gemm_small_full_check(oracle_mod, fmt, M, N, K):
+    """Several tiles with ragged edges, a short contraction, one split-K case
+    (64 x 96 x 8192) and a 1 x 1 output; every element checked."""
+    mx = need_gpu()
+    A = workloads.small_t_bf16((M, K), 3.0, seed=31, outlier_frac=0.02)
+    B = workloads.small_normal_bf16((N, K), 0.02, seed=32)
+    qa, qb, oa, ob = _quant_pair(mx, oracle_mod, A, B, fmt)
+    say("gemm", fmt, M, N, K, "ws", mx.mxfp4_gemm_workspace_bytes(qa, qb))
+    C = mx.mxfp4_gemm(qa, qb)
+    torch.cuda.synchronize()
+    Co, So = oracle_mod.gemm(fmt, oa, ob)
+    assert_gemm_within(C.cpu().numpy(), Co, So, f"{fmt} {M}x{N}x{K}")
+
+
+def test_gemm_config1_full(oracle_mod):
+    """MXFP4 RTN 256 x 256 x 1024: N(0,1) activations, N(0,0.02) weights."""
+    mx = need_gpu()
+    X = workloads.make_tensor(1, "X")
+    W = workloads.make_tensor(1, "W")
+    qa, qb, oa, ob = _quant_pair(mx, oracle_mod, X, W, "mx")
+    say("gemm config 1")
+    C = mx.mxfp4_gemm(qa, qb).cpu().numpy()
+    Co, So = oracle_mod.gemm("mx", oa, ob)
+    assert_gemm_within(C, Co, So, "config1")
+
+
+def test_gemm_one_hot_exact(oracle_mod):
+    """Codes of +-1 with unit scales: the result is an exact integer count."""
+    mx = need_gpu()
+    rng = np.random.default_rng(33)
+    M, N, K = 256, 256, 512
+    va = rng.choice([-1.0, 0.0, 1.0], size=(M, K))
+    vb = rng.choice([-1.0, 1.0], size=(N, K))
+    va[:, 0] = 4.0
+    vb[:, 0] = 4.0      # absmax 4 -> e = 0 so +-1 maps to the codes of +-1
+    A = workloads.f32_to_bf16_bits(va.astype(np.float32))
+    B = workloads.f32_to_bf16_bits(vb.astype(np.float32))
+    qa, qb, oa, ob = _quant_pair(mx, oracle_mod, A, B, "mx")
+    C = mx.mxfp4_gemm(qa, qb).cpu().numpy()
+    assert np.array_equal(C.astype(np.float64), va @ vb.T)
+
+
+def test_gemm_writes_into_strided_output(oracle_mod):
+    mx = need_gpu()
+    A = workloads.small_normal_bf16((128, 256), 1.0, seed=34)
+    B = workloads.small_normal_bf16((96, 256), 1.0, seed=35)
+    qa, qb, oa, ob = _quant_pair(mx, oracle_mod, A, B, "mx")
+    big = torch.full((128, 200), 7.0, device="cuda")
+    mx.mxfp4_gemm(qa, qb, out=big[:, 50:146])
+    host = big.cpu().numpy()
+    Co, So = oracle_mod.gemm("mx", oa, ob)
+    assert_gemm_within(host[:, 50:146], Co, So, "strided")
+    assert (host[:, :50] == 7.0).all() and (host[:, 146:] == 7.0).all()
+
+
+def _sampled_check(mx, oracle_mod, qa, qb, oa, ob, fmt, what, nsample=48, seed=0):
+    C = mx.mxfp4_gemm(qa, qb)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed)
+    M, N = qa.rows, qb.rows
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, size=min(nsample, M), replace=False)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, size=min(nsample, N), replace=False)]))
+    Cr = C[torch.from_numpy(rows).cuda()].cpu().numpy()
+    Cc = C[:, torch.from_numpy(cols).cuda()].cpu().numpy()
+    # full rows and full columns of C
+    Co_r, So_r = oracle_mod.gemm(fmt, oa, ob, rows=rows)
+    Co_c, So_c = oracle_mod.gemm(fmt, oa, ob, cols=cols)
+    e1 = assert_gemm_within(Cr, Co_r, So_r, what + " rows")
+    e2 = assert_gemm_within(Cc, Co_c, So_c, what + " cols")
+    say(what, "max |err|/S", max(e1, e2))
+
+
+def test_gemm_headline_sampled(oracle_mod):
+    """4096 x 14336 x 8192 MXFP4 (the benchmark's launch), checked on full
+    sampled rows and columns of C."""
+    mx = need_gpu()
+    A = workloads.make_tensor(0, "A")
+    B = workloads.make_tensor(0, "B")
+    say("headline quantize")
+    qa, qb, oa, ob = _quant_pair(mx, oracle_mod, A, B, "mx")
+    _sampled_check(mx, oracle_mod, qa, qb, oa, ob, "mx", "headline", nsample=24)
+
+
+def test_gemm_config2_sampled(oracle_mod):
+    """NVFP4 8192 x 4096 x 4096, Student-t(3) activations with 1% x50 outlier channels."""
+    mx = need_gpu()
+    X = workloads.make_tensor(2, "X")
+    W = workloads.make_tensor(2, "W")
+    qa, qb, oa, ob = _quant_pair(mx, oracle_mod, X, W, "nv")
+    _sampled_check(mx, oracle_mod, qa, qb, oa, ob, "nv", "config2", nsample=32)
+
+
+def test_gemm_config3_decode_and_prefill_sampled(oracle_mod):
+    """MXFP4 with block Hadamard on both operands: decode M = 16 and prefill."""
+    mx = need_gpu()
+    W = workloads.make_tensor(3, "W_up")
+    qw = mx.mxfp4_quantize(to_device_bf16(W), "mx", "rtn", True)
+    ow = oracle_mod.quantize(W, "mx", "rtn", True)
+    for name in ("x_dec_up", "x_pre_up"):
+        X = workloads.make_tensor(3, name)
+        qx = mx.mxfp4_quantize(to_device_bf16(X), "mx", "rtn", True)
+        ox = oracle_mod.quantize(X, "mx", "rtn", True)
+        _sampled_check(mx, oracle_mod, qx, qw, ox, ow, "mx", "config3 " + name, nsample=24)
+
+
+def test_gemm_config4_wgrad_split_k(oracle_mod):
+    """ViT fc2 wgrad dW = dY^T X: 768 x 3072 x 50432 with both operands
+    quantized along the token axis (axis 0) with stochastic rounding."""
+    mx = need_gpu()
+    dY = workloads.make_tensor(4, "dY2")       # [50432, 768]
+    X = workloads.make_tensor(4, "X2")         # [50432, 3072]
+    qa, qb, oa, ob = _quant_pair(mx, oracle_mod, dY, X, "mx", rnd="sr", axis_a=0, axis_b=0, seeds=(2, 3))
+    assert mx.mxfp4_gemm_workspace_bytes(qa, qb) > 0          # split along K
+    _sampled_check(mx, oracle_mod, qa, qb, oa, ob, "mx", "config4 wgrad fc2", nsample=16)
+
+
+def test_gemm_format_mismatch_rejected(oracle_mod):
+    mx = need_gpu()
+    A = workloads.small_normal_bf16((64, 256), 1.0, seed=36)
+    qa = mx.mxfp4_quantize(to_device_bf16(A), "mx", "rtn", False)
+    qh = mx.mxfp4_quantize(to_device_bf16(A), "mx", "rtn", True)
+    with pytest.raises(mx.MxFp4Error) as e:
+        mx.mxfp4_gemm(qa, qh)
+    assert e.value.status == -3
