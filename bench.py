@@ -1,0 +1,180 @@
+"""Benchmark of the microscaling-FP4 linear-layer hot path on one MI355X.
+
+One step = quantize the activations A [4096, 8192] and the weights
+B [14336, 8192] (bf16 -> MXFP4, round-to-nearest, no rotation), then the
+block-scaled FP4 GEMM C = A B^T (M x N x K = 4096 x 14336 x 8192, FP32 out).
+Inputs are seeded synthetic bf16 tensors resident in HBM before timing starts
+(A ~ N(0, 1), B ~ N(0, 0.02); the pages' own datasets are not available).
+
+Prints one JSON line.  `value` is the whole step's throughput expressed as
+GEMM FLOP per second (2 M N K / step time); the per-kernel figures (GEMM
+TFLOP/s against the dense-FP4 MFMA peak, quantizer GB/s against HBM) are in
+`components`, and `roofline` reports the dominant kernel (the GEMM), timed
+with HIP events on the stream it is launched on.  `cpu_baseline` times the
+CPU oracle on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP4 GEMM TFLOPS + quantizer GB/s (4096×14336×8192) and % of 1-GPU roofline"
+M, N, K = 4096, 14336, 8192
+PEAK_FP4_TFLOPS = 10100.0      # MI355X dense FP4 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+MX_BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0   # bf16 in, packed codes + E8M0 scale out
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "gemm_mx_traffic.json"),
+                    help="HBM bytes per GEMM launch from rocprofv3 counters (optional)")
+    return ap.parse_args()
+
+
+def gemm_traffic(path):
+    """HBM bytes per launch of the GEMM kernel measured with rocprofv3 PMC
+    counters (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration);
+    None when not measured for the current kernel."""
+    try:
+        with open(path) as f:
+            d = json.load(f)
+        return float(d["bytes_per_launch"]) if d.get("current", False) else None
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def cpu_baseline():
+    """The CPU oracle on a bounded sample of the step, scaled to the whole step."""
+    import oracle
+    import workloads
+    os.environ.setdefault("OMP_NUM_THREADS", str(len(os.sched_getaffinity(0))))
+    cores = int(os.environ["OMP_NUM_THREADS"])       # threads the OpenMP oracle runs with
+    oracle._load()
+    qa_rows, qb_rows, g_rows, g_cols = 1024, 4096, 512, 4096
+    A = workloads.make_tensor(0, "A", rows=qa_rows)
+    B = workloads.make_tensor(0, "B", rows=qb_rows)
+    t0 = time.perf_counter()
+    qa = oracle.quantize(A, "mx", "rtn")
+    t1 = time.perf_counter()
+    qb = oracle.quantize(B, "mx", "rtn")
+    t2 = time.perf_counter()
+    oracle.gemm("mx", qa, qb, rows=np.arange(g_rows), cols=np.arange(g_cols))
+    t3 = time.perf_counter()
+    step_s = ((t1 - t0) * (M / qa_rows) + (t2 - t1) * (N / qb_rows)
+              + (t3 - t2) * (M * N) / (g_rows * g_cols))
+    return {
+        "value": 2.0 * M * N * K / step_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"quantize {qa_rows} of {M} rows of A and {qb_rows} of {N} rows of B, "
+                   f"fp64 GEMM of {g_rows}x{g_cols} outputs (K={K}); each part scaled to the full step"),
+        "sample_seconds": round(t3 - t0, 2),
+        "step_seconds_extrapolated": round(step_s, 1),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs on a single "
+              "MI355X; see the sharding note in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads
+    import microscaling_fp4_quantized_block_amd as mx
+
+    dev = torch.device("cuda", 0)
+    A_bits = workloads.make_tensor(0, "A")
+    B_bits = workloads.make_tensor(0, "B")
+    A = torch.from_numpy(A_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    B = torch.from_numpy(B_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    qa = mx.empty_qtensor("mx", M, K, False, dev)
+    qb = mx.empty_qtensor("mx", N, K, False, dev)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    mx.mxfp4_quantize(A, "mx", "rtn", False, 1, 0, out=qa)
+    mx.mxfp4_quantize(B, "mx", "rtn", False, 1, 0, out=qb)
+    ws_bytes = mx.mxfp4_gemm_workspace_bytes(qa, qb)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        mx.mxfp4_quantize(A, "mx", "rtn", False, 1, 0, out=qa)
+        if ev is not None:
+            ev[1].record()
+        mx.mxfp4_quantize(B, "mx", "rtn", False, 1, 0, out=qb)
+        if ev is not None:
+            ev[2].record()
+        mx.mxfp4_gemm(qa, qb, out=C, workspace=ws)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    qa_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    qb_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    g_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+
+    flops = 2.0 * M * N * K
+    gemm_tflops = flops / (g_ms * 1e-3) / 1e12
+    qa_gbps = M * K * MX_BYTES_PER_ELEM / (qa_ms * 1e-3) / 1e9
+    qb_gbps = N * K * MX_BYTES_PER_ELEM / (qb_ms * 1e-3) / 1e9
+    traffic = gemm_traffic(args.traffic_json)
+    out = {
+        "metric": METRIC,
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": "mx-rtn-4096x14336x8192", "M": M, "N": N, "K": K, "fmt": "mxfp4",
+                   "rounding": "rtn", "hadamard": False,
+                   "step": "quantize A + quantize B + FP4 GEMM", "parallelism": "none (1 GPU)"},
+        "components": {
+            "gemm": {"ms": round(g_ms, 4), "tflops": round(gemm_tflops, 1),
+                     "frac_of_fp4_peak": round(gemm_tflops / PEAK_FP4_TFLOPS, 4)},
+            "quantize_A": {"ms": round(qa_ms, 4), "gbps": round(qa_gbps, 1),
+                           "frac_of_hbm_peak": round(qa_gbps / PEAK_HBM_GBPS, 4)},
+            "quantize_B": {"ms": round(qb_ms, 4), "gbps": round(qb_gbps, 1),
+                           "frac_of_hbm_peak": round(qb_gbps / PEAK_HBM_GBPS, 4)},
+        },
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP4_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
