@@ -55,9 +55,12 @@ constexpr int SB_BYTES = BN * SROW;
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;   // 36 KB
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
 
-// 16-byte chunk swizzle within a 64-byte row: rows that one MFMA operand read
-// touches together (8 or 16 consecutive rows) land on distinct LDS banks.
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// 16-byte chunk swizzle within a 64-byte row.  An MFMA operand read has lane l
+// fetch 16 B of row l % 32; with 64-byte rows, rows r and r + 4 fall on the
+// same banks, so the chunk index is XORed with bits 2..3 of the row.  (Measured
+// on gfx950 with SQ_LDS_BANK_CONFLICT: this pattern is conflict-free, while
+// XORing bits 0..1 or 1..2 leaves 2- to 4-way conflicts.)
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
 struct GemmArgs {
   const uint8_t* a;
@@ -220,62 +223,251 @@ __device__ __forceinline__ void gemm_mainloop(const GemmArgs& p, uint8_t* smem, 
 // ---------------------------------------------------------------------------
 // MXFP4
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * STAGE_BYTES];
+// s_waitcnt with vmcnt <= VM and lgkmcnt <= LGKM (expcnt left alone).
+template <int VM, int LGKM>
+__device__ __forceinline__ void wait_cnt() {
+  static_assert(VM < 64 && LGKM < 16, "counter range");
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (LGKM << 8));
+}
+
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The MXFP4 kernel runs 8 waves per workgroup (2 per SIMD): one wave per SIMD
+// cannot keep enough loads in flight (measured on gfx950: about 40 GB/s per
+// CU from L2 with 4 waves, 65 GB/s with 8), and the second wave per SIMD hides
+// LDS latency.  Wave w owns output rows 128 (w / 4) .. +128 and columns
+// 64 (w % 4) .. +64: 4 x 2 MFMA tiles, 128 accumulators per lane.
+//
+// LDS: a ring of 4 code stages (A and B, 64 B per row each) and a ring of 3
+// scale groups.  A scale group holds 16 scale bytes per row = 4 stages, so each
+// row's scales arrive as one 16-byte load instead of four 4-byte loads (the
+// scale rows are K/32 bytes apart, so every small load is a separate cache
+// line).  Group G is loaded in four 64-row pieces alongside stages 4G-4..4G-1.
+constexpr int MX_WAVES = 8;
+constexpr int MX_TM = 4;
+constexpr int MX_CODE_STAGE = A_BYTES + B_BYTES;               // 32 KB
+constexpr int MX_SG_BYTES = BM * 16;                            // one operand's scale group: 4 KB
+constexpr int MX_SCALE_OFF = NSTAGE * MX_CODE_STAGE;            // 128 KB
+constexpr int MX_SGROUPS = 3;
+constexpr int MX_LDS = MX_SCALE_OFF + MX_SGROUPS * 2 * MX_SG_BYTES;   // 152 KB
+
+template <int NW>
+struct MxOperand {
+  static constexpr int CL = 256 / (16 * NW);   // 16-row code loads per wave per stage
+  __amdgpu_buffer_rsrc_t codes, scales;
+  uint32_t code_off[CL];  // this lane's code offsets in stage 0
+  uint32_t scale_row;     // byte offset of row (lane) in the scales, for 64-row piece 0
+};
+
+template <int NW>
+__device__ __forceinline__ MxOperand<NW> mx_make_operand(const uint8_t* codes, const uint8_t* scales, int64_t rows_total,
+                                                     int64_t row0, int64_t K) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int64_t krow = K / 2, srow = K / 32;
+  int64_t nrows = rows_total - row0;
+  if (nrows > 256) nrows = 256;
+  MxOperand<NW> o;
+  constexpr int CL = MxOperand<NW>::CL;
+  o.codes = __builtin_amdgcn_make_buffer_rsrc((void*)(codes + row0 * krow), (short)0, (int)(nrows * krow), kRsrcWord3);
+  o.scales = __builtin_amdgcn_make_buffer_rsrc((void*)(scales + row0 * srow), (short)0, (int)(nrows * srow), kRsrcWord3);
+#pragma unroll
+  for (int j = 0; j < CL; j++) {
+    const int row = 16 * CL * w + 16 * j + (l >> 2);
+    o.code_off[j] = (uint32_t)(row * krow + (((l & 3) ^ swz(row)) * 16));
+  }
+  o.scale_row = (uint32_t)(l * srow);
+  return o;
+}
+
+// This wave's 256/NW rows of one operand's codes for absolute stage kt.
+template <int NW>
+__device__ __forceinline__ void mx_issue_codes(const MxOperand<NW>& o, uint8_t* codes_lds, int kt) {
+  constexpr int CL = MxOperand<NW>::CL;
+  const int w = threadIdx.x >> 6;
+  const uint32_t kb = (uint32_t)kt * ROWB;
+#pragma unroll
+  for (int j = 0; j < CL; j++)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(o.codes, (lds_void*)(codes_lds + (16 * CL * w + 16 * j) * ROWB), 16,
+                                             o.code_off[j] + kb, 0, 0, 0);
+}
+// Rows 64 piece .. +63 of a scale group starting at absolute stage kt_first:
+// 16 bytes (4 stages) per row.
+template <int NW>
+__device__ __forceinline__ void mx_issue_scale_piece(const MxOperand<NW>& o, uint8_t* group_lds, int piece, int kt_first,
+                                                     uint32_t srow) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(o.scales, (lds_void*)(group_lds + piece * 64 * 16), 16,
+                                           o.scale_row + (uint32_t)(64 * piece) * srow + (uint32_t)kt_first * 4u,
+                                           0, 0, 0);
+}
+
+template <int MX_TN>
+struct MxFrag {
+  v4i a[MX_TM], b[MX_TN];
+};
+
+// One wave's operand fragments of sub-step s (blocks 2g + s) of a stage.
+template <int MX_TN>
+__device__ __forceinline__ void mx_load_frag(const uint8_t* st, int ra0, int rb0, int offc, MxFrag<MX_TN>& f) {
+  const uint8_t* A = st;
+  const uint8_t* B = st + A_BYTES;
+#pragma unroll
+  for (int t = 0; t < MX_TM; t++) f.a[t] = *(const v4i*)(A + (ra0 + 32 * t) * ROWB + offc);
+#pragma unroll
+  for (int t = 0; t < MX_TN; t++) f.b[t] = *(const v4i*)(B + (rb0 + 32 * t) * ROWB + offc);
+}
+
+// Scale bytes of blocks 2g, 2g+1 of stage j (0..3) of a group, for each of the lane's rows.
+template <int MX_TN>
+__device__ __forceinline__ void mx_load_scales(const uint8_t* grp, int ra0, int rb0, int j, int g, int (&sa)[MX_TM],
+                                               int (&sb)[MX_TN]) {
+  const uint8_t* SA = grp;
+  const uint8_t* SB = grp + MX_SG_BYTES;
+#pragma unroll
+  for (int t = 0; t < MX_TM; t++) sa[t] = *(const uint16_t*)(SA + (ra0 + 32 * t) * 16 + 4 * j + 2 * g);
+#pragma unroll
+  for (int t = 0; t < MX_TN; t++) sb[t] = *(const uint16_t*)(SB + (rb0 + 32 * t) * 16 + 4 * j + 2 * g);
+}
+
+template <int S, int MX_TN>
+__device__ __forceinline__ void mx_mfma(v16f (&acc)[MX_TM][MX_TN], const MxFrag<MX_TN>& f, const int (&sa)[MX_TM],
+                                        const int (&sb)[MX_TN]) {
+#pragma unroll
+  for (int i = 0; i < MX_TM; i++) {
+    const v8i a = __builtin_shufflevector(f.a[i], f.a[i], 0, 1, 2, 3, -1, -1, -1, -1);
+#pragma unroll
+    for (int j = 0; j < MX_TN; j++) {
+      const v8i b = __builtin_shufflevector(f.b[j], f.b[j], 0, 1, 2, 3, -1, -1, -1, -1);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 4, 4, S, sa[i], S, sb[j]);
+    }
+  }
+}
+
+// Main loop, software-pipelined so that LDS reads always run under MFMAs:
+//   stage i:  read sub-step 1 fragments | MFMAs of sub-step 0
+//             wait for stage i+1, barrier, refill stage i's buffer with i+4
+//             read stage i+1 sub-step 0 | MFMAs of sub-step 1
+// Stage i's buffer is refilled right after the barrier that follows the last
+// read of it, so four buffers keep three stages of loads in flight.  The loop
+// body has no branches (stages past the end are loaded into buffers that are
+// never read again, and reads past the end are never consumed): a branch would
+// let the compiler sink the first MFMA group below the barrier.
+template <int NW>
+__global__ void __launch_bounds__(64 * NW, 1) gemm_mx_kernel(GemmArgs p) {
+  constexpr int MX_TN = 16 / NW;            // 4 waves: 128 x 128 per wave; 8 waves: 128 x 64
+  constexpr int WN = NW / 2;                 // waves along N
+  __shared__ __attribute__((aligned(16))) uint8_t smem[MX_LDS];
   int tm_, tn_;
   tile_coords(p, tm_, tn_);
   const int64_t m0 = (int64_t)tm_ * BM, n0 = (int64_t)tn_ * BN;
   const int z = blockIdx.y;
   const int kt0 = (int)((int64_t)p.k_tiles * z / p.splits), kt1 = (int)((int64_t)p.k_tiles * (z + 1) / p.splits);
+  const int nk = kt1 - kt0;
 
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 5;
-  const int wm = w >> 1, wn = w & 1;
-  // LDS byte offsets of this lane's operand rows (tile t adds t * 32 rows)
-  const int ra0 = wm * 128 + (l & 31), rb0 = wn * 128 + (l & 31);
-  const int zs = swz(ra0);            // equal for every t (t * 32 leaves bits 1..4 alone)
+  const int wm = w / WN, wn = w % WN;
+  const int ra0 = wm * 128 + (l & 31), rb0 = wn * (32 * MX_TN) + (l & 31);
+  const int zs = swz(ra0);            // equal for every t (t * 32 leaves bits 2..3 alone), and for rb0
   const int offc0 = ((2 * g + 0) ^ zs) << 4, offc1 = ((2 * g + 1) ^ zs) << 4;
 
-  v16f acc[4][4];
+  v16f acc[MX_TM][MX_TN];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < MX_TM; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = (v16f){};
+    for (int j = 0; j < MX_TN; j++) acc[i][j] = (v16f){};
 
-  gemm_mainloop<4, 10>(p, smem, m0, n0, kt0, kt1, [&](const uint8_t* st) {
-    const uint8_t* A = st;
-    const uint8_t* B = st + A_BYTES;
-    const uint8_t* SA = st + A_BYTES + B_BYTES;
-    const uint8_t* SB = SA + SA_BYTES;
-    int sa[4], sb[4];
+  if (nk > 0) {
+    // buffer->LDS instructions per wave per stage: the code loads, plus one
+    // scale piece on waves 0 and 1.  Waiting for "at most 2 * LOADS
+    // outstanding" is exact for the other waves and slightly conservative for
+    // waves 0 and 1.
+    constexpr int LOADS = 2 * MxOperand<NW>::CL;
+    const uint32_t srow = (uint32_t)(p.K / 32);
+    const MxOperand<NW> oa = mx_make_operand<NW>(p.a, p.as, p.M, m0, p.K);
+    const MxOperand<NW> ob = mx_make_operand<NW>(p.b, p.bs, p.N, n0, p.K);
+    auto stage = [&](int i) { return smem + (i & (NSTAGE - 1)) * MX_CODE_STAGE; };
+    auto group = [&](int h) { return smem + MX_SCALE_OFF + (h % MX_SGROUPS) * 2 * MX_SG_BYTES; };
+    // stage i's codes, and scale piece i % 4 of group i / 4 + 1.  Stages and
+    // groups at or past the end load whatever lies there (in bounds of the
+    // operand buffers, or zero past them) into buffers that are never read.
+    auto issue = [&](int i) {
+      uint8_t* st = stage(i);
+      mx_issue_codes(oa, st, kt0 + i);
+      mx_issue_codes(ob, st + A_BYTES, kt0 + i);
+      const int h = (i >> 2) + 1;
+      if (w == 0) mx_issue_scale_piece(oa, group(h), i & 3, kt0 + 4 * h, srow);
+      if (w == 1) mx_issue_scale_piece(ob, group(h) + MX_SG_BYTES, i & 3, kt0 + 4 * h, srow);
+    };
+    // prologue: scale group 0 (8 pieces spread over the waves), then stages 0..2
 #pragma unroll
-    for (int t = 0; t < 4; t++) {
-      sa[t] = *(const uint16_t*)(SA + (ra0 + 32 * t) * 4 + 2 * g);
-      sb[t] = *(const uint16_t*)(SB + (rb0 + 32 * t) * 4 + 2 * g);
+    for (int q = 0; q < 8 / NW; q++) {
+      const int piece = w * (8 / NW) + q;
+      if (piece < 4) mx_issue_scale_piece(oa, group(0), piece, kt0, srow);
+      else mx_issue_scale_piece(ob, group(0) + MX_SG_BYTES, piece - 4, kt0, srow);
     }
+    issue(0);
+    issue(1);
+    issue(2);
+    wait_cnt<2 * LOADS, 15>();
+    block_barrier();
+    issue(3);
+
+    MxFrag<MX_TN> f0, f1;
+    int sa[MX_TM], sb[MX_TN], sa_n[MX_TM], sb_n[MX_TN];
+    mx_load_scales(group(0), ra0, rb0, 0, g, sa, sb);
+    mx_load_frag(stage(0), ra0, rb0, offc0, f0);
+    for (int i = 0; i < nk; i++) {
+      // phase A: sub-step 1 fragment reads under the sub-step 0 MFMAs
+      mx_load_frag(stage(i), ra0, rb0, offc1, f1);
+      mx_mfma<0>(acc, f0, sa, sb);
 #pragma unroll
-    for (int s = 0; s < 2; s++) {
-      const int offc = s ? offc1 : offc0;
-      v8i af[4], bf[4];
-#pragma unroll
-      for (int t = 0; t < 4; t++) {
-        v4i x = *(const v4i*)(A + (ra0 + 32 * t) * ROWB + offc);
-        v4i y = *(const v4i*)(B + (rb0 + 32 * t) * ROWB + offc);
-        af[t] = __builtin_shufflevector(x, x, 0, 1, 2, 3, -1, -1, -1, -1);
-        bf[t] = __builtin_shufflevector(y, y, 0, 1, 2, 3, -1, -1, -1, -1);
+      for (int q = 0; q < MX_TM + MX_TN; q++) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, MX_TN / 2 + 1, 0);   // MFMAs
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // stage i+1 has landed for this wave, and its own reads of stage i are done
+      wait_cnt<2 * LOADS, 0>();
+      block_barrier();
+      issue(i + 4);
+      __builtin_amdgcn_sched_barrier(0);
+      // phase B: scales and sub-step 0 fragments of stage i+1 under sub-step 1
+      mx_load_scales(group((i + 1) >> 2), ra0, rb0, (i + 1) & 3, g, sa_n, sb_n);
+      mx_load_frag(stage(i + 1), ra0, rb0, offc0, f0);
+      mx_mfma<1>(acc, f1, sa, sb);
 #pragma unroll
-      for (int i = 0; i < 4; i++)
+      for (int q = 0; q < 2 * (MX_TM + MX_TN); q++) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          if (s == 0)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 4, 4, 0, sa[i], 0, sb[j]);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 4, 4, 1, sa[i], 1, sb[j]);
-        }
+      for (int t = 0; t < MX_TM; t++) sa[t] = sa_n[t];
+#pragma unroll
+      for (int t = 0; t < MX_TN; t++) sb[t] = sb_n[t];
     }
-  });
+    wait_cnt<0, 0>();   // nothing may still write LDS when the workgroup exits
+  }
+  // epilogue
   float* Cz = p.C + (int64_t)z * p.split_stride;
-  store_acc(p, Cz, p.ldc, m0, n0, wm, wn, acc, 1.0f);
+#pragma unroll
+  for (int tm = 0; tm < MX_TM; tm++) {
+#pragma unroll
+    for (int tn = 0; tn < MX_TN; tn++) {
+      const int64_t n = n0 + wn * (32 * MX_TN) + tn * 32 + (l & 31);
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        const int64_t m = m0 + wm * 128 + tm * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+        if (m < p.M) Cz[m * p.ldc + n] = acc[tm][tn][v];
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -313,7 +505,7 @@ __global__ void __launch_bounds__(256, 1) gemm_nv_kernel(GemmArgs p) {
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 5;
   const int wm = w >> 1, wn = w & 1;
   const int ra0 = wm * 128 + (l & 31), rb0 = wn * 128 + (l & 31);
-  const int zs = swz(ra0);
+  const int zs = swz(ra0);            // equal for every t (t * 32 leaves bits 2..3 alone)
   const int offc0 = ((2 * g + 0) ^ zs) << 4, offc1 = ((2 * g + 1) ^ zs) << 4;
 
   v16f acc[4][4];
@@ -420,7 +612,7 @@ static hipError_t launch_gemm_common(bool nv, GemmArgs p, float* C, int64_t ldc,
   }
   dim3 grid((unsigned)(p.ntm * p.ntn), (unsigned)plan.splits);
   if (nv) hipLaunchKernelGGL(gemm_nv_kernel, grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(gemm_mx_kernel, grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(gemm_mx_kernel<MX_WAVES>, grid, dim3(64 * MX_WAVES), 0, stream, p);
   if (plan.splits > 1) {
     int64_t work = p.M * p.N;
     int64_t g = (work + 255) / 256;
