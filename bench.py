@@ -39,21 +39,95 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "gemm_mx_traffic.json"),
-                    help="HBM bytes per GEMM launch from rocprofv3 counters (optional)")
+    ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "gemm_mx_headline_traffic.txt"),
+                    help="HBM bytes per GEMM launch from rocprofv3 counters (written by --summarize-pmc)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 256 MiB device copy first (calibrates the PMC byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into the traffic file")
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "OUT_MD"),
+                    help="turn a rocprofv3 --stats kernel_stats.csv into a short markdown summary")
     return ap.parse_args()
+
+
+GEMM_SRC = os.path.join(ROOT, "microscaling_fp4_quantized_block_amd", "csrc", "gemm.hip")
+COPY_BYTES = 1 << 30
+
+
+def source_digest(path=GEMM_SRC):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def gemm_traffic(path):
     """HBM bytes per launch of the GEMM kernel measured with rocprofv3 PMC
-    counters (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration);
-    None when not measured for the current kernel."""
+    counters (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads
+    for a plain copy of known size); None when the file is missing or was
+    measured on a different GEMM source."""
     try:
         with open(path) as f:
-            d = json.load(f)
-        return float(d["bytes_per_launch"]) if d.get("current", False) else None
-    except (OSError, ValueError, KeyError):
+            d = json.loads(f.read().split("\n", 1)[1])
+        if d.get("gemm_source_sha256_16") != source_digest():
+            return None
+        return float(d["bytes_per_launch"])
+    except (OSError, ValueError, KeyError, IndexError):
         return None
+
+
+def _pmc_per_kernel(run_dir, counter):
+    """Average per-dispatch value of `counter` for each kernel name in a
+    rocprofv3 --pmc csv run directory."""
+    import csv
+    import glob
+    vals = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                vals.setdefault(r["Kernel_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+                vals[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: (sum(v.values()) / len(v), len(v)) for k, v in vals.items()}
+
+
+def summarize_pmc(fetch_dir, write_dir, out_path):
+    fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_dir, "WRITE_SIZE")
+    pick = lambda d, key: next(v for k, v in d.items() if key(k))
+    is_gemm = lambda k: "gemm_mx_kernel" in k
+    # the copy is the elementwise kernel with the largest counts (the fills of
+    # the calibration and eviction buffers are separate, smaller or write-only)
+    is_copy = lambda k: "elementwise" in k.lower() and "fill" not in k.lower()
+    cands_f = [v[0] for k, v in fetch.items() if is_copy(k)]
+    cands_w = [v[0] for k, v in write.items() if is_copy(k)]
+    g_f, g_w = pick(fetch, is_gemm)[0], pick(write, is_gemm)[0]
+    c_f, c_w = max(cands_f), max(cands_w)
+    f_scale, w_scale = COPY_BYTES / c_f, COPY_BYTES / c_w     # bytes per counter unit
+    fetched, written = g_f * f_scale, g_w * w_scale
+    algorithmic = M * K // 2 + N * K // 2 + (M + N) * K // 32 + 4 * M * N
+    d = {"bytes_per_launch": fetched + written, "fetched_bytes": fetched, "written_bytes": written,
+         "algorithmic_bytes": algorithmic, "copy_calibration": {"bytes": COPY_BYTES, "fetch_counter": c_f,
+                                                                "write_counter": c_w},
+         "gemm_counters": {"FETCH_SIZE": g_f, "WRITE_SIZE": g_w},
+         "gemm_source_sha256_16": source_digest()}
+    with open(out_path, "w") as f:
+        f.write("HBM traffic of gemm_mx_kernel, 4096x14336x8192 MXFP4 (rocprofv3 PMC FETCH_SIZE / WRITE_SIZE, "
+                "scaled by a 1 GiB copy; commands in profiles/README.md)\n")
+        f.write(json.dumps(d, indent=1) + "\n")
+    print(json.dumps(d, indent=1))
+
+
+def summarize_stats(stats_csv, out_md):
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    with open(out_md, "w") as f:
+        f.write("| kernel | calls | average us | min us | max us | share % |\n|---|---|---|---|---|---|\n")
+        for r in rows:
+            f.write("| %s | %s | %.1f | %.1f | %.1f | %.1f |\n" % (
+                r["Name"][:90], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    print(open(out_md).read())
 
 
 def cpu_baseline():
@@ -89,6 +163,12 @@ def cpu_baseline():
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.traffic_file)
+        return
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs on a single "
               "MI355X; see the sharding note in DESIGN.md)", file=sys.stderr)
@@ -98,6 +178,16 @@ def main():
     import microscaling_fp4_quantized_block_amd as mx
 
     dev = torch.device("cuda", 0)
+    if args.copy_calibration:
+        # a plain elementwise copy of COPY_BYTES whose source is not cache
+        # resident (a 512 MiB write in between evicts the 256 MiB MALL)
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        evict = torch.zeros((512 << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)          # one elementwise kernel: reads and writes COPY_BYTES
+        torch.cuda.synchronize()
+        del src, dst, evict
     A_bits = workloads.make_tensor(0, "A")
     B_bits = workloads.make_tensor(0, "B")
     A = torch.from_numpy(A_bits.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -142,7 +232,7 @@ def main():
     gemm_tflops = flops / (g_ms * 1e-3) / 1e12
     qa_gbps = M * K * MX_BYTES_PER_ELEM / (qa_ms * 1e-3) / 1e9
     qb_gbps = N * K * MX_BYTES_PER_ELEM / (qb_ms * 1e-3) / 1e9
-    traffic = gemm_traffic(args.traffic_json)
+    traffic = gemm_traffic(args.traffic_file)
     out = {
         "metric": METRIC,
         "value": round(flops / (ms_per_step * 1e-3) / 1e12, 1),

@@ -104,7 +104,7 @@ mxfp4_status mxfp4_quantize_workspace_bytes(int fmt, int64_t R, int64_t C, int a
  * out: caller-filled descriptor; out->rows, out->k and out->fmt must match the
  *      call, and out->hadamard is compared with hadamard; codes/scales (and
  *      tensor_scale for NVFP4) must be non-NULL device buffers of the sizes
- *      mxfp4_tensor_bytes reports.
+ *      mxfp4_tensor_bytes reports; codes must be 16-byte aligned.
  * k must be a multiple of the block size, and of 32 when hadamard = 1.
  * Blocks holding a NaN or infinity get the format's NaN scale byte (0xFF for
  * E8M0, 0x7F for E4M3) and all-zero codes.
@@ -130,10 +130,13 @@ mxfp4_status mxfp4_gemm_workspace_bytes(const mxfp4_tensor *A, const mxfp4_tenso
  * [N, k], both quantized along k (the three GEMMs of a linear layer -- XW^T,
  * dY.W and dY^T.X -- are all this call on operands quantized with the axis
  * that puts their contraction last).  MXFP4 runs on the CDNA4 block-scaled
- * FP4 matrix cores; NVFP4 dequantizes exactly to bf16 in registers and
- * applies both tensor scales in the epilogue.
- * C: device, row-major, ldc >= N.  k must be a multiple of 128 (MXFP4) or
- * 64 (NVFP4); fmt, k and hadamard of A and B must agree (FORMAT_MISMATCH).
+ * FP4 matrix cores; NVFP4 dequantizes exactly to fp16 in registers (an
+ * E2M1 x E4M3 product has at most 6 significant bits) for the fp16 matrix
+ * cores and applies both tensor scales in the epilogue.
+ * C: device, row-major, ldc >= N.  k must be a multiple of 128
+ * (UNSUPPORTED_SHAPE otherwise); fmt, k and hadamard of A and B must agree
+ * (FORMAT_MISMATCH).  A->codes and B->codes must be 16-byte aligned and the
+ * scales 4-byte aligned (INVALID_ARG otherwise).
  * workspace: device, at least mxfp4_gemm_workspace_bytes (NULL if 0). */
 mxfp4_status mxfp4_gemm(const mxfp4_tensor *A, const mxfp4_tensor *B, float *C, int64_t ldc,
                         void *workspace, size_t ws_bytes, hipStream_t stream);

@@ -93,8 +93,8 @@ static mxfp4_status check_gemm_operands(const mxfp4_tensor* A, const mxfp4_tenso
   if (!A || !B || !fmt_ok(A->fmt) || !fmt_ok(B->fmt) || A->rows < 0 || B->rows < 0 || A->k < 0 || B->k < 0)
     return MXFP4_ERR_INVALID_ARG;
   if (A->fmt != B->fmt || A->k != B->k || A->hadamard != B->hadamard) return MXFP4_ERR_FORMAT_MISMATCH;
-  const int kmul = A->fmt == MXFP4_FMT_MX ? 128 : 64;
-  if (A->k % kmul != 0) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  // the kernels' contraction step is 128 (one 64-byte chunk of codes per row)
+  if (A->k % 128 != 0) return MXFP4_ERR_UNSUPPORTED_SHAPE;
   return MXFP4_OK;
 }
 
