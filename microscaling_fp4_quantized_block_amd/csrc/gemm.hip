@@ -81,14 +81,19 @@ struct GemmArgs {
 // Tile order: consecutive workgroup ids go to consecutive XCDs, so gather
 // the ids one XCD receives into a contiguous range, then walk that range in
 // groups of GROUP_M tile rows.
+#ifndef MXFP4_GROUP_M
+#define MXFP4_GROUP_M 4
+#endif
 __device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn) {
   const int ntiles = p.ntm * p.ntn;
   int id = blockIdx.x;
+#ifndef MXFP4_NO_XCD_REMAP
   if ((ntiles & 7) == 0) {
     const int per = ntiles >> 3;
     id = (id & 7) * per + (id >> 3);
   }
-  constexpr int GROUP_M = 4;
+#endif
+  constexpr int GROUP_M = MXFP4_GROUP_M;
   const int group = id / (GROUP_M * p.ntn);
   const int first_m = group * GROUP_M;
   const int gm = min(p.ntm - first_m, GROUP_M);
@@ -236,6 +241,66 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Epilogue of a wave's TM x TN grid of 32x32 fp32 accumulators whose top-left
+// output is (mb, nb).  In an accumulator, lane l holds column l % 32 and rows
+// 8 (v / 4) + 4 (l / 32) + v % 4 (v = 0..15): four consecutive rows of one
+// column per group of four registers.  A 4x4 transpose across each quad of
+// lanes (two DPP exchange steps) turns that into one row and four consecutive
+// columns per lane, written with one 16-byte store: a quarter of the store
+// instructions, each covering whole 128-byte row segments.  Ragged edges and
+// unaligned outputs use 4-byte stores.
+__device__ __forceinline__ float dpp_xor1_f(float v) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)__float_as_uint(v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_xor2_f(float v) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)__float_as_uint(v), 0x4E, 0xF, 0xF, true));
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void store_tile_f32x4(const GemmArgs& p, float* Cz, int64_t mb, int64_t nb,
+                                                 const v16f (&acc)[TM][TN]) {
+  const int l = threadIdx.x & 63, g = l >> 5, c = l & 3;
+  const bool vec_ok = ((p.ldc & 3) == 0) && ((((uintptr_t)Cz) & 15) == 0);
+#pragma unroll
+  for (int tm = 0; tm < TM; tm++) {
+#pragma unroll
+    for (int tn = 0; tn < TN; tn++) {
+      const int64_t ncol0 = nb + tn * 32 + (l & 31);          // this lane's column before the transpose
+      const int64_t nq = nb + tn * 32 + (l & 28);             // first column of the lane's quad
+#pragma unroll
+      for (int a = 0; a < 4; a++) {
+        float x[4], z[4], y[4];
+#pragma unroll
+        for (int b = 0; b < 4; b++) x[b] = acc[tm][tn][4 * a + b];
+        // stage 1: keep x[k] where k and c agree in bit 0, else take the partner lane's x[k ^ 1]
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          const float o = dpp_xor1_f(x[k ^ 1]);
+          z[k] = ((k ^ c) & 1) ? o : x[k];
+        }
+        // stage 2: the same on bit 1 with the lane two apart
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          const float o = dpp_xor2_f(z[k ^ 2]);
+          y[k] = ((k ^ c) & 2) ? o : z[k];
+        }
+        // lane c of the quad now holds row 8a + 4g + c, columns nq .. nq+3
+        const int64_t m = mb + tm * 32 + 8 * a + 4 * g + c;
+        if (vec_ok && nq + 3 < p.N) {
+          if (m < p.M) *(float4*)(Cz + m * p.ldc + nq) = make_float4(y[0], y[1], y[2], y[3]);
+        } else {
+          // ragged or unaligned: the untransposed values, one column per lane
+#pragma unroll
+          for (int b = 0; b < 4; b++) {
+            const int64_t mm = mb + tm * 32 + 8 * a + 4 * g + b;
+            if (mm < p.M && ncol0 < p.N) Cz[mm * p.ldc + ncol0] = x[b];
+          }
+        }
+      }
+    }
+  }
+}
+
 // The MXFP4 kernel runs 8 waves per workgroup (2 per SIMD): one wave per SIMD
 // cannot keep enough loads in flight (measured on gfx950: about 40 GB/s per
 // CU from L2 with 4 waves, 65 GB/s with 8), and the second wave per SIMD hides
@@ -253,7 +318,8 @@ constexpr int MX_CODE_STAGE = A_BYTES + B_BYTES;               // 32 KB
 constexpr int MX_SG_BYTES = BM * 16;                            // one operand's scale group: 4 KB
 constexpr int MX_SCALE_OFF = NSTAGE * MX_CODE_STAGE;            // 128 KB
 constexpr int MX_SGROUPS = 3;
-constexpr int MX_LDS = MX_SCALE_OFF + MX_SGROUPS * 2 * MX_SG_BYTES;   // 152 KB
+constexpr int MX_SPARE_OFF = MX_SCALE_OFF + MX_SGROUPS * 2 * MX_SG_BYTES;   // 152 KB
+constexpr int MX_LDS = MX_SPARE_OFF + 6 * 1024;                             // + 1 KB sink per wave 2..7
 
 template <int NW>
 struct MxOperand {
@@ -295,13 +361,17 @@ __device__ __forceinline__ void mx_issue_codes(const MxOperand<NW>& o, uint8_t* 
                                              o.code_off[j] + kb, 0, 0, 0);
 }
 // Rows 64 piece .. +63 of a scale group starting at absolute stage kt_first:
-// 16 bytes (4 stages) per row.
+// 16 bytes (4 stages) per row, from `rsrc` into `dst` (1 KB).
+__device__ __forceinline__ void mx_issue_scale_piece_to(__amdgpu_buffer_rsrc_t rsrc, uint32_t scale_row, uint8_t* dst,
+                                                        int piece, int kt_first, uint32_t srow) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16,
+                                           scale_row + (uint32_t)(64 * piece) * srow + (uint32_t)kt_first * 4u,
+                                           0, 0, 0);
+}
 template <int NW>
 __device__ __forceinline__ void mx_issue_scale_piece(const MxOperand<NW>& o, uint8_t* group_lds, int piece, int kt_first,
                                                      uint32_t srow) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(o.scales, (lds_void*)(group_lds + piece * 64 * 16), 16,
-                                           o.scale_row + (uint32_t)(64 * piece) * srow + (uint32_t)kt_first * 4u,
-                                           0, 0, 0);
+  mx_issue_scale_piece_to(o.scales, o.scale_row, group_lds + piece * 64 * 16, piece, kt_first, srow);
 }
 
 template <int MX_TN>
@@ -367,7 +437,8 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_mx_kernel(GemmArgs p) {
   const int kt0 = (int)((int64_t)p.k_tiles * z / p.splits), kt1 = (int)((int64_t)p.k_tiles * (z + 1) / p.splits);
   const int nk = kt1 - kt0;
 
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, g = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar branches
+  const int l = threadIdx.x & 63, g = l >> 5;
   const int wm = w / WN, wn = w % WN;
   const int ra0 = wm * 128 + (l & 31), rb0 = wn * (32 * MX_TN) + (l & 31);
   const int zs = swz(ra0);            // equal for every t (t * 32 leaves bits 2..3 alone), and for rb0
@@ -380,14 +451,20 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_mx_kernel(GemmArgs p) {
     for (int j = 0; j < MX_TN; j++) acc[i][j] = (v16f){};
 
   if (nk > 0) {
-    // buffer->LDS instructions per wave per stage: the code loads, plus one
-    // scale piece on waves 0 and 1.  Waiting for "at most 2 * LOADS
-    // outstanding" is exact for the other waves and slightly conservative for
-    // waves 0 and 1.
-    constexpr int LOADS = 2 * MxOperand<NW>::CL;
+    // buffer->LDS instructions per wave per stage: the code loads plus one
+    // scale load.  Waves 0 and 1 load the scale pieces; the other waves issue
+    // the same instruction on an empty buffer (out of range: no memory
+    // traffic, zeros into a private LDS sink), so every wave has the same
+    // count and "at most 2 * LOADS outstanding" is exact.
+    constexpr int LOADS = 2 * MxOperand<NW>::CL + 1;
     const uint32_t srow = (uint32_t)(p.K / 32);
     const MxOperand<NW> oa = mx_make_operand<NW>(p.a, p.as, p.M, m0, p.K);
     const MxOperand<NW> ob = mx_make_operand<NW>(p.b, p.bs, p.N, n0, p.K);
+    const __amdgpu_buffer_rsrc_t srsrc =
+        w == 0 ? oa.scales : w == 1 ? ob.scales : __builtin_amdgcn_make_buffer_rsrc((void*)p.as, (short)0, 0, kRsrcWord3);
+    // scale destinations as arithmetic on wave-uniform values (no branches in the loop)
+    const int sc_real = w < 2 ? 1 : 0;
+    uint8_t* const sc_base = sc_real ? smem + MX_SCALE_OFF + w * MX_SG_BYTES : smem + MX_SPARE_OFF + (w - 2) * 1024;
     auto stage = [&](int i) { return smem + (i & (NSTAGE - 1)) * MX_CODE_STAGE; };
     auto group = [&](int h) { return smem + MX_SCALE_OFF + (h % MX_SGROUPS) * 2 * MX_SG_BYTES; };
     // stage i's codes, and scale piece i % 4 of group i / 4 + 1.  Stages and
@@ -398,8 +475,8 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_mx_kernel(GemmArgs p) {
       mx_issue_codes(oa, st, kt0 + i);
       mx_issue_codes(ob, st + A_BYTES, kt0 + i);
       const int h = (i >> 2) + 1;
-      if (w == 0) mx_issue_scale_piece(oa, group(h), i & 3, kt0 + 4 * h, srow);
-      if (w == 1) mx_issue_scale_piece(ob, group(h) + MX_SG_BYTES, i & 3, kt0 + 4 * h, srow);
+      uint8_t* sdst = sc_base + sc_real * ((h % MX_SGROUPS) * 2 * MX_SG_BYTES + (i & 3) * 1024);
+      mx_issue_scale_piece_to(srsrc, oa.scale_row, sdst, i & 3, kt0 + 4 * h, srow);
     };
     // prologue: scale group 0 (8 pieces spread over the waves), then stages 0..2
 #pragma unroll
@@ -433,17 +510,21 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_mx_kernel(GemmArgs p) {
       // stage i+1 has landed for this wave, and its own reads of stage i are done
       wait_cnt<2 * LOADS, 0>();
       block_barrier();
+      // phase B: the loads of stage i+4, and the scales and sub-step 0
+      // fragments of stage i+1, spread under the sub-step 1 MFMAs.  A load
+      // instruction can stall its wave while the memory pipeline is full, so
+      // each one is separated by MFMAs already queued.
       issue(i + 4);
-      __builtin_amdgcn_sched_barrier(0);
-      // phase B: scales and sub-step 0 fragments of stage i+1 under sub-step 1
       mx_load_scales(group((i + 1) >> 2), ra0, rb0, (i + 1) & 3, g, sa_n, sb_n);
       mx_load_frag(stage(i + 1), ra0, rb0, offc0, f0);
       mx_mfma<1>(acc, f1, sa, sb);
 #pragma unroll
-      for (int q = 0; q < 2 * (MX_TM + MX_TN); q++) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      for (int q = 0; q < LOADS; q++) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one buffer->LDS load
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -455,19 +536,7 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_mx_kernel(GemmArgs p) {
   }
   // epilogue
   float* Cz = p.C + (int64_t)z * p.split_stride;
-#pragma unroll
-  for (int tm = 0; tm < MX_TM; tm++) {
-#pragma unroll
-    for (int tn = 0; tn < MX_TN; tn++) {
-      const int64_t n = n0 + wn * (32 * MX_TN) + tn * 32 + (l & 31);
-      if (n >= p.N) continue;
-#pragma unroll
-      for (int v = 0; v < 16; v++) {
-        const int64_t m = m0 + wm * 128 + tm * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-        if (m < p.M) Cz[m * p.ldc + n] = acc[tm][tn][v];
-      }
-    }
-  }
+  store_tile_f32x4<MX_TM, MX_TN>(p, Cz, m0 + wm * 128, n0 + wn * (32 * MX_TN), acc);
 }
 
 // ---------------------------------------------------------------------------
