@@ -45,7 +45,7 @@ mxfp4_status mxfp4_tensor_bytes(int fmt, int64_t rows, int64_t k, size_t* codes_
 
 mxfp4_status mxfp4_quantize_workspace_bytes(int fmt, int64_t R, int64_t C, int axis, size_t* bytes) {
   if (!fmt_ok(fmt) || R < 0 || C < 0 || (axis != 0 && axis != 1) || !bytes) return MXFP4_ERR_INVALID_ARG;
-  *bytes = (fmt == MXFP4_FMT_NV) ? (size_t)mxfp4::kAmaxPartials * sizeof(uint32_t) : 0;
+  *bytes = mxfp4::quantize_workspace_bytes(fmt, R, C);
   return MXFP4_OK;
 }
 
@@ -68,7 +68,7 @@ mxfp4_status mxfp4_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx
   uint32_t* partials = nullptr;
   if (fmt == MXFP4_FMT_NV) {
     if (!out->tensor_scale) return MXFP4_ERR_INVALID_ARG;
-    if (!workspace || ws_bytes < (size_t)mxfp4::kAmaxPartials * sizeof(uint32_t) || !aligned(workspace, 4))
+    if (!workspace || ws_bytes < mxfp4::quantize_workspace_bytes(fmt, R, C) || !aligned(workspace, 4))
       return MXFP4_ERR_WORKSPACE;
     partials = (uint32_t*)workspace;
   }

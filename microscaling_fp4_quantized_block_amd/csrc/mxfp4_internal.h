@@ -5,9 +5,16 @@
 
 namespace mxfp4 {
 
-// Upper bound on the tensor-amax partials (one per workgroup of the amax
-// pass); the NVFP4 quantize workspace holds this many 32-bit words.
-constexpr int kAmaxPartials = 1024;
+// Work per workgroup of the quantizer kernels, in 16-byte (8-element) chunks:
+// the row quantizer and the NVFP4 tensor-amax scan use an exact grid.
+constexpr int kRowChunksPerWG = 512;
+constexpr int kAmaxChunksPerWG = 2048;
+// Workgroups (and partial maxima) of the rotated tensor-amax pass.
+constexpr int kAmaxRotPartials = 1024;
+
+// Workspace of mxfp4_quantize: one 32-bit partial maximum per workgroup of
+// the NVFP4 tensor-amax pass (0 bytes for MXFP4).
+size_t quantize_workspace_bytes(int fmt, int64_t R, int64_t C);
 
 hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int fmt, int rounding,
                            int hadamard, int axis, uint64_t seed, uint8_t* codes, uint8_t* scales,

@@ -88,7 +88,7 @@ __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w <
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // ---------------------------------------------------------------------------
-// NVFP4 tensor scale from the tensor-amax partials.
+// NVFP4 tensor scale.
 // s_t = RN(amax / 2688), 1 for an all-zero tensor, kept >= 2^-117 so that
 // s_b * s_t (s_b >= 2^-9) stays a normal binary32 number.
 // ---------------------------------------------------------------------------
@@ -97,25 +97,6 @@ __device__ __forceinline__ float nv_tensor_scale_from_amax_bits(uint32_t amax_bi
   if (!(amax > 0.0f)) return 1.0f;
   float st = __fdiv_rn(amax, 2688.0f);
   return st < 0x1p-117f ? 0x1p-117f : st;
-}
-
-// Every workgroup of the quantize pass reduces the (few hundred) partial
-// maxima itself; workgroup 0 publishes s_t.  Runs before any other work.
-__device__ float load_tensor_scale(const uint32_t* partials, int nparts, float* ts_out) {
-  __shared__ float s_ts;
-  if (threadIdx.x < 64) {
-    uint32_t m = 0;
-    for (int i = threadIdx.x; i < nparts; i += 64) m = max(m, partials[i]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-    if (threadIdx.x == 0) {
-      float st = nv_tensor_scale_from_amax_bits(m);
-      s_ts = st;
-      if (blockIdx.x == 0 && blockIdx.y == 0) ts_out[0] = st;
-    }
-  }
-  __syncthreads();
-  return s_ts;
 }
 
 // Per NVFP4 block: scale byte and the reciprocal used on the elements.
@@ -129,50 +110,146 @@ __device__ __forceinline__ void nv_block_scale(float amax, float st, uint32_t& b
   inv = byte ? __fdiv_rn(1.0f, d) : 0.0f;
 }
 
+// Division of a 32-bit index by a divisor fixed for the launch
+// (Granlund & Montgomery: q = (umulhi(n, m) + n) >> s, the sum in 64 bits).
+struct FastDiv {
+  uint32_t d, m, s;
+};
+static FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while ((1ull << s) < d) s++;
+  const uint64_t m = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
+  return FastDiv{d, (uint32_t)m, s};
+}
+__device__ __forceinline__ uint32_t fastdiv(uint32_t n, const FastDiv& f) {
+  const uint32_t hi = __umulhi(n, f.m);
+  return (uint32_t)(((uint64_t)hi + n) >> f.s);
+}
+
+// ---------------------------------------------------------------------------
+// Encoding of 8 consecutive contraction elements of one block into a 32-bit
+// word of codes (element j in bits 4j+3..4j), given the block's scale byte.
+//   MXFP4 RTN: the hardware FP4 conversion of y / 2^e (nearest-even,
+//              saturating); bf16 inputs go in directly as packed pairs.
+//   NVFP4:     x' = RN(y * inv) (+-0 for a zero scale), then RTN (conversion
+//              with unit scale) or SR.
+//   SR:        16 bits per element from the lane's Philox block rw.
+// ---------------------------------------------------------------------------
+template <int FMT, int RND, bool BF16IN>
+__device__ __forceinline__ uint32_t encode8(const float y[8], const uint32_t w[4], uint32_t byte, float mul,
+                                            const uint32_t rw[4]) {
+  uint32_t packed = 0;
+  if (FMT == FMT_MX && RND == RND_RTN) {
+    const float sc = e8m0_as_cvt_scale(byte);
+    if (BF16IN) {
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2, w[0]), sc, 0);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2, w[1]), sc, 1);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2, w[2]), sc, 2);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2, w[3]), sc, 3);
+    } else {
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[0], y[1], sc, 0);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[2], y[3], sc, 1);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[4], y[5], sc, 2);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[6], y[7], sc, 3);
+    }
+    return packed;
+  }
+  float xs[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    if (FMT == FMT_MX) xs[j] = y[j] * mul;                      // exact: mul is a power of two
+    else xs[j] = byte ? y[j] * mul : __builtin_copysignf(0.0f, y[j]);
+  }
+  if (RND == RND_RTN) {
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, xs[0], xs[1], 1.0f, 0);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, xs[2], xs[3], 1.0f, 1);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, xs[4], xs[5], 1.0f, 2);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, xs[6], xs[7], 1.0f, 3);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const uint32_t rnd = (rw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+      packed |= sr_code(xs[j], rnd) << (4 * j);
+    }
+  }
+  return packed;
+}
+
+// Scale byte and element multiplier of a block from its absmax bit pattern.
+template <int FMT>
+__device__ __forceinline__ void block_scale(uint32_t amax_bits, float st, uint32_t& byte, float& mul, bool& nonfinite) {
+  nonfinite = amax_bits >= 0x7F800000u;
+  if (FMT == FMT_MX) {
+    byte = nonfinite ? 0xFFu : mx_scale_byte_from_f32bits(amax_bits);
+    mul = mx_inv_scale(byte);
+  } else if (nonfinite) {
+    byte = 0x7Fu;
+    mul = 0.0f;
+  } else {
+    nv_block_scale(__uint_as_float(amax_bits), st, byte, mul);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Tensor amax pass (NVFP4): largest finite |y| over the tensor, y the input
 // or its block rotation.  Each workgroup writes one partial (binary32 bits;
-// non-negative floats order like unsigned integers).
+// non-negative floats order like unsigned integers); a one-workgroup
+// finalize reduces them into s_t.
 // ---------------------------------------------------------------------------
-template <bool VEC>
-__global__ void __launch_bounds__(256) amax_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
-                                                   int64_t ldx, uint32_t* __restrict__ partials) {
-  uint32_t m = 0;
-  const int64_t cpr = (C + 7) / 8;                 // 8-element chunks per row (last may be partial)
-  const int64_t total = R * cpr;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
-    const int64_t i = t / cpr, q = t - i * cpr;
-    const uint16_t* src = x + i * ldx + q * 8;
-    uint32_t w[4];
-    if (VEC) {
-      u32v4 v = __builtin_nontemporal_load((const u32v4*)src);
-      w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
-    } else {
-      const int n = (C - q * 8) < 8 ? (int)(C - q * 8) : 8;
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        uint32_t lo = (2 * j < n) ? src[2 * j] : 0u, hi = (2 * j + 1 < n) ? src[2 * j + 1] : 0u;
-        w[j] = lo | (hi << 16);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
-      if (lo < 0x7F80u) m = max(m, lo << 16);
-      if (hi < 0x7F80u) m = max(m, hi << 16);
-    }
-  }
-  __shared__ uint32_t red[4];
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t m) {
+  __shared__ uint32_t red[16];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = red[0];
-    for (int k = 1; k < (int)(blockDim.x >> 6); k++) r = max(r, red[k]);
-    partials[blockIdx.x] = r;
+  uint32_t r = red[0];
+  for (int k = 1; k < (int)(blockDim.x >> 6); k++) r = max(r, red[k]);
+  return r;
+}
+
+__device__ __forceinline__ uint32_t finite_abs_max16(uint32_t w, uint32_t m) {
+  const uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
+  if (lo < 0x7F80u) m = max(m, lo << 16);
+  if (hi < 0x7F80u) m = max(m, hi << 16);
+  return m;
+}
+
+// Exact grid: a workgroup scans kAmaxChunksPerWG consecutive 16-byte chunks
+// (eight per thread, all loads issued before the reductions) and writes one
+// partial.  The rows may be padded: a chunk's row comes from a fast division.
+template <bool VEC>
+__global__ void __launch_bounds__(256) amax_kernel(const uint16_t* __restrict__ x, int64_t C, int64_t ldx,
+                                                   FastDiv cpr, uint32_t total, uint32_t* __restrict__ partials) {
+  constexpr int U = kAmaxChunksPerWG / 256;
+  uint32_t m = 0;
+  const uint32_t base = blockIdx.x * (uint32_t)kAmaxChunksPerWG + threadIdx.x;
+  uint32_t w[U][4];
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    const uint32_t t = base + u * 256u;
+    w[u][0] = w[u][1] = w[u][2] = w[u][3] = 0;
+    if (t < total) {
+      const uint32_t i = fastdiv(t, cpr), q = t - i * cpr.d;
+      const uint16_t* src = x + (int64_t)i * ldx + (int64_t)q * 8;
+      if (VEC) {
+        u32v4 v = __builtin_nontemporal_load((const u32v4*)src);
+        w[u][0] = v[0]; w[u][1] = v[1]; w[u][2] = v[2]; w[u][3] = v[3];
+      } else {
+        const int n = (C - (int64_t)q * 8) < 8 ? (int)(C - (int64_t)q * 8) : 8;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const uint32_t lo = (2 * j < n) ? src[2 * j] : 0u, hi = (2 * j + 1 < n) ? src[2 * j + 1] : 0u;
+          w[u][j] = lo | (hi << 16);
+        }
+      }
+    }
   }
+#pragma unroll
+  for (int u = 0; u < U; u++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) m = finite_abs_max16(w[u][j], m);
+  const uint32_t r = block_max_u32(m);
+  if (threadIdx.x == 0) partials[blockIdx.x] = r;
 }
 
 // Tensor amax with the rotation applied (NVFP4 + Hadamard), contraction along
@@ -202,177 +279,224 @@ __global__ void __launch_bounds__(256) amax_rot_kernel(const uint16_t* __restric
       if (a < 0x7F800000u) m = max(m, a);
     }
   }
-  __shared__ uint32_t red[4];
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = red[0];
-    for (int k = 1; k < (int)(blockDim.x >> 6); k++) r = max(r, red[k]);
-    partials[blockIdx.x] = r;
-  }
+  const uint32_t r = block_max_u32(m);
+  if (threadIdx.x == 0) partials[blockIdx.x] = r;
+}
+
+__global__ void __launch_bounds__(1024) amax_finalize_kernel(const uint32_t* __restrict__ partials, int64_t nparts,
+                                                             float* __restrict__ ts_out) {
+  uint32_t m = 0;
+  for (int64_t i = threadIdx.x; i < nparts; i += blockDim.x) m = max(m, partials[i]);
+  const uint32_t r = block_max_u32(m);
+  if (threadIdx.x == 0) ts_out[0] = nv_tensor_scale_from_amax_bits(r);
 }
 
 // ---------------------------------------------------------------------------
-// Row quantizer (axis = 1).  Lane = 8 consecutive elements of one row; the
-// row's chunks are numbered t = i * (C/8) + q, so a Philox block (8
-// elements of the output stream, counter = output index / 8) is exactly the
-// lane's chunk: one Philox call per lane.
+// Row quantizer (axis = 1).  Lane = 8 consecutive elements of one row, chunk
+// t = i * (C/8) + q; a 32-block is a quad of lanes (16-block: a pair).  The
+// codes of chunk t are bytes 4t..4t+3 and its block's scale byte is t / (lanes
+// per block), whatever the row length.  A Philox block (8 elements of the
+// output stream, counter = output index / 8) is exactly one chunk.  Each
+// thread keeps four 16-byte loads in flight.
 // ---------------------------------------------------------------------------
 struct RowArgs {
-  const uint16_t* x;
-  int64_t R, C, ldx;
-  uint8_t* codes;
+  const uint16_t* x;      // first element of the launch's slice
+  int64_t ldx;
+  FastDiv cpr;            // chunks per row
+  uint32_t total;         // chunks in the slice (< 2^31)
+  uint64_t tbase;         // global index of the slice's first chunk (Philox counter)
+  uint8_t* codes;         // codes and scales of the slice's first chunk
   uint8_t* scales;
   uint64_t seed;
-  const uint32_t* partials;
-  int nparts;
-  float* ts_out;
+  const float* st;        // NVFP4 tensor scale (device), written by the finalize kernel
 };
 
-template <int FMT, int RND, bool HAD, bool VEC>
+// LOAD bit 0: element loads (the input is not 16-byte aligned), else 16-byte
+// loads.  LOAD bit 1: rows are padded (ldx > C), so a chunk's row comes from a
+// division; else the slice is contiguous.
+template <int FMT, int RND, bool HAD, int LOAD>
 __global__ void __launch_bounds__(256) quant_rows_kernel(RowArgs a) {
   constexpr int LPB = (FMT == FMT_MX) ? 4 : 2;   // lanes per scale block
-  float st = 1.0f;
-  if (FMT == FMT_NV) st = load_tensor_scale(a.partials, a.nparts, a.ts_out);
-
-  const int64_t cpr = a.C / 8;
-  const int64_t total = a.R * cpr;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  constexpr int U = kRowChunksPerWG / 256;
+  const float st = (FMT == FMT_NV) ? a.st[0] : 1.0f;
   const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
   const uint32_t p = threadIdx.x & 3u;           // position in the quad
-
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
-    const int64_t i = t / cpr, q = t - i * cpr;
-    const uint16_t* src = a.x + i * a.ldx + q * 8;
-    uint32_t w[4];
-    if (VEC) {
-      u32v4 v = __builtin_nontemporal_load((const u32v4*)src);
-      w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
-    } else {
+  const uint32_t base = blockIdx.x * (uint32_t)kRowChunksPerWG + threadIdx.x;
+  uint32_t w[U][4];
 #pragma unroll
-      for (int j = 0; j < 4; j++) w[j] = (uint32_t)src[2 * j] | ((uint32_t)src[2 * j + 1] << 16);
+  for (int u = 0; u < U; u++) {
+    const uint32_t t = base + u * 256u;
+    w[u][0] = w[u][1] = w[u][2] = w[u][3] = 0;
+    if (t < a.total) {
+      const uint16_t* src;
+      if (LOAD & 2) {
+        const uint32_t i = fastdiv(t, a.cpr), q = t - i * a.cpr.d;
+        src = a.x + (int64_t)i * a.ldx + (int64_t)q * 8;
+      } else {
+        src = a.x + (uint64_t)t * 8;
+      }
+      if (LOAD & 1) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) w[u][j] = (uint32_t)src[2 * j] | ((uint32_t)src[2 * j + 1] << 16);
+      } else {
+        u32v4 v = __builtin_nontemporal_load((const u32v4*)src);
+        w[u][0] = v[0]; w[u][1] = v[1]; w[u][2] = v[2]; w[u][3] = v[3];
+      }
     }
-
-    float y[8];
-    uint32_t amax_bits;   // binary32 pattern of the lane's largest |y|
-    bool nonfinite;
-    if (HAD) {
+  }
 #pragma unroll
-      for (int j = 0; j < 4; j++) { y[2 * j] = bf16lo(w[j]); y[2 * j + 1] = bf16hi(w[j]); }
+  for (int u = 0; u < U; u++) {
+    const uint32_t t = base + u * 256u;
+    if (t >= a.total) break;     // whole blocks leave together: total is a multiple of the lanes per block
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 4; j++) { y[2 * j] = bf16lo(w[u][j]); y[2 * j + 1] = bf16hi(w[u][j]); }
+    uint32_t amax_bits;
+    if (HAD) {
       fwht32_quad(y, p);
       uint32_t m = 0;
 #pragma unroll
       for (int j = 0; j < 8; j++) m = max(m, __float_as_uint(y[j]) & 0x7FFFFFFFu);
       amax_bits = m;
     } else {
-      uint32_t m = pk_max_u16(pk_max_u16(w[0] & 0x7FFF7FFFu, w[1] & 0x7FFF7FFFu),
-                              pk_max_u16(w[2] & 0x7FFF7FFFu, w[3] & 0x7FFF7FFFu));
+      const uint32_t m = pk_max_u16(pk_max_u16(w[u][0] & 0x7FFF7FFFu, w[u][1] & 0x7FFF7FFFu),
+                                    pk_max_u16(w[u][2] & 0x7FFF7FFFu, w[u][3] & 0x7FFF7FFFu));
       amax_bits = max(m & 0xFFFFu, m >> 16) << 16;
     }
-    // block reduction across the lanes of the block
     amax_bits = max(amax_bits, dpp_xor1(amax_bits));
     if (LPB == 4) amax_bits = max(amax_bits, dpp_xor2(amax_bits));
-    nonfinite = amax_bits >= 0x7F800000u;
-
-    uint32_t byte, packed = 0;
-    if (FMT == FMT_MX) {
-      byte = nonfinite ? 0xFFu : mx_scale_byte_from_f32bits(amax_bits);
-      if (!nonfinite) {
-        if (RND == RND_RTN) {
-          const float sc = e8m0_as_cvt_scale(byte);
-          if (HAD) {
-            packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[0], y[1], sc, 0);
-            packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[2], y[3], sc, 1);
-            packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[4], y[5], sc, 2);
-            packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[6], y[7], sc, 3);
-          } else {
-            packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2, w[0]), sc, 0);
-            packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2, w[1]), sc, 1);
-            packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2, w[2]), sc, 2);
-            packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(packed, __builtin_bit_cast(bf16x2, w[3]), sc, 3);
-          }
-        } else {
-          if (!HAD) {
-#pragma unroll
-            for (int j = 0; j < 4; j++) { y[2 * j] = bf16lo(w[j]); y[2 * j + 1] = bf16hi(w[j]); }
-          }
-          const float inv = mx_inv_scale(byte);
-          const uint64_t g = (uint64_t)t;        // output index / 8
-          u32x4 r = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), 1u, 0u, k0, k1);
-          const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-          for (int j = 0; j < 8; j++) {
-            uint32_t rnd = (rw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-            packed |= sr_code(y[j] * inv, rnd) << (4 * j);
-          }
-        }
-      }
-    } else {
-      if (!HAD) {
-#pragma unroll
-        for (int j = 0; j < 4; j++) { y[2 * j] = bf16lo(w[j]); y[2 * j + 1] = bf16hi(w[j]); }
-      }
-      float inv = 0.0f;
-      if (nonfinite) {
-        byte = 0x7Fu;
-      } else {
-        nv_block_scale(__uint_as_float(amax_bits), st, byte, inv);
-      }
-      if (!nonfinite) {
-        float xs[8];
-#pragma unroll
-        for (int j = 0; j < 8; j++) xs[j] = byte ? y[j] * inv : __builtin_copysignf(0.0f, y[j]);
-        if (RND == RND_RTN) {
-          packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, xs[0], xs[1], 1.0f, 0);
-          packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, xs[2], xs[3], 1.0f, 1);
-          packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, xs[4], xs[5], 1.0f, 2);
-          packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, xs[6], xs[7], 1.0f, 3);
-        } else {
-          const uint64_t g = (uint64_t)t;
-          u32x4 r = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), 1u, 0u, k0, k1);
-          const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-          for (int j = 0; j < 8; j++) {
-            uint32_t rnd = (rw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-            packed |= sr_code(xs[j], rnd) << (4 * j);
-          }
-        }
-      }
+    uint32_t byte;
+    float mul;
+    bool nonfinite;
+    block_scale<FMT>(amax_bits, st, byte, mul, nonfinite);
+    uint32_t rw[4] = {0, 0, 0, 0};
+    if (RND == RND_SR && !nonfinite) {
+      const uint64_t g = a.tbase + t;      // = output index / 8
+      const u32x4 r = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), 1u, 0u, k0, k1);
+      rw[0] = r.x; rw[1] = r.y; rw[2] = r.z; rw[3] = r.w;
     }
-    // codes: 4 bytes per lane; scales: one byte per block, from its first lane
-    *(uint32_t*)(a.codes + i * (a.C / 2) + q * 4) = packed;
-    if ((q & (LPB - 1)) == 0) a.scales[i * (a.C / (8 * LPB)) + q / LPB] = (uint8_t)byte;
+    const uint32_t packed = nonfinite ? 0u : encode8<FMT, RND, !HAD>(y, w[u], byte, mul, rw);
+    // outputs are not re-read by this kernel: stream them past the caches
+    __builtin_nontemporal_store(packed, (uint32_t*)(a.codes + (uint64_t)t * 4));
+    if ((p & (LPB - 1)) == 0) __builtin_nontemporal_store((uint8_t)byte, a.scales + t / LPB);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Transposing quantizer (axis = 0).  Output row c (input column c), contraction
-// index r.  A lane holds columns 2l, 2l+1 of a 32-row slab as 32 packed
-// bf16 pairs; a wave covers 128 columns.  Grid: x over 128-column groups,
-// y over 32-row slabs.
+// Transposing quantizer (axis = 0), output row c = input column c, contraction
+// index r.  Main kernel: a workgroup stages a 256-row x 64-column bf16 tile in
+// LDS with 16-byte coalesced loads (8 rows x 128 B per wave instruction);
+// wave w then owns rows 64w..64w+63 and lane l column l, so every contraction
+// block of a column is in one lane's registers and the four waves write 128
+// contiguous bytes of each output row.  Needs C % 8 == 0 and 16-byte aligned
+// rows; the small kernel after it covers the rest.
 // ---------------------------------------------------------------------------
 struct ColArgs {
   const uint16_t* x;
   int64_t R, C, ldx;
+  int64_t r_off;          // first input row of the launch (grid.y covers at most 65535 tiles)
   uint8_t* codes;
   uint8_t* scales;
   uint64_t seed;
-  const uint32_t* partials;
-  int nparts;
-  float* ts_out;
+  const float* st;
 };
 
-template <int FMT, int RND, bool HAD, bool VEC>
-__global__ void __launch_bounds__(256) quant_cols_kernel(ColArgs a) {
-  float st = 1.0f;
-  if (FMT == FMT_NV) st = load_tensor_scale(a.partials, a.nparts, a.ts_out);
+template <int FMT, int RND, bool HAD>
+__global__ void __launch_bounds__(256) quant_cols_tile_kernel(ColArgs a) {
+  constexpr int BS = (FMT == FMT_MX) ? 32 : 16;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[256 * 64];   // 32 KB
+  const float st = (FMT == FMT_NV) ? a.st[0] : 1.0f;
   const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
   const int64_t R = a.R, C = a.C;
+  const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = a.r_off + (int64_t)blockIdx.y * 256;
+  const int tid = threadIdx.x;
+
+  // stage: thread loads 8 x 16 B (rows tid/8 + 32j, columns c0 + 8 (tid % 8)
+  // ..).  Addresses are clamped into the tensor and the out-of-range chunks
+  // zeroed afterwards, so all eight loads are issued back to back.
+  {
+    const int cc = (tid & 7) * 8;
+    const bool col_ok = c0 + cc < C;
+    const int64_t cl = col_ok ? c0 + cc : C - 8;
+    u32v4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int64_t row = r0 + (tid >> 3) + 32 * j;
+      const int64_t rl = row < R ? row : R - 1;
+      v[j] = __builtin_nontemporal_load((const u32v4*)(a.x + rl * a.ldx + cl));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int row = (tid >> 3) + 32 * j;
+      const bool ok = col_ok && (r0 + row < R);
+      *(u32v4*)(tile + row * 64 + cc) = ok ? v[j] : (u32v4){0, 0, 0, 0};
+    }
+  }
+  __syncthreads();
+
+  const int w = tid >> 6, l = tid & 63;
+  const int64_t c = c0 + l;
+  const int64_t rw0 = r0 + 64 * w;                  // first contraction index of this wave
+  if (rw0 >= R || c >= C) return;
+  // two halves of 32 rows (one MXFP4 block, two NVFP4 blocks); R is a
+  // multiple of the block, so a half is whole, half-filled (NVFP4) or empty
+#pragma unroll 1
+  for (int h = 0; h < 2; h++) {
+    const int64_t rh = rw0 + 32 * h;
+    if (rh >= R) break;
+    const int nrows = (R - rh) >= 32 ? 32 : (int)(R - rh);
+    float y[32];
+#pragma unroll
+    for (int j = 0; j < 32; j++) y[j] = __uint_as_float((uint32_t)tile[(64 * w + 32 * h + j) * 64 + l] << 16);
+    if (HAD) fwht32_inlane(y);
+    uint32_t out[4];
+#pragma unroll
+    for (int b = 0; b < 32 / BS; b++) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < BS; j++) m = max(m, __float_as_uint(y[b * BS + j]) & 0x7FFFFFFFu);
+      uint32_t byte;
+      float mul;
+      bool nonfinite;
+      block_scale<FMT>(m, st, byte, mul, nonfinite);
+#pragma unroll
+      for (int j2 = 0; j2 < BS / 8; j2++) {
+        const int e0 = b * BS + j2 * 8;
+        uint32_t rw[4] = {0, 0, 0, 0};
+        if (RND == RND_SR && !nonfinite) {
+          const uint64_t g = (uint64_t)((c * R + rh + e0) >> 3);
+          const u32x4 r = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), 0u, 0u, k0, k1);
+          rw[0] = r.x; rw[1] = r.y; rw[2] = r.z; rw[3] = r.w;
+        }
+        const uint32_t dummy[4] = {0, 0, 0, 0};
+        out[e0 / 8] = nonfinite ? 0u : encode8<FMT, RND, false>(y + e0, dummy, byte, mul, rw);
+      }
+      if (b * BS < nrows) a.scales[c * (R / BS) + rh / BS + b] = (uint8_t)byte;
+    }
+    // plain stores: each lane writes part of a different output row, and the
+    // workgroup's four waves complete those lines in L2 (streaming stores of
+    // partial lines cost several times more here)
+    uint8_t* dst = a.codes + c * (R / 2) + rh / 2;
+    if (nrows == 32 && (R % 32) == 0) {
+      *(uint4*)dst = make_uint4(out[0], out[1], out[2], out[3]);
+    } else {
+      *(uint2*)dst = make_uint2(out[0], out[1]);
+      if (nrows == 32) *(uint2*)(dst + 8) = make_uint2(out[2], out[3]);
+    }
+  }
+}
+
+// Small transposing kernel for ragged or unaligned inputs: a lane holds
+// columns 2l, 2l+1 of a 32-row slab (32 loads of one 32-bit pair each).
+template <int FMT, int RND, bool HAD, bool VEC>
+__global__ void __launch_bounds__(256) quant_cols_kernel(ColArgs a) {
+  const float st = (FMT == FMT_NV) ? a.st[0] : 1.0f;
+  const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
+  const int64_t R = a.R, C = a.C;
+  constexpr int BS = (FMT == FMT_MX) ? 32 : 16;
 
   const int64_t slab = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);   // 32-row slab
-  const int64_t r0 = slab * 32;
+  const int64_t r0 = a.r_off + slab * 32;
   if (r0 >= R) return;
   const int nrows = (R - r0) >= 32 ? 32 : (int)(R - r0);             // 32, or 16 (NVFP4 tail)
   const int64_t c0 = ((int64_t)blockIdx.x * 64 + (threadIdx.x & 63)) * 2;
@@ -390,20 +514,13 @@ __global__ void __launch_bounds__(256) quant_cols_kernel(ColArgs a) {
       w[j] = 0;
     }
   }
-
   const int ncols = two ? 2 : 1;
   for (int h = 0; h < ncols; h++) {
     const int64_t c = c0 + h;
     float y[32];
-    uint32_t bits[32];
 #pragma unroll
-    for (int j = 0; j < 32; j++) {
-      bits[j] = h ? (w[j] & 0xFFFF0000u) : (w[j] << 16);
-      y[j] = __uint_as_float(bits[j]);
-    }
+    for (int j = 0; j < 32; j++) y[j] = __uint_as_float(h ? (w[j] & 0xFFFF0000u) : (w[j] << 16));
     if (HAD) fwht32_inlane(y);
-
-    constexpr int BS = (FMT == FMT_MX) ? 32 : 16;
     uint32_t out[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int b = 0; b < 32 / BS; b++) {
@@ -411,55 +528,21 @@ __global__ void __launch_bounds__(256) quant_cols_kernel(ColArgs a) {
       uint32_t m = 0;
 #pragma unroll
       for (int j = 0; j < BS; j++) m = max(m, __float_as_uint(y[b * BS + j]) & 0x7FFFFFFFu);
-      const bool nonfinite = m >= 0x7F800000u;
       uint32_t byte;
-      float mul = 0.0f, cvt_sc = 1.0f;
-      if (FMT == FMT_MX) {
-        byte = nonfinite ? 0xFFu : mx_scale_byte_from_f32bits(m);
-        mul = mx_inv_scale(byte);
-        cvt_sc = e8m0_as_cvt_scale(byte);
-      } else if (nonfinite) {
-        byte = 0x7Fu;
-      } else {
-        nv_block_scale(__uint_as_float(m), st, byte, mul);
-      }
-      if (!nonfinite) {
-        const int64_t kbase = r0 + b * BS;     // contraction index of the block's first element
+      float mul;
+      bool nonfinite;
+      block_scale<FMT>(m, st, byte, mul, nonfinite);
 #pragma unroll
-        for (int j2 = 0; j2 < BS / 8; j2++) {
-          // 8 elements = one 32-bit word of codes and one Philox block
-          uint32_t word = 0;
-          const int e0 = b * BS + j2 * 8;
-          if (RND == RND_RTN) {
-            if (FMT == FMT_MX) {
-              word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[e0 + 0], y[e0 + 1], cvt_sc, 0);
-              word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[e0 + 2], y[e0 + 3], cvt_sc, 1);
-              word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[e0 + 4], y[e0 + 5], cvt_sc, 2);
-              word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y[e0 + 6], y[e0 + 7], cvt_sc, 3);
-            } else {
-              float xs[8];
-#pragma unroll
-              for (int j = 0; j < 8; j++) xs[j] = byte ? y[e0 + j] * mul : __builtin_copysignf(0.0f, y[e0 + j]);
-              word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, xs[0], xs[1], 1.0f, 0);
-              word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, xs[2], xs[3], 1.0f, 1);
-              word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, xs[4], xs[5], 1.0f, 2);
-              word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, xs[6], xs[7], 1.0f, 3);
-            }
-          } else {
-            const uint64_t g = (uint64_t)((c * R + kbase + j2 * 8) >> 3);
-            u32x4 r = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), 0u, 0u, k0, k1);
-            const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-              float xs;
-              if (FMT == FMT_MX) xs = y[e0 + j] * mul;
-              else xs = byte ? y[e0 + j] * mul : __builtin_copysignf(0.0f, y[e0 + j]);
-              uint32_t rnd = (rw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-              word |= sr_code(xs, rnd) << (4 * j);
-            }
-          }
-          out[e0 / 8] = word;
+      for (int j2 = 0; j2 < BS / 8; j2++) {
+        const int e0 = b * BS + j2 * 8;
+        uint32_t rw[4] = {0, 0, 0, 0};
+        if (RND == RND_SR && !nonfinite) {
+          const uint64_t g = (uint64_t)((c * R + r0 + e0) >> 3);
+          const u32x4 r = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), 0u, 0u, k0, k1);
+          rw[0] = r.x; rw[1] = r.y; rw[2] = r.z; rw[3] = r.w;
         }
+        const uint32_t dummy[4] = {0, 0, 0, 0};
+        out[e0 / 8] = nonfinite ? 0u : encode8<FMT, RND, false>(y + e0, dummy, byte, mul, rw);
       }
       a.scales[c * (R / BS) + (r0 / BS) + b] = (uint8_t)byte;
     }
@@ -478,75 +561,174 @@ __global__ void __launch_bounds__(256) quant_cols_kernel(ColArgs a) {
 // ---------------------------------------------------------------------------
 // Host-side launchers (called from the C ABI after argument checks).
 // ---------------------------------------------------------------------------
-static int grid_for(int64_t work_items, int per_block) {
+static int grid_for(int64_t work_items, int per_block, int64_t cap) {
   int64_t g = (work_items + per_block - 1) / per_block;
-  const int64_t cap = 256 * 64;     // enough resident waves; larger work loops
   if (g > cap) g = cap;
   return (int)(g < 1 ? 1 : g);
 }
 
-int amax_partials_count(int64_t R, int64_t C) {
-  int64_t work = R * ((C + 7) / 8);
-  int64_t g = (work + 255) / 256;
-  return (int)(g > kAmaxPartials ? kAmaxPartials : (g < 1 ? 1 : g));
+template <int FMT, int RND, bool HAD>
+static void launch_rows(const RowArgs& a, int load, hipStream_t s) {
+  const int grid = (int)(((uint64_t)a.total + kRowChunksPerWG - 1) / kRowChunksPerWG);
+  switch (load) {
+    case 0: hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, 0>), dim3(grid), dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, 1>), dim3(grid), dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, 2>), dim3(grid), dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, 3>), dim3(grid), dim3(256), 0, s, a); break;
+  }
 }
 
 template <int FMT, int RND, bool HAD>
-static void launch_rows(const RowArgs& a, bool vec, hipStream_t s) {
-  int grid = grid_for(a.R * (a.C / 8), 256);
-  if (vec) hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, true>), dim3(grid), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, false>), dim3(grid), dim3(256), 0, s, a);
+static void launch_cols(ColArgs a, bool tiled, bool vec, hipStream_t s) {
+  // grid.y is limited to 65535: larger inputs go in slabs of rows
+  const int64_t rows_per = tiled ? 256 : 128;
+  const int64_t slab = 65535 * rows_per;
+  for (int64_t r = 0; r < a.R; r += slab) {
+    a.r_off = r;
+    const int64_t nr = (a.R - r) < slab ? (a.R - r) : slab;
+    const int64_t cols_per = tiled ? 64 : 128;
+    dim3 grid((unsigned)((a.C + cols_per - 1) / cols_per), (unsigned)((nr + rows_per - 1) / rows_per));
+    if (tiled) hipLaunchKernelGGL((quant_cols_tile_kernel<FMT, RND, HAD>), grid, dim3(256), 0, s, a);
+    else if (vec) hipLaunchKernelGGL((quant_cols_kernel<FMT, RND, HAD, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((quant_cols_kernel<FMT, RND, HAD, false>), grid, dim3(256), 0, s, a);
+  }
+}
+
+// Chunk ranges of one launch stay below 2^31 so the kernels index in 32 bits.
+constexpr uint64_t kSliceChunks = (uint64_t)1 << 30;
+
+template <int FMT, int RND, bool HAD>
+static void launch_rows_sliced(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, bool aligned16, uint64_t seed,
+                               uint8_t* codes, uint8_t* scales, const float* st, hipStream_t s) {
+  constexpr int LPB = (FMT == FMT_MX) ? 4 : 2;
+  const uint64_t cpr = (uint64_t)C / 8;
+  RowArgs a{};
+  a.ldx = ldx;
+  a.seed = seed;
+  a.st = st;
+  const int elem = aligned16 ? 0 : 1;
+  auto packed_range = [&](const uint16_t* xr, uint64_t t0, uint64_t n) {
+    // a contiguous range of n chunks starting at global chunk t0
+    for (uint64_t off = 0; off < n; off += kSliceChunks) {
+      const uint64_t m = (n - off) < kSliceChunks ? (n - off) : kSliceChunks;
+      a.x = xr + off * 8;
+      a.cpr = make_fastdiv(1);
+      a.total = (uint32_t)m;
+      a.tbase = t0 + off;
+      a.codes = codes + (t0 + off) * 4;
+      a.scales = scales + (t0 + off) / LPB;
+      launch_rows<FMT, RND, HAD>(a, elem, s);
+    }
+  };
+  if (ldx == C || R == 1) {
+    packed_range(x, 0, (uint64_t)R * cpr);
+  } else if (cpr < kSliceChunks) {
+    const int64_t rows_per = (int64_t)(kSliceChunks / cpr);
+    for (int64_t r = 0; r < R; r += rows_per) {
+      const int64_t nr = (R - r) < rows_per ? (R - r) : rows_per;
+      a.x = x + r * ldx;
+      a.cpr = make_fastdiv((uint32_t)cpr);
+      a.total = (uint32_t)((uint64_t)nr * cpr);
+      a.tbase = (uint64_t)r * cpr;
+      a.codes = codes + a.tbase * 4;
+      a.scales = scales + a.tbase / LPB;
+      launch_rows<FMT, RND, HAD>(a, 2 | elem, s);
+    }
+  } else {
+    for (int64_t r = 0; r < R; r++) packed_range(x + r * ldx, (uint64_t)r * cpr, cpr);
+  }
 }
 
 template <int FMT, int RND, bool HAD>
-static void launch_cols(const ColArgs& a, bool vec, hipStream_t s) {
-  dim3 grid((unsigned)((a.C + 127) / 128), (unsigned)((a.R + 127) / 128));
-  if (vec) hipLaunchKernelGGL((quant_cols_kernel<FMT, RND, HAD, true>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((quant_cols_kernel<FMT, RND, HAD, false>), grid, dim3(256), 0, s, a);
+static void launch_one(int axis, const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint64_t seed,
+                       uint8_t* codes, uint8_t* scales, const float* st, hipStream_t s) {
+  const bool aligned16 = (((uintptr_t)x & 15u) == 0) && (ldx % 8 == 0);
+  if (axis == 1) {
+    launch_rows_sliced<FMT, RND, HAD>(x, R, C, ldx, aligned16, seed, codes, scales, st, s);
+  } else {
+    ColArgs ca{x, R, C, ldx, 0, codes, scales, seed, st};
+    const bool tiled = aligned16 && (C % 8 == 0);
+    const bool vec = (((uintptr_t)x & 3u) == 0) && (ldx % 2 == 0);
+    launch_cols<FMT, RND, HAD>(ca, tiled, vec, s);
+  }
 }
 
 template <int FMT, int RND>
-static void dispatch_had(bool had, int axis, const RowArgs& ra, const ColArgs& ca, bool vec, hipStream_t s) {
-  if (axis == 1) {
-    if (had) launch_rows<FMT, RND, true>(ra, vec, s);
-    else launch_rows<FMT, RND, false>(ra, vec, s);
+static void launch_had(bool had, int axis, const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint64_t seed,
+                       uint8_t* codes, uint8_t* scales, const float* st, hipStream_t s) {
+  if (had) launch_one<FMT, RND, true>(axis, x, R, C, ldx, seed, codes, scales, st, s);
+  else launch_one<FMT, RND, false>(axis, x, R, C, ldx, seed, codes, scales, st, s);
+}
+
+// Tensor amax of an NVFP4 input into s_t (device): partial maxima, then the
+// one-workgroup finalize.
+static void launch_tensor_scale(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int hadamard, int axis,
+                                float* tensor_scale, uint32_t* partials, hipStream_t s) {
+  int64_t nparts = 0;
+  if (hadamard) {
+    const int64_t blocks = (axis == 1 ? R * (C / 32) : C * (R / 32));
+    nparts = grid_for(blocks, 256, kAmaxRotPartials);
+    if (axis == 1) hipLaunchKernelGGL((amax_rot_kernel<true>), dim3((unsigned)nparts), dim3(256), 0, s, x, R, C, ldx, partials);
+    else hipLaunchKernelGGL((amax_rot_kernel<false>), dim3((unsigned)nparts), dim3(256), 0, s, x, R, C, ldx, partials);
   } else {
-    if (had) launch_cols<FMT, RND, true>(ca, vec, s);
-    else launch_cols<FMT, RND, false>(ca, vec, s);
+    // the unrotated amax does not depend on the axis: scan the rows of [R, C]
+    // in ranges of whole rows below 2^31 chunks (a row of more chunks than
+    // that is scanned alone, as a contiguous range); each range writes its
+    // own run of partials
+    const uint64_t cpr = ((uint64_t)C + 7) / 8;
+    const bool vec = (((uintptr_t)x & 15u) == 0) && (ldx % 8 == 0) && (C % 8 == 0);
+    auto scan = [&](const uint16_t* xr, int64_t nr, int64_t c, uint64_t per_row) {
+      const uint32_t total = (uint32_t)((uint64_t)nr * per_row);
+      const unsigned grid = (unsigned)((total + kAmaxChunksPerWG - 1) / kAmaxChunksPerWG);
+      const FastDiv f = make_fastdiv((uint32_t)per_row);
+      if (vec) hipLaunchKernelGGL((amax_kernel<true>), dim3(grid), dim3(256), 0, s, xr, c, ldx, f, total, partials + nparts);
+      else hipLaunchKernelGGL((amax_kernel<false>), dim3(grid), dim3(256), 0, s, xr, c, ldx, f, total, partials + nparts);
+      nparts += grid;
+    };
+    if (cpr < kSliceChunks) {
+      const int64_t rows_per = (int64_t)(kSliceChunks / cpr);
+      for (int64_t r = 0; r < R; r += rows_per) scan(x + r * ldx, (R - r) < rows_per ? (R - r) : rows_per, C, cpr);
+    } else {
+      for (int64_t r = 0; r < R; r++)
+        for (uint64_t off = 0; off < cpr; off += kSliceChunks) {
+          const uint64_t m = (cpr - off) < kSliceChunks ? (cpr - off) : kSliceChunks;
+          const int64_t c = (int64_t)(m * 8) < (C - (int64_t)off * 8) ? (int64_t)(m * 8) : (C - (int64_t)off * 8);
+          scan(x + r * ldx + off * 8, 1, c, m);
+        }
+    }
   }
+  hipLaunchKernelGGL(amax_finalize_kernel, dim3(1), dim3(1024), 0, s, partials, nparts, tensor_scale);
+}
+
+size_t quantize_workspace_bytes(int fmt, int64_t R, int64_t C) {
+  if (fmt != FMT_NV) return 0;
+  // partials written by launch_tensor_scale's unrotated scan, range by range
+  const uint64_t cpr = ((uint64_t)C + 7) / 8;
+  const uint64_t per = kAmaxChunksPerWG;
+  uint64_t n = 0;
+  if (R > 0 && cpr > 0) {
+    if (cpr < kSliceChunks) {
+      const uint64_t rows_per = kSliceChunks / cpr, full = (uint64_t)R / rows_per, rem = (uint64_t)R % rows_per;
+      n = full * ((rows_per * cpr + per - 1) / per) + (rem ? (rem * cpr + per - 1) / per : 0);
+    } else {
+      const uint64_t m_full = cpr / kSliceChunks, m_rem = cpr % kSliceChunks;
+      n = (uint64_t)R * (m_full * ((kSliceChunks + per - 1) / per) + (m_rem ? (m_rem + per - 1) / per : 0));
+    }
+  }
+  if (n < (uint64_t)kAmaxRotPartials) n = kAmaxRotPartials;
+  return (size_t)n * sizeof(uint32_t);
 }
 
 hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int fmt, int rounding,
                            int hadamard, int axis, uint64_t seed, uint8_t* codes, uint8_t* scales,
                            float* tensor_scale, uint32_t* partials, hipStream_t stream) {
-  int nparts = 0;
-  if (fmt == FMT_NV) {
-    if (hadamard) {
-      int64_t blocks = (axis == 1 ? R * (C / 32) : C * (R / 32));
-      nparts = (int)((blocks + 255) / 256);
-      if (nparts > kAmaxPartials) nparts = kAmaxPartials;
-      if (nparts < 1) nparts = 1;
-      if (axis == 1) hipLaunchKernelGGL((amax_rot_kernel<true>), dim3(nparts), dim3(256), 0, stream, x, R, C, ldx, partials);
-      else hipLaunchKernelGGL((amax_rot_kernel<false>), dim3(nparts), dim3(256), 0, stream, x, R, C, ldx, partials);
-    } else {
-      // the unrotated amax does not depend on the axis: scan the rows of [R, C]
-      nparts = amax_partials_count(R, C);
-      const bool v16 = (((uintptr_t)x & 15u) == 0) && (ldx % 8 == 0) && (C % 8 == 0);
-      if (v16) hipLaunchKernelGGL((amax_kernel<true>), dim3(nparts), dim3(256), 0, stream, x, R, C, ldx, partials);
-      else hipLaunchKernelGGL((amax_kernel<false>), dim3(nparts), dim3(256), 0, stream, x, R, C, ldx, partials);
-    }
-  }
-  const bool vec = (((uintptr_t)x & 15u) == 0) && (ldx % 8 == 0);
-  RowArgs ra{x, R, C, ldx, codes, scales, seed, partials, nparts, tensor_scale};
-  ColArgs ca{x, R, C, ldx, codes, scales, seed, partials, nparts, tensor_scale};
-  const bool vec_cols = (((uintptr_t)x & 3u) == 0) && (ldx % 2 == 0);
-  const bool v = (axis == 1) ? vec : vec_cols;
+  if (fmt == FMT_NV) launch_tensor_scale(x, R, C, ldx, hadamard, axis, tensor_scale, partials, stream);
   if (fmt == FMT_MX) {
-    if (rounding == RND_RTN) dispatch_had<FMT_MX, RND_RTN>(hadamard, axis, ra, ca, v, stream);
-    else dispatch_had<FMT_MX, RND_SR>(hadamard, axis, ra, ca, v, stream);
+    if (rounding == RND_RTN) launch_had<FMT_MX, RND_RTN>(hadamard, axis, x, R, C, ldx, seed, codes, scales, tensor_scale, stream);
+    else launch_had<FMT_MX, RND_SR>(hadamard, axis, x, R, C, ldx, seed, codes, scales, tensor_scale, stream);
   } else {
-    if (rounding == RND_RTN) dispatch_had<FMT_NV, RND_RTN>(hadamard, axis, ra, ca, v, stream);
-    else dispatch_had<FMT_NV, RND_SR>(hadamard, axis, ra, ca, v, stream);
+    if (rounding == RND_RTN) launch_had<FMT_NV, RND_RTN>(hadamard, axis, x, R, C, ldx, seed, codes, scales, tensor_scale, stream);
+    else launch_had<FMT_NV, RND_SR>(hadamard, axis, x, R, C, ldx, seed, codes, scales, tensor_scale, stream);
   }
   return hipGetLastError();
 }
@@ -590,7 +772,7 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict_
 
 hipError_t launch_dequantize(int fmt, int64_t rows, int64_t K, const uint8_t* codes, const uint8_t* scales,
                              const float* ts, float* y, int64_t ldy, hipStream_t stream) {
-  int grid = grid_for(rows * (K / 8), 256);
+  int grid = grid_for(rows * (K / 8), 256, 256 * 64);
   if (fmt == FMT_MX)
     hipLaunchKernelGGL((dequant_kernel<FMT_MX>), dim3(grid), dim3(256), 0, stream, codes, scales, ts, rows, K, y, ldy);
   else

@@ -57,6 +57,12 @@ def test_tensor_bytes(mx):
 def test_quantize_workspace_bytes(mx):
     assert mx.mxfp4_quantize_workspace_bytes("mx", 100, 64) == 0
     assert mx.mxfp4_quantize_workspace_bytes("nv", 100, 64) == 4096
+    # NVFP4: one 32-bit partial per 2048 16-byte chunks of the tensor-amax scan,
+    # at least 1024 (the rotated pass), ranges of whole rows below 2^30 chunks
+    assert mx.mxfp4_quantize_workspace_bytes("nv", 14336, 8192) == 4 * (14336 * 1024 // 2048)
+    assert mx.mxfp4_quantize_workspace_bytes("nv", 2 ** 20 + 1, 2 ** 13) == 4 * (2 ** 30 // 2048 + 1)
+    assert mx.mxfp4_quantize_workspace_bytes("nv", 3, 2 ** 33) == 4 * 3 * (2 ** 30 // 2048)
+    assert mx.mxfp4_quantize_workspace_bytes("nv", 3, 2 ** 33 + 16) == 4 * 3 * (2 ** 30 // 2048 + 1)
     b = ctypes.c_size_t()
     assert mx.lib.mxfp4_quantize_workspace_bytes(0, 4, 64, 2, ctypes.byref(b)) == INVALID
 

@@ -41,6 +41,42 @@ def test_ragged_and_strided(oracle_mod, fmt, rnd, had, axis):
     _run(mx, oracle_mod, bits, fmt, rnd, had, axis, pad=3, what="ragged-pad3")
 
 
+@pytest.mark.parametrize("fmt,rnd,had", [(f, r, h) for f in ("mx", "nv") for r in ("rtn", "sr") for h in (False, True)])
+def test_transpose_tile_edges(oracle_mod, fmt, rnd, had):
+    """axis 0 through the LDS-tiled transpose: more than one 256-row tile with
+    a ragged last one (a 16-row NVFP4 tail when unrotated), a column count
+    that is a multiple of 8 but not of 64, packed and padded rows."""
+    mx = need_gpu()
+    shape = (304 if (fmt == "nv" and not had) else 288, 200)
+    bits = workloads.small_t_bf16(shape, 3.0, seed=27, outlier_frac=0.02)
+    _run(mx, oracle_mod, bits, fmt, rnd, had, 0, what="tile-edges")
+    _run(mx, oracle_mod, bits, fmt, rnd, had, 0, pad=8, what="tile-edges-pad8")
+
+
+def _offset_view(bits: np.ndarray, pad: int):
+    """A device view whose first element sits 2 bytes past a 16-byte boundary."""
+    import torch
+    R, C = bits.shape
+    ld = C + pad
+    flat = np.zeros(R * ld + 1, dtype=np.uint16)
+    flat[1:].reshape(R, ld)[:, :C] = bits
+    t = torch.from_numpy(flat.view(np.int16)).view(torch.bfloat16).cuda()
+    return t[1:].view(R, ld)[:, :C]
+
+
+@pytest.mark.parametrize("fmt,rnd,had,axis", COMBOS)
+def test_unaligned_input(oracle_mod, fmt, rnd, had, axis):
+    """Inputs that are not 16-byte aligned take the element-load paths;
+    packed (ldx == C) and padded rows."""
+    mx = need_gpu()
+    bits = workloads.small_normal_bf16((96, 256), 0.9, seed=28)
+    for pad in (0, 5):
+        say("quantize unaligned", fmt, rnd, had, axis, f"pad{pad}")
+        q = mx.mxfp4_quantize(_offset_view(bits, pad), fmt, rnd, had, axis, 99)
+        assert_codes_equal(q_to_host(q), oracle_mod.quantize(bits, fmt, rnd, had, axis, 99),
+                           f"unaligned pad{pad} {fmt} {rnd} H={had} axis={axis}")
+
+
 @pytest.mark.parametrize("fmt", ["mx", "nv"])
 @pytest.mark.parametrize("axis", [1, 0])
 def test_special_values(oracle_mod, fmt, axis):
