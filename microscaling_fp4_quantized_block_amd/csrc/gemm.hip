@@ -22,16 +22,19 @@
 //   scale, so the two lane groups of one MFMA step may take different blocks.
 //   The two tensor scales multiply the FP32 result in the epilogue.
 //
-// Tiling: 256 x 256 output tile per workgroup of 4 waves (2 x 2, 128 x 128 per
-// wave = 4 x 4 MFMA tiles, 256 accumulators per lane), K step 128 per stage,
-// four LDS stages (36 KB each) filled by buffer->LDS loads issued three stages
-// ahead (no staging registers, no LDS write instructions).  Codes sit in LDS as
-// 16-byte chunks, XOR-swizzled per row so that the rows an MFMA operand read
-// touches together hit distinct banks.
+// Tiling (MXFP4): 256 x 256 output tile per workgroup of 4 waves (2 x 2,
+// 128 x 128 per wave = 4 x 4 MFMA tiles, 256 accumulators per lane in AGPRs),
+// K stage 256 (one 128-byte line per operand row), two LDS stages of 64 KB
+// filled by buffer->LDS loads, three scale-group buffers; details at the
+// kernel.  NVFP4 keeps a 128-wide K stage with four 36 KB stages.  Codes sit
+// in LDS as 16-byte chunks, XOR-swizzled per row so that the rows an MFMA
+// operand read touches together hit distinct banks.
 // Workgroup ids are remapped so that tiles running at the same time on one XCD
 // (which owns one L2) share A and B panels.  Long contractions with few
 // output tiles are split along K; the partial sums land in the workspace and a
 // second kernel adds them in a fixed order.
+#include <type_traits>
+
 #include "fp4_device.h"
 #include "mxfp4_internal.h"
 
@@ -76,6 +79,7 @@ struct GemmArgs {
   int k_tiles;              // stages over the whole contraction
   int splits;
   int ntm, ntn;
+  int rem;                  // MXFP4: remainder tiles run as two 256 x 128 halves (see the kernel)
 };
 
 // Tile order: consecutive workgroup ids go to consecutive XCDs, so gather
@@ -301,242 +305,340 @@ __device__ __forceinline__ void store_tile_f32x4(const GemmArgs& p, float* Cz, i
   }
 }
 
-// The MXFP4 kernel runs 8 waves per workgroup (2 per SIMD): one wave per SIMD
-// cannot keep enough loads in flight (measured on gfx950: about 40 GB/s per
-// CU from L2 with 4 waves, 65 GB/s with 8), and the second wave per SIMD hides
-// LDS latency.  Wave w owns output rows 128 (w / 4) .. +128 and columns
-// 64 (w % 4) .. +64: 4 x 2 MFMA tiles, 128 accumulators per lane.
+// MXFP4 kernel.  Workgroup = 4 waves (one per SIMD), output tile 256 x 256,
+// wave (wm, wn) owns rows 128 wm .. +128 and columns 128 wn .. +128: 4 x 4
+// MFMA tiles, 256 fp32 accumulators per lane (held in AGPRs).  Per output
+// element pair this reads each LDS fragment once per 128 MACs, so LDS traffic
+// (fragment reads plus the buffer->LDS fills) stays under the MFMA time.
 //
-// LDS: a ring of 4 code stages (A and B, 64 B per row each) and a ring of 3
-// scale groups.  A scale group holds 16 scale bytes per row = 4 stages, so each
-// row's scales arrive as one 16-byte load instead of four 4-byte loads (the
-// scale rows are K/32 bytes apart, so every small load is a separate cache
-// line).  Group G is loaded in four 64-row pieces alongside stages 4G-4..4G-1.
-constexpr int MX_WAVES = 8;
-constexpr int MX_TM = 4;
-constexpr int MX_CODE_STAGE = A_BYTES + B_BYTES;               // 32 KB
-constexpr int MX_SG_BYTES = BM * 16;                            // one operand's scale group: 4 KB
-constexpr int MX_SCALE_OFF = NSTAGE * MX_CODE_STAGE;            // 128 KB
-constexpr int MX_SGROUPS = 3;
-constexpr int MX_SPARE_OFF = MX_SCALE_OFF + MX_SGROUPS * 2 * MX_SG_BYTES;   // 152 KB
-constexpr int MX_LDS = MX_SPARE_OFF + 6 * 1024;                             // + 1 KB sink per wave 2..7
+// K stage = 256 elements: every operand row contributes 128 bytes, one whole
+// cache line, to a stage, so each buffer->LDS instruction (64 lanes x 16 B)
+// moves 8 complete lines.  Two stages (64 KB each) alternate; the loads for
+// stage a + 2 are issued right after the barrier that ends the reads of stage
+// a and have a full stage of MFMAs to land.
+//
+// Stage layout: row r at r * 128, 16-byte chunk c (contraction 32c .. 32c+31,
+// one MX block) at position c ^ ((r >> 1) & 7).  The LDS of gfx950 serves 256
+// bytes (64 banks) per clock, i.e. 16 lanes of a 16-byte read; an MFMA
+// fragment read has lanes l = 0..31 take rows r0 + l at one chunk index, and
+// among 16 consecutive rows the rows of equal parity (same 128-byte half of
+// the bank space) then sit at eight distinct positions: no bank conflicts
+// (measured with SQ_LDS_BANK_CONFLICT; XORing with r & 7 leaves 2-way ones).
+//
+// Scales: a scale group is 16 bytes per row = two stages.  Group G is loaded
+// one operand at a time, A in the iteration of stage 2G - 3 and B in that of
+// 2G - 2, into one of three group buffers, so a stage's scales are in LDS a
+// full iteration before the stage starts and can be read under the MFMAs of
+// the stage before.  Lanes read a row's whole 16 bytes (16 consecutive rows =
+// 256 contiguous bytes, conflict-free); the stage's two scale bytes per
+// 64-wide step (one per lane half) are then rearranged with one byte permute
+// per row block so that step s takes byte s of a register.
+constexpr int MX_BK = 256;                       // contraction elements per stage
+constexpr int MX_ROW = MX_BK / 2;                // 128 code bytes per row per stage
+constexpr int MX_OPND = 256 * MX_ROW;            // one operand's codes per stage: 32 KB
+constexpr int MX_STAGE = 2 * MX_OPND;            // 64 KB
+constexpr int MX_GROUP_OPND = 256 * 16;          // one operand's scale group: 4 KB
+constexpr int MX_GROUP_OFF = 2 * MX_STAGE;       // 128 KB
+constexpr int MX_GROUPS = 3;                     // scale group buffers
+constexpr int MX_LDS = MX_GROUP_OFF + MX_GROUPS * 2 * MX_GROUP_OPND;   // 152 KB
+constexpr int MX_LOADS = 17;                     // buffer->LDS instructions per wave per stage
 
-template <int NW>
-struct MxOperand {
-  static constexpr int CL = 256 / (16 * NW);   // 16-row code loads per wave per stage
-  __amdgpu_buffer_rsrc_t codes, scales;
-  uint32_t code_off[CL];  // this lane's code offsets in stage 0
-  uint32_t scale_row;     // byte offset of row (lane) in the scales, for 64-row piece 0
+// Per-wave operand blocks: TM = 4 row blocks of A (128 rows), TN = 4 or 2
+// column blocks of B (128 or 64 columns); TN = 2 serves the 256 x 128
+// half-tiles of the balanced schedule (below).
+template <int TN>
+struct MxFrag {
+  v4i a[4], b[TN];
 };
 
-template <int NW>
-__device__ __forceinline__ MxOperand<NW> mx_make_operand(const uint8_t* codes, const uint8_t* scales, int64_t rows_total,
-                                                     int64_t row0, int64_t K) {
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+// Fragments of 64-wide step s of a stage for this lane: rows ra0 + 32t of A
+// and rb0 + 32t of B, chunk 2s + (lane half).
+template <int TN>
+__device__ __forceinline__ void mx_read_frag(const uint8_t* st, int ra0, int rb0, int pos_byte, MxFrag<TN>& f) {
+#pragma unroll
+  for (int t = 0; t < 4; t++) f.a[t] = *(const v4i*)(st + (ra0 + 32 * t) * MX_ROW + pos_byte);
+#pragma unroll
+  for (int t = 0; t < TN; t++) f.b[t] = *(const v4i*)(st + MX_OPND + (rb0 + 32 * t) * MX_ROW + pos_byte);
+}
+
+// The 16 scale bytes of this lane's rows (A rows ra0 + 32t, then B rows
+// rb0 + 32t) in one group.
+template <int TN>
+__device__ __forceinline__ void mx_read_group(const uint8_t* grp, int ra0, int rb0, u32v4 (&d)[4 + TN]) {
+#pragma unroll
+  for (int t = 0; t < 4; t++) d[t] = *(const u32v4*)(grp + (ra0 + 32 * t) * 16);
+#pragma unroll
+  for (int t = 0; t < TN; t++) d[4 + t] = *(const u32v4*)(grp + MX_GROUP_OPND + (rb0 + 32 * t) * 16);
+}
+
+// Scale registers of one stage from its group's bytes: byte s = this lane's
+// block of step s.  HALF = stage parity inside the group; sel picks the lane
+// half's bytes; mask clears the bytes of steps past K (their products then
+// vanish).
+template <int HALF, int TN>
+__device__ __forceinline__ void mx_stage_scales(const u32v4 (&d)[4 + TN], uint32_t sel, uint32_t mask,
+                                                uint32_t (&sa)[4], uint32_t (&sb)[TN]) {
+#pragma unroll
+  for (int t = 0; t < 4; t++) sa[t] = __builtin_amdgcn_perm(d[t][2 * HALF + 1], d[t][2 * HALF], sel) & mask;
+#pragma unroll
+  for (int t = 0; t < TN; t++)
+    sb[t] = __builtin_amdgcn_perm(d[4 + t][2 * HALF + 1], d[4 + t][2 * HALF], sel) & mask;
+}
+
+template <int S, int TN>
+__device__ __forceinline__ void mx_mfma(v16f (&acc)[4][TN], const MxFrag<TN>& f, const uint32_t (&sa)[4],
+                                        const uint32_t (&sb)[TN]) {
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const v8i a = __builtin_shufflevector(f.a[i], f.a[i], 0, 1, 2, 3, -1, -1, -1, -1);
+#pragma unroll
+    for (int j = 0; j < TN; j++) {
+      const v8i b = __builtin_shufflevector(f.b[j], f.b[j], 0, 1, 2, 3, -1, -1, -1, -1);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 4, 4, S, (int)sa[i], S,
+                                                                 (int)sb[j]);
+    }
+  }
+}
+
+// Scheduling of one step: NM MFMAs with, ahead of each of the first ones, one
+// buffer->LDS load (NV of them) and one DS read (ND of them), in the program
+// order in which they were issued.
+template <int NV, int ND, int NM>
+__device__ __forceinline__ void mx_sched() {
+#pragma unroll
+  for (int q = 0; q < NM; q++) {
+    if (q < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one buffer->LDS load
+    if (q < ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // one MFMA
+  }
+  if (NV > NM) __builtin_amdgcn_sched_group_barrier(0x020, NV - NM, 0);
+  if (ND > NM) __builtin_amdgcn_sched_group_barrier(0x100, ND - NM, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Operand resources of one tile: they end at the operand's last row of the
+// tile (at most ROWS rows from its first), so rows past M or N read as zeros.
+// Each wave loads RPW = ROWS / 4 rows per stage, 8 rows per load.
+struct MxOperand {
+  __amdgpu_buffer_rsrc_t codes, scales;
+  uint32_t code_off[2];  // this lane's offset for loads 0 and 1 of the wave (load j: [j & 1] + (j >> 1) * 16 rows)
+  uint32_t scale_off;    // this lane's row in the wave's 64-row scale piece
+};
+
+template <int ROWS>
+__device__ __forceinline__ MxOperand mx_make_operand(const uint8_t* codes, const uint8_t* scales, int64_t rows_total,
+                                                     int64_t row0, int64_t K, int w, int l) {
+  constexpr int RPW = ROWS / 4;
   const int64_t krow = K / 2, srow = K / 32;
   int64_t nrows = rows_total - row0;
-  if (nrows > 256) nrows = 256;
-  MxOperand<NW> o;
-  constexpr int CL = MxOperand<NW>::CL;
+  if (nrows > ROWS) nrows = ROWS;
+  if (nrows < 0) nrows = 0;   // a half tile wholly past N
+  MxOperand o;
   o.codes = __builtin_amdgcn_make_buffer_rsrc((void*)(codes + row0 * krow), (short)0, (int)(nrows * krow), kRsrcWord3);
   o.scales = __builtin_amdgcn_make_buffer_rsrc((void*)(scales + row0 * srow), (short)0, (int)(nrows * srow), kRsrcWord3);
+  // load j of wave w fills rows RPW w + 8j .. +7; lane l writes position l & 7
+  // of row r = RPW w + 8j + (l >> 3), i.e. chunk (l & 7) ^ ((r >> 1) & 7), where
+  // (r >> 1) & 7 = (4j + (l >> 4)) & 7 depends on the parity of j only
 #pragma unroll
-  for (int j = 0; j < CL; j++) {
-    const int row = 16 * CL * w + 16 * j + (l >> 2);
-    o.code_off[j] = (uint32_t)(row * krow + (((l & 3) ^ swz(row)) * 16));
+  for (int j = 0; j < 2; j++) {
+    const int row = RPW * w + 8 * j + (l >> 3);
+    o.code_off[j] = (uint32_t)(row * krow + (((l & 7) ^ ((row >> 1) & 7)) << 4));
   }
-  o.scale_row = (uint32_t)(l * srow);
+  // scale piece w is rows 64w .. 64w + 63 (past ROWS: out of range, zeros)
+  o.scale_off = (uint32_t)((64 * w + l) * srow);
   return o;
 }
 
-// This wave's 256/NW rows of one operand's codes for absolute stage kt.
-template <int NW>
-__device__ __forceinline__ void mx_issue_codes(const MxOperand<NW>& o, uint8_t* codes_lds, int kt) {
-  constexpr int CL = MxOperand<NW>::CL;
-  const int w = threadIdx.x >> 6;
-  const uint32_t kb = (uint32_t)kt * ROWB;
+// Code loads L0 .. L1-1 of this wave for absolute stage kt into stage buffer
+// st: loads 0..7 are A's (64 rows per wave), loads 8.. B's (16 TN rows per
+// wave, 2 TN loads).
+template <int L0, int L1, int TN>
+__device__ __forceinline__ void mx_issue_codes(const MxOperand& oa, const MxOperand& ob, uint8_t* st, int kt,
+                                               uint32_t krow16, int w) {
+  const int soff = kt * MX_ROW;
 #pragma unroll
-  for (int j = 0; j < CL; j++)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(o.codes, (lds_void*)(codes_lds + (16 * CL * w + 16 * j) * ROWB), 16,
-                                             o.code_off[j] + kb, 0, 0, 0);
-}
-// Rows 64 piece .. +63 of a scale group starting at absolute stage kt_first:
-// 16 bytes (4 stages) per row, from `rsrc` into `dst` (1 KB).
-__device__ __forceinline__ void mx_issue_scale_piece_to(__amdgpu_buffer_rsrc_t rsrc, uint32_t scale_row, uint8_t* dst,
-                                                        int piece, int kt_first, uint32_t srow) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16,
-                                           scale_row + (uint32_t)(64 * piece) * srow + (uint32_t)kt_first * 4u,
-                                           0, 0, 0);
-}
-template <int NW>
-__device__ __forceinline__ void mx_issue_scale_piece(const MxOperand<NW>& o, uint8_t* group_lds, int piece, int kt_first,
-                                                     uint32_t srow) {
-  mx_issue_scale_piece_to(o.scales, o.scale_row, group_lds + piece * 64 * 16, piece, kt_first, srow);
-}
-
-template <int MX_TN>
-struct MxFrag {
-  v4i a[MX_TM], b[MX_TN];
-};
-
-// One wave's operand fragments of sub-step s (blocks 2g + s) of a stage.
-template <int MX_TN>
-__device__ __forceinline__ void mx_load_frag(const uint8_t* st, int ra0, int rb0, int offc, MxFrag<MX_TN>& f) {
-  const uint8_t* A = st;
-  const uint8_t* B = st + A_BYTES;
-#pragma unroll
-  for (int t = 0; t < MX_TM; t++) f.a[t] = *(const v4i*)(A + (ra0 + 32 * t) * ROWB + offc);
-#pragma unroll
-  for (int t = 0; t < MX_TN; t++) f.b[t] = *(const v4i*)(B + (rb0 + 32 * t) * ROWB + offc);
-}
-
-// Scale bytes of blocks 2g, 2g+1 of stage j (0..3) of a group, for each of the lane's rows.
-template <int MX_TN>
-__device__ __forceinline__ void mx_load_scales(const uint8_t* grp, int ra0, int rb0, int j, int g, int (&sa)[MX_TM],
-                                               int (&sb)[MX_TN]) {
-  const uint8_t* SA = grp;
-  const uint8_t* SB = grp + MX_SG_BYTES;
-#pragma unroll
-  for (int t = 0; t < MX_TM; t++) sa[t] = *(const uint16_t*)(SA + (ra0 + 32 * t) * 16 + 4 * j + 2 * g);
-#pragma unroll
-  for (int t = 0; t < MX_TN; t++) sb[t] = *(const uint16_t*)(SB + (rb0 + 32 * t) * 16 + 4 * j + 2 * g);
-}
-
-template <int S, int MX_TN>
-__device__ __forceinline__ void mx_mfma(v16f (&acc)[MX_TM][MX_TN], const MxFrag<MX_TN>& f, const int (&sa)[MX_TM],
-                                        const int (&sb)[MX_TN]) {
-#pragma unroll
-  for (int i = 0; i < MX_TM; i++) {
-    const v8i a = __builtin_shufflevector(f.a[i], f.a[i], 0, 1, 2, 3, -1, -1, -1, -1);
-#pragma unroll
-    for (int j = 0; j < MX_TN; j++) {
-      const v8i b = __builtin_shufflevector(f.b[j], f.b[j], 0, 1, 2, 3, -1, -1, -1, -1);
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 4, 4, S, sa[i], S, sb[j]);
-    }
+  for (int L = L0; L < L1; L++) {
+    const int j = L < 8 ? L : L - 8;
+    const int rpw = L < 8 ? 64 : 16 * TN;
+    const MxOperand& o = L < 8 ? oa : ob;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(o.codes,
+                                             (lds_void*)(st + (L < 8 ? 0 : MX_OPND) + (rpw * w + 8 * j) * MX_ROW),
+                                             16, o.code_off[j & 1] + (uint32_t)(j >> 1) * krow16, soff, 0, 0);
   }
 }
 
-// Main loop, software-pipelined so that LDS reads always run under MFMAs:
-//   stage i:  read sub-step 1 fragments | MFMAs of sub-step 0
-//             wait for stage i+1, barrier, refill stage i's buffer with i+4
-//             read stage i+1 sub-step 0 | MFMAs of sub-step 1
-// Stage i's buffer is refilled right after the barrier that follows the last
-// read of it, so four buffers keep three stages of loads in flight.  The loop
-// body has no branches (stages past the end are loaded into buffers that are
-// never read again, and reads past the end are never consumed): a branch would
-// let the compiler sink the first MFMA group below the barrier.
-template <int NW>
-__global__ void __launch_bounds__(64 * NW, 1) gemm_mx_kernel(GemmArgs p) {
-  constexpr int MX_TN = 16 / NW;            // 4 waves: 128 x 128 per wave; 8 waves: 128 x 64
-  constexpr int WN = NW / 2;                 // waves along N
-  __shared__ __attribute__((aligned(16))) uint8_t smem[MX_LDS];
-  int tm_, tn_;
-  tile_coords(p, tm_, tn_);
-  const int64_t m0 = (int64_t)tm_ * BM, n0 = (int64_t)tn_ * BN;
-  const int z = blockIdx.y;
-  const int kt0 = (int)((int64_t)p.k_tiles * z / p.splits), kt1 = (int)((int64_t)p.k_tiles * (z + 1) / p.splits);
-  const int nk = kt1 - kt0;
+// One output tile (256 x 64 TN), contraction stages kt0 .. kt1-1 (kt0 even).
+// Iteration a (stage a), each step = 4 TN MFMAs with the next step's
+// fragment reads under them:
+//   step 0: + loads 6..11 of stage a + 1
+//   step 1: + loads 12.. of stage a + 1, the scale piece of iteration a, and
+//           the scale bytes of stage a + 1 (when a + 1 opens a group)
+//   step 2: then stage a + 1's scale registers
+//   wait for this wave's loads of stage a + 1 and its LDS reads; barrier
+//   step 3: stage a + 1's step-0 fragments first, + loads 0..5 of stage a + 2
+//           (into stage a's buffer)
+// A stage's buffer->LDS loads are spread over three steps: bunched into one,
+// they back up the address unit and the stalled load issue holds back the
+// MFMAs queued behind it.  The body has no branches: loads for stages past
+// the end land in buffers that are never read again, and reads past the end
+// are never consumed.
+template <int TN>
+__device__ __forceinline__ void mx_tile(const GemmArgs& p, uint8_t* smem, int64_t m0, int64_t n0, int kt0, int kt1,
+                                        float* Cz) {
+  constexpr int NL = 8 + 2 * TN;   // code loads per wave per stage
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63, h = l >> 5;
+  const int wm = w >> 1, wn = w & 1;
+  const int ra0 = wm * 128 + (l & 31), rb0 = wn * (32 * TN) + (l & 31);
+  auto pos = [&](int c) { return ((c ^ ((l >> 1) & 7)) << 4); };   // chunk c of a row r with r % 32 == l % 32
+  const uint32_t sel = h ? 0x07050301u : 0x06040200u;
+  const int ksteps = (int)(p.K / 64);                              // 64-wide steps in the whole contraction
 
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar branches
-  const int l = threadIdx.x & 63, g = l >> 5;
-  const int wm = w / WN, wn = w % WN;
-  const int ra0 = wm * 128 + (l & 31), rb0 = wn * (32 * MX_TN) + (l & 31);
-  const int zs = swz(ra0);            // equal for every t (t * 32 leaves bits 2..3 alone), and for rb0
-  const int offc0 = ((2 * g + 0) ^ zs) << 4, offc1 = ((2 * g + 1) ^ zs) << 4;
-
-  v16f acc[MX_TM][MX_TN];
+  v16f acc[4][TN];
 #pragma unroll
-  for (int i = 0; i < MX_TM; i++)
+  for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < MX_TN; j++) acc[i][j] = (v16f){};
+    for (int j = 0; j < TN; j++) acc[i][j] = (v16f){};
 
-  if (nk > 0) {
-    // buffer->LDS instructions per wave per stage: the code loads plus one
-    // scale load.  Waves 0 and 1 load the scale pieces; the other waves issue
-    // the same instruction on an empty buffer (out of range: no memory
-    // traffic, zeros into a private LDS sink), so every wave has the same
-    // count and "at most 2 * LOADS outstanding" is exact.
-    constexpr int LOADS = 2 * MxOperand<NW>::CL + 1;
-    const uint32_t srow = (uint32_t)(p.K / 32);
-    const MxOperand<NW> oa = mx_make_operand<NW>(p.a, p.as, p.M, m0, p.K);
-    const MxOperand<NW> ob = mx_make_operand<NW>(p.b, p.bs, p.N, n0, p.K);
-    const __amdgpu_buffer_rsrc_t srsrc =
-        w == 0 ? oa.scales : w == 1 ? ob.scales : __builtin_amdgcn_make_buffer_rsrc((void*)p.as, (short)0, 0, kRsrcWord3);
-    // scale destinations as arithmetic on wave-uniform values (no branches in the loop)
-    const int sc_real = w < 2 ? 1 : 0;
-    uint8_t* const sc_base = sc_real ? smem + MX_SCALE_OFF + w * MX_SG_BYTES : smem + MX_SPARE_OFF + (w - 2) * 1024;
-    auto stage = [&](int i) { return smem + (i & (NSTAGE - 1)) * MX_CODE_STAGE; };
-    auto group = [&](int h) { return smem + MX_SCALE_OFF + (h % MX_SGROUPS) * 2 * MX_SG_BYTES; };
-    // stage i's codes, and scale piece i % 4 of group i / 4 + 1.  Stages and
-    // groups at or past the end load whatever lies there (in bounds of the
-    // operand buffers, or zero past them) into buffers that are never read.
-    auto issue = [&](int i) {
-      uint8_t* st = stage(i);
-      mx_issue_codes(oa, st, kt0 + i);
-      mx_issue_codes(ob, st + A_BYTES, kt0 + i);
-      const int h = (i >> 2) + 1;
-      uint8_t* sdst = sc_base + sc_real * ((h % MX_SGROUPS) * 2 * MX_SG_BYTES + (i & 3) * 1024);
-      mx_issue_scale_piece_to(srsrc, oa.scale_row, sdst, i & 3, kt0 + 4 * h, srow);
+  if (kt1 > kt0) {
+    const uint32_t krow16 = (uint32_t)(16 * (p.K / 2));
+    const MxOperand oa = mx_make_operand<256>(p.a, p.as, p.M, m0, p.K, w, l);
+    const MxOperand ob = mx_make_operand<64 * TN>(p.b, p.bs, p.N, n0, p.K, w, l);
+    auto stage = [&](int a) { return smem + (a & 1) * MX_STAGE; };
+    auto group = [&](int G) { return smem + MX_GROUP_OFF + (G % MX_GROUPS) * 2 * MX_GROUP_OPND; };
+    // scale-byte mask of absolute stage a: bytes of the 64-wide steps below K
+    auto mask_of = [&](int a) -> uint32_t {
+      const int v = min(max(ksteps - 4 * a, 0), 4);
+      return (uint32_t)((1ull << (8 * v)) - 1ull);
     };
-    // prologue: scale group 0 (8 pieces spread over the waves), then stages 0..2
-#pragma unroll
-    for (int q = 0; q < 8 / NW; q++) {
-      const int piece = w * (8 / NW) + q;
-      if (piece < 4) mx_issue_scale_piece(oa, group(0), piece, kt0, srow);
-      else mx_issue_scale_piece(ob, group(0) + MX_SG_BYTES, piece - 4, kt0, srow);
-    }
-    issue(0);
-    issue(1);
-    issue(2);
-    wait_cnt<2 * LOADS, 15>();
-    block_barrier();
-    issue(3);
+    // piece w of one operand's scale group G (a value select of the resource
+    // on a uniform flag; the row offset is the same for both operands)
+    auto issue_piece = [&](int G, int b_side) {
+      const __amdgpu_buffer_rsrc_t r = b_side ? ob.scales : oa.scales;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(group(G) + b_side * MX_GROUP_OPND + w * 1024), 16,
+                                               oa.scale_off, 16 * G, 0, 0);
+    };
 
-    MxFrag<MX_TN> f0, f1;
-    int sa[MX_TM], sb[MX_TN], sa_n[MX_TM], sb_n[MX_TN];
-    mx_load_scales(group(0), ra0, rb0, 0, g, sa, sb);
-    mx_load_frag(stage(0), ra0, rb0, offc0, f0);
-    for (int i = 0; i < nk; i++) {
-      // phase A: sub-step 1 fragment reads under the sub-step 0 MFMAs
-      mx_load_frag(stage(i), ra0, rb0, offc1, f1);
-      mx_mfma<0>(acc, f0, sa, sb);
-#pragma unroll
-      for (int q = 0; q < MX_TM + MX_TN; q++) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, MX_TN / 2 + 1, 0);   // MFMAs
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      // stage i+1 has landed for this wave, and its own reads of stage i are done
-      wait_cnt<2 * LOADS, 0>();
+    // prologue: group kt0/2 (A and B), group kt0/2 + 1's A piece (the piece
+    // of iteration kt0 - 1), stage kt0, and the first part of stage kt0 + 1
+    // (iteration kt0 issues the rest)
+    const int G0 = kt0 >> 1;
+    issue_piece(G0, 0);
+    issue_piece(G0, 1);
+    issue_piece(G0 + 1, 0);
+    mx_issue_codes<0, NL, TN>(oa, ob, stage(kt0), kt0, krow16, w);
+    mx_issue_codes<0, 6, TN>(oa, ob, stage(kt0 + 1), kt0 + 1, krow16, w);
+    wait_cnt<6, 15>();
+    block_barrier();
+
+    MxFrag<TN> f0, f1;
+    uint32_t sa[4], sb[TN];
+    u32v4 gd[4 + TN];
+    mx_read_group<TN>(group(G0), ra0, rb0, gd);
+    mx_stage_scales<0, TN>(gd, sel, mask_of(kt0), sa, sb);
+    mx_read_frag<TN>(stage(kt0), ra0, rb0, pos(h), f0);
+    // one iteration; H = a & 1 (kt0 is even, the loop takes stages in pairs)
+    auto iteration = [&](auto Hc, int a) {
+      constexpr int H = decltype(Hc)::value;
+      constexpr int NM = 4 * TN;              // MFMAs per step
+      constexpr int NF = 4 + TN;              // fragment reads per step
+      const uint8_t* st = stage(H);
+      mx_issue_codes<6, (NL < 12 ? NL : 12), TN>(oa, ob, stage(H ^ 1), a + 1, krow16, w);
+      mx_read_frag<TN>(st, ra0, rb0, pos(2 + h), f1);
+      mx_mfma<0, TN>(acc, f0, sa, sb);
+      mx_sched<(NL < 12 ? NL : 12) - 6, NF, NM>();
+      mx_issue_codes<(NL < 12 ? NL : 12), NL, TN>(oa, ob, stage(H ^ 1), a + 1, krow16, w);
+      // iteration a's scale piece: group (a + 3) / 2's A piece when a is odd,
+      // group a / 2 + 1's B piece when a is even.  Group G is then complete at
+      // the barrier of iteration 2G - 2, before stage 2G's scale bytes are
+      // read in iteration 2G - 1, and its buffer last held group G - 3.
+      issue_piece(H ? (a + 3) >> 1 : (a >> 1) + 1, H ^ 1);
+      if (H) mx_read_group<TN>(group((a + 1) >> 1), ra0, rb0, gd);   // stage a + 1 opens the next group
+      mx_read_frag<TN>(st, ra0, rb0, pos(4 + h), f0);
+      mx_mfma<1, TN>(acc, f1, sa, sb);
+      mx_sched<NL - (NL < 12 ? NL : 12) + 1, NF + (H ? 4 + TN : 0), NM>();
+      mx_read_frag<TN>(st, ra0, rb0, pos(6 + h), f1);
+      mx_mfma<2, TN>(acc, f0, sa, sb);
+      uint32_t sa_n[4], sb_n[TN];
+      mx_stage_scales<H ^ 1, TN>(gd, sel, mask_of(a + 1), sa_n, sb_n);
+      mx_sched<0, NF, NM>();
+      wait_cnt<0, 0>();
       block_barrier();
-      // phase B: the loads of stage i+4, and the scales and sub-step 0
-      // fragments of stage i+1, spread under the sub-step 1 MFMAs.  A load
-      // instruction can stall its wave while the memory pipeline is full, so
-      // each one is separated by MFMAs already queued.
-      issue(i + 4);
-      mx_load_scales(group((i + 1) >> 2), ra0, rb0, (i + 1) & 3, g, sa_n, sb_n);
-      mx_load_frag(stage(i + 1), ra0, rb0, offc0, f0);
-      mx_mfma<1>(acc, f1, sa, sb);
+      mx_read_frag<TN>(stage(H ^ 1), ra0, rb0, pos(h), f0);
+      mx_issue_codes<0, 6, TN>(oa, ob, stage(H), a + 2, krow16, w);
+      mx_mfma<3, TN>(acc, f1, sa, sb);
+      // the fragment reads first, then the loads, over the MFMAs
 #pragma unroll
-      for (int q = 0; q < LOADS; q++) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one buffer->LDS load
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two DS reads
+      for (int q = 0; q < NF; q++) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one DS read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+#pragma unroll
+      for (int q = 0; q < 6; q++) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one buffer->LDS load
+        if (NF + q < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      }
+      if (NM > NF + 6) __builtin_amdgcn_sched_group_barrier(0x008, NM - NF - 6, 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int t = 0; t < MX_TM; t++) sa[t] = sa_n[t];
+      for (int t = 0; t < 4; t++) sa[t] = sa_n[t];
 #pragma unroll
-      for (int t = 0; t < MX_TN; t++) sb[t] = sb_n[t];
+      for (int t = 0; t < TN; t++) sb[t] = sb_n[t];
+    };
+    // an odd stage count only happens at the end of K: the extra stage then
+    // lies past K, so its scale mask is zero and it adds nothing
+    for (int a = kt0; a < kt1; a += 2) {
+      iteration(std::integral_constant<int, 0>{}, a);
+      iteration(std::integral_constant<int, 1>{}, a + 1);
     }
     wait_cnt<0, 0>();   // nothing may still write LDS when the workgroup exits
   }
-  // epilogue
+  store_tile_f32x4<4, TN>(p, Cz, m0 + wm * 128, n0 + wn * (32 * TN), acc);
+}
+
+// Work items.  Without split-K the grid is laid out as
+//   [R half tiles (first halves)] [T - R full tiles] [R half tiles (second halves)]
+// where T = 256 x 256 tiles and R = T mod (compute units) (p.rem; 0 when the
+// tiles divide evenly or a split is used): the R remainder tiles are cut into
+// two 256 x 128 halves, one run by the first workgroups and one by the last,
+// so every compute unit ends at the same time and the C stores of the two
+// groups of compute units fall at alternating times.  Within each range,
+// consecutive workgroup ids go to consecutive XCDs, so the ids one XCD runs
+// are gathered into a contiguous run of tiles, walked in groups of GROUP_M
+// tile rows.
+__device__ __forceinline__ int mx_walk(const GemmArgs& p, int t, int& tn) {
+  constexpr int GROUP_M = MXFP4_GROUP_M;
+  const int group = t / (GROUP_M * p.ntn);
+  const int first_m = group * GROUP_M;
+  const int gm = min(p.ntm - first_m, GROUP_M);
+  const int in_group = t - group * GROUP_M * p.ntn;
+  tn = in_group / gm;
+  return first_m + in_group % gm;
+}
+__device__ __forceinline__ int xcd_gather(int id, int n) {
+  return (n & 7) == 0 ? (id & 7) * (n >> 3) + (id >> 3) : id;
+}
+
+// Split ranges start on even stages (a scale group spans two stages).
+__global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[MX_LDS];
+  const int b = blockIdx.x, z = blockIdx.y;
+  const int pairs = (p.k_tiles + 1) >> 1;
+  const int kt0 = 2 * (int)((int64_t)pairs * z / p.splits);
+  int kt1 = 2 * (int)((int64_t)pairs * (z + 1) / p.splits);
+  if (kt1 > p.k_tiles) kt1 = p.k_tiles;
   float* Cz = p.C + (int64_t)z * p.split_stride;
-  store_tile_f32x4<MX_TM, MX_TN>(p, Cz, m0 + wm * 128, n0 + wn * (32 * MX_TN), acc);
+  const int R = p.rem, T = p.ntm * p.ntn, F = T - R;
+  int tm, tn;
+  if (b >= R && b < R + F) {
+    tm = mx_walk(p, xcd_gather(b - R, F), tn);
+    mx_tile<4>(p, smem, (int64_t)tm * BM, (int64_t)tn * BN, kt0, kt1, Cz);
+  } else {
+    const int second = b >= R + F;
+    const int i = second ? b - R - F : b;
+    tm = mx_walk(p, F + xcd_gather(i, R), tn);
+    mx_tile<2>(p, smem, (int64_t)tm * BM, (int64_t)tn * BN + 128 * second, kt0, kt1, Cz);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -646,22 +748,38 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
 // Planning and launch
 // ---------------------------------------------------------------------------
 GemmPlan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
-  (void)fmt;
+  const bool mx = fmt == FMT_MX;
   GemmPlan pl;
-  pl.k_tiles = (K + BK - 1) / BK;
+  pl.k_tiles = (K + (mx ? MX_BK : BK) - 1) / (mx ? MX_BK : BK);
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  // the MXFP4 kernel splits in pairs of stages (one scale group)
+  const int64_t units = mx ? (pl.k_tiles + 1) / 2 : pl.k_tiles;
+  const int64_t min_units = mx ? 2 : 4;        // at least 4 stages of 256 / 128 per split
   int splits = 1;
   // fewer output tiles than compute units: split the contraction so that
-  // about one wave of workgroups fills the chip, keeping >= 4 stages per split
+  // about one wave of workgroups fills the chip
   const int64_t cus = 256;
-  if (tiles < cus && pl.k_tiles >= 8) {
+  if (tiles < cus && units >= 2 * min_units) {
     int64_t s = cus / tiles;
-    if (s > pl.k_tiles / 4) s = pl.k_tiles / 4;
+    if (s > units / min_units) s = units / min_units;
     if (s > 32) s = 32;
     if (s > 1) splits = (int)s;
   }
   pl.splits = splits;
   return pl;
+}
+
+// Compute units of the current device (cached per device).
+static int compute_units() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 static hipError_t launch_gemm_common(bool nv, GemmArgs p, float* C, int64_t ldc, float* workspace,
@@ -679,9 +797,15 @@ static hipError_t launch_gemm_common(bool nv, GemmArgs p, float* C, int64_t ldc,
     p.ldc = ldc;
     p.split_stride = 0;
   }
-  dim3 grid((unsigned)(p.ntm * p.ntn), (unsigned)plan.splits);
+  p.rem = 0;
+  const int64_t tiles = (int64_t)p.ntm * p.ntn;
+  if (!nv && plan.splits == 1) {
+    const int64_t cus = compute_units();
+    if (tiles > cus && tiles % cus != 0) p.rem = (int)(tiles % cus);
+  }
+  dim3 grid((unsigned)(tiles + p.rem), (unsigned)plan.splits);
   if (nv) hipLaunchKernelGGL(gemm_nv_kernel, grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(gemm_mx_kernel<MX_WAVES>, grid, dim3(64 * MX_WAVES), 0, stream, p);
+  else hipLaunchKernelGGL(gemm_mx_kernel, grid, dim3(256), 0, stream, p);
   if (plan.splits > 1) {
     int64_t work = p.M * p.N;
     int64_t g = (work + 255) / 256;

@@ -24,10 +24,12 @@ def _quant_pair(mx, oracle_mod, A_bits, B_bits, fmt, had=False, rnd="rtn", axis_
 
 @pytest.mark.parametrize("fmt", ["mx", "nv"])
 @pytest.mark.parametrize("M,N,K", [(256, 256, 1024), (300, 200, 384), (17, 529, 256), (512, 768, 2048),
-                                   (64, 96, 8192), (1, 1, 128)])
+                                   (64, 96, 8192), (1, 1, 128), (128, 160, 640), (64, 64, 4224)])
 def test_gemm_small_full_check(oracle_mod, fmt, M, N, K):
-    """Several tiles with ragged edges, a short contraction, one split-K case
-    (64 x 96 x 8192) and a 1 x 1 output; every element checked."""
+    """Several tiles with ragged edges, short contractions, contractions that
+    end half way into a 256-wide stage (384, 640, 128, 4224), split-K cases
+    (64 x 96 x 8192; 64 x 64 x 4224 with an odd stage count) and a 1 x 1
+    output; every element checked."""
     mx = need_gpu()
     A = workloads.small_t_bf16((M, K), 3.0, seed=31, outlier_frac=0.02)
     B = workloads.small_normal_bf16((N, K), 0.02, seed=32)
@@ -106,6 +108,30 @@ def test_gemm_headline_sampled(oracle_mod):
     say("headline quantize")
     qa, qb, oa, ob = _quant_pair(mx, oracle_mod, A, B, "mx")
     _sampled_check(mx, oracle_mod, qa, qb, oa, ob, "mx", "headline", nsample=24)
+
+
+def test_gemm_balanced_half_tiles(oracle_mod):
+    """More 256 x 256 tiles than compute units, not a multiple of them: the
+    remainder tiles run as 256 x 128 halves at the start and at the end of
+    the launch.  M = 4352 (17 tile rows), N = 3904 (the last tile column has
+    64 valid columns, so its second half lies wholly past N); the 16
+    remainder tiles are the bottom tile row, checked in full."""
+    mx = need_gpu()
+    M, N, K = 4352, 3904, 512
+    A = workloads.small_t_bf16((M, K), 3.0, seed=36, outlier_frac=0.01)
+    B = workloads.small_normal_bf16((N, K), 0.02, seed=37)
+    qa, qb, oa, ob = _quant_pair(mx, oracle_mod, A, B, "mx")
+    say("gemm balanced", M, N, K)
+    C = mx.mxfp4_gemm(qa, qb)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(4096, M), np.arange(0, 4096, 97)])
+    Cr = C[torch.from_numpy(rows).cuda()].cpu().numpy()
+    Co, So = oracle_mod.gemm("mx", oa, ob, rows=rows)
+    assert_gemm_within(Cr, Co, So, "balanced rows")
+    cols = np.array([0, 1, 127, 128, 255, 256, 3839, 3840, 3871, 3872, N - 1])
+    Cc = C[:, torch.from_numpy(cols).cuda()].cpu().numpy()
+    Co, So = oracle_mod.gemm("mx", oa, ob, cols=cols)
+    assert_gemm_within(Cc, Co, So, "balanced cols")
 
 
 def test_gemm_config2_sampled(oracle_mod):
