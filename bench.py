@@ -47,6 +47,11 @@ def parse():
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into the traffic file")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "OUT_MD"),
                     help="turn a rocprofv3 --stats kernel_stats.csv into a short markdown summary")
+    ap.add_argument("--sweep", metavar="OUT_MD", nargs="?", const="-",
+                    help="time every quantizer call and GEMM of all workload configurations against their "
+                         "rooflines and write a markdown table (to stdout with no file)")
+    ap.add_argument("--sweep-reps", type=int, default=10)
+    ap.add_argument("--sweep-configs", default="1,2,3,4,5,0", help="comma-separated configurations to sweep")
     return ap.parse_args()
 
 
@@ -161,8 +166,148 @@ def cpu_baseline():
     }
 
 
+PEAK_FP16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA (the exact NVFP4 path)
+
+# The hot-path calls of each workload configuration: quantizer calls
+# (tensor, rounding, axis) and GEMMs (A call, B call).  Config 3's weights are
+# quantized once offline in the method; their quantization is timed too.
+# Config 4: fc1 = (X1, W1, dY1), fc2 = (X2, W2, dY2); config 5: one
+# (input, weight, output gradient) triple per projection.  Forward X W^T takes
+# both operands RTN along K; dgrad dY W takes dY along N (axis 1) and W along
+# its rows (axis 0); wgrad dY^T X takes both along the token axis (axis 0);
+# backward operands use stochastic rounding.
+def _training_gemms(triples):
+    calls, gemms = [], []
+    for name, (x, w, dy) in triples.items():
+        q = [(x, "rtn", 1), (w, "rtn", 1), (dy, "sr", 1), (w, "sr", 0), (dy, "sr", 0), (x, "sr", 0)]
+        calls += q
+        gemms += [(name + " fwd", q[0], q[1]), (name + " dgrad", q[2], q[3]), (name + " wgrad", q[4], q[5])]
+    return calls, gemms
+
+
+def sweep_plan():
+    plan = {}
+    c = [("X", "rtn", 1), ("W", "rtn", 1)]
+    plan[1] = (c, [("fwd", c[0], c[1])])
+    plan[2] = (c, [("fwd", c[0], c[1])])
+    c3 = [(t, "rtn", 1) for t in ("W_up", "W_down", "x_dec_up", "x_pre_up", "x_dec_down", "x_pre_down")]
+    plan[3] = (c3, [("decode up", c3[2], c3[0]), ("prefill up", c3[3], c3[0]),
+                    ("decode down", c3[4], c3[1]), ("prefill down", c3[5], c3[1])])
+    plan[4] = _training_gemms({"fc1": ("X1", "W1", "dY1"), "fc2": ("X2", "W2", "dY2")})
+    plan[5] = _training_gemms({"qkv": ("X", "W_qkv", "dY_qkv"), "o": ("X", "W_o", "dY_o"),
+                               "gate": ("X", "W_gate", "dY_gate"), "up": ("X", "W_up", "dY_gate"),
+                               "down": ("X_down", "W_down", "dY_down")})
+    c0 = [("A", "rtn", 1), ("B", "rtn", 1)]
+    plan[0] = (c0, [("fwd", c0[0], c0[1])])
+    return plan
+
+
+def sweep(args):
+    """Every quantizer call and GEMM of every configuration, timed with HIP
+    events (median of --sweep-reps launches; a 512 MiB write before each
+    quantizer launch evicts the MALL), against its roofline.  Inputs are drawn
+    on the device with the configurations' distributions (normal std, or
+    Student-t with outlier channels), seeded."""
+    import torch
+    import workloads
+    import microscaling_fp4_quantized_block_amd as mx
+    dev = torch.device("cuda", 0)
+    evict = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
+    gen = torch.Generator(device=dev)
+
+    def draw(cfg, name):
+        shape, kw = workloads.CONFIGS[cfg]["tensors"][name]
+        gen.manual_seed(1000 * cfg + list(workloads.CONFIGS[cfg]["tensors"]).index(name))
+        torch.manual_seed(1000 * cfg + list(workloads.CONFIGS[cfg]["tensors"]).index(name))
+        if kw["kind"] == "normal":
+            x = torch.randn(shape, generator=gen, device=dev) * kw["std"]
+        else:
+            nu = kw["nu"]
+            z = torch.randn(shape, generator=gen, device=dev)
+            chi2 = torch.distributions.Chi2(torch.tensor(nu, device=dev)).sample(shape)
+            x = z / torch.sqrt(chi2 / nu)
+            if kw.get("outlier_frac", 0.0) > 0:
+                ch = torch.randperm(shape[1], generator=gen, device=dev)[: int(round(kw["outlier_frac"] * shape[1]))]
+                x[:, ch] *= kw.get("outlier_scale", 50.0)
+        return x.to(torch.bfloat16)
+
+    def timed(fn, evict_first):
+        ts = []
+        for i in range(args.sweep_reps + 2):
+            if evict_first:
+                evict.fill_(float(i))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts)) * 1e-3
+
+    rows = []
+    wanted = [int(c) for c in args.sweep_configs.split(",")]
+    for cfg, (calls, gemms) in sweep_plan().items():
+        if cfg not in wanted:
+            continue
+        print(f"[sweep] config {cfg}", file=sys.stderr, flush=True)
+        spec = workloads.CONFIGS[cfg]
+        fmt, had = spec["fmt"], spec["hadamard"]
+        bs = 32 if fmt == "mx" else 16
+        tens, qs = {}, {}
+        for (name, rnd, axis) in dict.fromkeys(calls):
+            if name not in tens:
+                tens[name] = draw(cfg, name)
+            x = tens[name]
+            R, Cc = x.shape
+            rows_, k = (R, Cc) if axis == 1 else (Cc, R)
+            q = mx.empty_qtensor(fmt, rows_, k, had, dev)
+            wsb = mx.mxfp4_quantize_workspace_bytes(fmt, R, Cc, axis)
+            ws = torch.empty(max(wsb, 4), dtype=torch.uint8, device=dev)
+            f = lambda x=x, q=q, ws=ws, rnd=rnd, axis=axis: mx.mxfp4_quantize(x, fmt, rnd, had, axis, 7, out=q,
+                                                                               workspace=ws)
+            t = timed(f, True)
+            qs[(name, rnd, axis)] = q
+            nbytes = R * Cc * (2.0 + 0.5 + 1.0 / bs) + (4 if fmt == "nv" else 0)
+            gbps = nbytes / t / 1e9
+            rows.append((cfg, "quantize", f"{name} {rnd} axis{axis}" + (" H" if had else ""), f"{R}x{Cc}",
+                         t * 1e6, gbps, "GB/s", "hbm", gbps / PEAK_HBM_GBPS))
+        for (gname, ca, cb) in gemms:
+            qa, qb = qs[ca], qs[cb]
+            Mg, Ng, Kg = qa.rows, qb.rows, qa.k
+            C = torch.empty((Mg, Ng), dtype=torch.float32, device=dev)
+            wsb = mx.mxfp4_gemm_workspace_bytes(qa, qb)
+            ws = torch.empty(max(wsb, 4), dtype=torch.uint8, device=dev)
+            t = timed(lambda: mx.mxfp4_gemm(qa, qb, out=C, workspace=ws), False)
+            flops = 2.0 * Mg * Ng * Kg
+            nbytes = (Mg + Ng) * Kg * (0.5 + 1.0 / bs) + 4.0 * Mg * Ng
+            peak = PEAK_FP4_TFLOPS if fmt == "mx" else PEAK_FP16_TFLOPS
+            bound_t = max(flops / (peak * 1e12), nbytes / (PEAK_HBM_GBPS * 1e9))
+            bound = "mfma" if flops / (peak * 1e12) >= nbytes / (PEAK_HBM_GBPS * 1e9) else "hbm"
+            tf = flops / t / 1e12
+            rows.append((cfg, "gemm", gname, f"{Mg}x{Ng}x{Kg}", t * 1e6, tf, "TFLOP/s",
+                         bound + ("-fp16" if fmt == "nv" and bound == "mfma" else ""), bound_t / t))
+            del C, ws
+        del tens, qs
+        torch.cuda.empty_cache()
+    lines = ["| config | kernel | call | shape | time us | achieved | unit | bound | frac of roofline |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append("| %d | %s | %s | %s | %.1f | %.0f | %s | %s | %.3f |" % r)
+    text = "\n".join(lines) + "\n"
+    if args.sweep == "-":
+        print(text)
+    else:
+        with open(args.sweep, "w") as f:
+            f.write(text)
+        print(text)
+
+
 def main():
     args = parse()
+    if args.sweep:
+        sweep(args)
+        return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.traffic_file)
         return

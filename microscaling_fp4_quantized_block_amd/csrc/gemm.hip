@@ -645,8 +645,10 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs p) {
 // NVFP4
 // ---------------------------------------------------------------------------
 // 8 codes (4 bytes) of one block, exactly dequantized to fp16: hardware
-// E2M1 -> fp16 convert, then multiply by the block's E4M3 scale (as fp16;
-// the product has at most 6 significant bits and lies in [2^-10, 2688]).
+// E2M1 -> fp16 convert, then a packed fp16 multiply by the block's E4M3
+// scale (code x scale has at most 6 significant bits and lies in
+// [2^-10, 2688]).  (The convert's own f32 scale operand only takes a power
+// of two, so it cannot carry an E4M3 scale.)
 __device__ __forceinline__ v8h nv_dequant8(uint32_t codes4, v2h s2) {
   v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes4, 1.0f, 0);
   v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes4, 1.0f, 1);
@@ -656,9 +658,12 @@ __device__ __forceinline__ v8h nv_dequant8(uint32_t codes4, v2h s2) {
   return (v8h){h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
-__device__ __forceinline__ v2h e4m3_as_h2(uint32_t byte) {
-  const _Float16 s = (_Float16)e4m3_value(byte);
-  return (v2h){s, s};
+// E4M3 scale byte k of a word -> an fp16 pair (hardware FP8 convert, OCP
+// E4M3: 0x7F / 0xFF decode to NaN; every E4M3 value is exact in fp16).
+template <int K>
+__device__ __forceinline__ v2h e4m3_pair(int word) {
+  const _Float16 v = (_Float16)__builtin_amdgcn_cvt_f32_fp8(word, K);
+  return (v2h){v, v};
 }
 
 // A stage holds 8 NVFP4 blocks per row.  Lane group g owns blocks 4g..4g+3
@@ -690,11 +695,14 @@ __global__ void __launch_bounds__(256, 1) gemm_nv_kernel(GemmArgs p) {
     const uint8_t* B = st + A_BYTES;
     const uint8_t* SA = st + A_BYTES + B_BYTES;
     const uint8_t* SB = SA + SA_BYTES;
-    uint32_t sa[4], sb[4];
+    // the lane's four block scales per row, once per stage
+    v2h fa[4][4], fb[4][4];
 #pragma unroll
     for (int t = 0; t < 4; t++) {
-      sa[t] = *(const uint32_t*)(SA + (ra0 + 32 * t) * 8 + 4 * g);
-      sb[t] = *(const uint32_t*)(SB + (rb0 + 32 * t) * 8 + 4 * g);
+      const int sa = *(const int*)(SA + (ra0 + 32 * t) * 8 + 4 * g);
+      const int sb = *(const int*)(SB + (rb0 + 32 * t) * 8 + 4 * g);
+      fa[t][0] = e4m3_pair<0>(sa); fa[t][1] = e4m3_pair<1>(sa); fa[t][2] = e4m3_pair<2>(sa); fa[t][3] = e4m3_pair<3>(sa);
+      fb[t][0] = e4m3_pair<0>(sb); fb[t][1] = e4m3_pair<1>(sb); fb[t][2] = e4m3_pair<2>(sb); fb[t][3] = e4m3_pair<3>(sb);
     }
 #pragma unroll
     for (int half = 0; half < 2; half++) {        // 16-byte chunk: blocks 4g + 2 half, +1
@@ -711,8 +719,8 @@ __global__ void __launch_bounds__(256, 1) gemm_nv_kernel(GemmArgs p) {
         v8h af[4], bf[4];
 #pragma unroll
         for (int t = 0; t < 4; t++) {
-          af[t] = nv_dequant8((uint32_t)ca[t][u], e4m3_as_h2((sa[t] >> (8 * blk)) & 0xFFu));
-          bf[t] = nv_dequant8((uint32_t)cb[t][u], e4m3_as_h2((sb[t] >> (8 * blk)) & 0xFFu));
+          af[t] = nv_dequant8((uint32_t)ca[t][u], fa[t][blk]);
+          bf[t] = nv_dequant8((uint32_t)cb[t][u], fb[t][blk]);
         }
 #pragma unroll
         for (int i = 0; i < 4; i++)
