@@ -122,8 +122,9 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
   for (int r = 0; r < 10; r++) {
     uint64_t p0 = (uint64_t)0xD2511F53u * c0;
     uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    // three-input XOR in one v_bitop3 (truth table 0x96)
+    uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+    uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;
@@ -144,19 +145,13 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 // Round up iff rnd16 < t.  The sign bit is the input's.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t sr_code(float xs, uint32_t rnd16) {
-  uint32_t sign = (__float_as_uint(xs) >> 28) & 8u;
-  float a = __builtin_fminf(__builtin_fabsf(xs), 6.0f);
-  uint32_t ab = __float_as_uint(a);
-  uint32_t lo, t;
-  if (a >= 1.0f) {
-    lo = (ab >> 22) - 252u;
-    t = (ab >> 6) & 0xFFFFu;
-  } else {
-    uint32_t q = (uint32_t)(a * 131072.0f);
-    lo = q >> 16;
-    t = q & 0xFFFFu;
-  }
-  return sign | (lo + (rnd16 < t ? 1u : 0u));
+  const uint32_t sign = (__float_as_uint(xs) >> 28) & 8u;
+  const float a = __builtin_fminf(__builtin_fabsf(xs), 6.0f);
+  const uint32_t ab = __float_as_uint(a);
+  // fixed point: low code in bits 16 and up, t in bits 0..15 (for a >= 1,
+  // (ab - 252 * 2^22) >> 6 puts (ab >> 22) - 252 above bits [21:6] of ab)
+  const uint32_t x = (a >= 1.0f) ? ((ab - (252u << 22)) >> 6) : (uint32_t)(a * 131072.0f);
+  return sign | ((x >> 16) + (rnd16 < (x & 0xFFFFu) ? 1u : 0u));
 }
 
 }  // namespace mxfp4
