@@ -134,6 +134,29 @@ def test_gemm_balanced_half_tiles(oracle_mod):
     assert_gemm_within(Cc, Co, So, "balanced cols")
 
 
+def test_gemm_balanced_halves_partial_column(oracle_mod):
+    """Tile count = 1.5 x 256: 128 remainder tiles run as 256 x 128 halves at
+    the start and at the end of the launch.  M = 3072, N = 8128 (the last tile
+    column has 192 valid columns, so its second half is partly past N),
+    K = 256; rows of the remainder tiles checked across all columns."""
+    mx = need_gpu()
+    M, N, K = 3072, 8128, 256
+    A = workloads.small_t_bf16((M, K), 3.0, seed=38, outlier_frac=0.01)
+    B = workloads.small_normal_bf16((N, K), 0.02, seed=39)
+    qa, qb, oa, ob = _quant_pair(mx, oracle_mod, A, B, "mx")
+    say("gemm halves, partial column", M, N, K)
+    C = mx.mxfp4_gemm(qa, qb)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(1024, 3072, 7), np.arange(0, 1024, 61), [M - 1]])
+    Cr = C[torch.from_numpy(rows).cuda()].cpu().numpy()
+    Co, So = oracle_mod.gemm("mx", oa, ob, rows=rows)
+    assert_gemm_within(Cr, Co, So, "halves rows")
+    cols = np.array([0, 63, 64, 127, 128, 191, 192, 255, 4096, 4160, 4288, 4351, 7936, 8000, 8127])
+    Cc = C[:, torch.from_numpy(cols).cuda()].cpu().numpy()
+    Co, So = oracle_mod.gemm("mx", oa, ob, cols=cols)
+    assert_gemm_within(Cc, Co, So, "halves cols")
+
+
 def test_gemm_config2_sampled(oracle_mod):
     """NVFP4 8192 x 4096 x 4096, Student-t(3) activations with 1% x50 outlier channels."""
     mx = need_gpu()
