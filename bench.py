@@ -204,8 +204,10 @@ def sweep_plan():
 
 def sweep(args):
     """Every quantizer call and GEMM of every configuration, timed with HIP
-    events (median of --sweep-reps launches; a 512 MiB write before each
-    quantizer launch evicts the MALL), against its roofline.  Inputs are drawn
+    events around replays of a HIP graph holding 8 back-to-back calls (median
+    of --sweep-reps; for quantizer calls each call is preceded by a 512 MiB
+    write that evicts the MALL, whose own time is subtracted), against its
+    roofline.  Inputs are drawn
     on the device with the configurations' distributions (normal std, or
     Student-t with outlier channels), seeded."""
     import torch
@@ -231,19 +233,49 @@ def sweep(args):
                 x[:, ch] *= kw.get("outlier_scale", 50.0)
         return x.to(torch.bfloat16)
 
-    def timed(fn, evict_first):
+    inner = 8
+
+    def graph_of(fn):
+        """`inner` back-to-back calls of fn captured into one HIP graph
+        (replays cost no Python or ctypes time per call)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(inner):
+                fn()
+        torch.cuda.synchronize()
+        return g
+
+    def replay_time(g):
         ts = []
         for i in range(args.sweep_reps + 2):
-            if evict_first:
-                evict.fill_(float(i))
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            fn()
+            g.replay()
             e1.record()
             torch.cuda.synchronize()
             if i >= 2:
                 ts.append(e0.elapsed_time(e1))
-        return float(np.median(ts)) * 1e-3
+        return float(np.median(ts)) * 1e-3 / inner
+
+    g_evict = graph_of(lambda: evict.fill_(1.0))
+    t_evict = replay_time(g_evict)
+
+    def timed(fn, evict_first):
+        """GPU time of one call: graphs of back-to-back calls (each after a
+        512 MiB MALL eviction, whose own time is subtracted, for quantizer
+        calls)."""
+        if evict_first:
+            def both():
+                evict.fill_(1.0)
+                fn()
+            return max(replay_time(graph_of(both)) - t_evict, 1e-7)
+        return replay_time(graph_of(fn))
 
     rows = []
     wanted = [int(c) for c in args.sweep_configs.split(",")]

@@ -327,53 +327,54 @@ constexpr int MX_GROUPS = 3;                     // scale group buffers
 constexpr int MX_LDS = MX_GROUP_OFF + MX_GROUPS * 2 * MX_GROUP_OPND;   // 152 KB
 constexpr int MX_LOADS = 17;                     // buffer->LDS instructions per wave per stage
 
-// Per-wave operand blocks: TM = 4 row blocks of A (128 rows), TN = 4 or 2
-// column blocks of B (128 or 64 columns); TN = 2 serves the 256 x 128
-// half-tiles of the balanced schedule (below).
-template <int TN>
+// Per-wave operand blocks: TM row blocks of A (32 TM rows) and TN column
+// blocks of B (32 TN columns).  Wide tiles: TM = 4, TN = 4 (or 2 for the
+// 256 x 128 half tiles of the balanced schedule), waves 2 x 2.  Narrow tiles
+// (M <= 128): TM = 1, 2 or 4, TN = 2, all four waves side by side along N.
+template <int TM, int TN>
 struct MxFrag {
-  v4i a[4], b[TN];
+  v4i a[TM], b[TN];
 };
 
 // Fragments of 64-wide step s of a stage for this lane: rows ra0 + 32t of A
 // and rb0 + 32t of B, chunk 2s + (lane half).
-template <int TN>
-__device__ __forceinline__ void mx_read_frag(const uint8_t* st, int ra0, int rb0, int pos_byte, MxFrag<TN>& f) {
+template <int TM, int TN>
+__device__ __forceinline__ void mx_read_frag(const uint8_t* st, int ra0, int rb0, int pos_byte, MxFrag<TM, TN>& f) {
 #pragma unroll
-  for (int t = 0; t < 4; t++) f.a[t] = *(const v4i*)(st + (ra0 + 32 * t) * MX_ROW + pos_byte);
+  for (int t = 0; t < TM; t++) f.a[t] = *(const v4i*)(st + (ra0 + 32 * t) * MX_ROW + pos_byte);
 #pragma unroll
   for (int t = 0; t < TN; t++) f.b[t] = *(const v4i*)(st + MX_OPND + (rb0 + 32 * t) * MX_ROW + pos_byte);
 }
 
 // The 16 scale bytes of this lane's rows (A rows ra0 + 32t, then B rows
 // rb0 + 32t) in one group.
-template <int TN>
-__device__ __forceinline__ void mx_read_group(const uint8_t* grp, int ra0, int rb0, u32v4 (&d)[4 + TN]) {
+template <int TM, int TN>
+__device__ __forceinline__ void mx_read_group(const uint8_t* grp, int ra0, int rb0, u32v4 (&d)[TM + TN]) {
 #pragma unroll
-  for (int t = 0; t < 4; t++) d[t] = *(const u32v4*)(grp + (ra0 + 32 * t) * 16);
+  for (int t = 0; t < TM; t++) d[t] = *(const u32v4*)(grp + (ra0 + 32 * t) * 16);
 #pragma unroll
-  for (int t = 0; t < TN; t++) d[4 + t] = *(const u32v4*)(grp + MX_GROUP_OPND + (rb0 + 32 * t) * 16);
+  for (int t = 0; t < TN; t++) d[TM + t] = *(const u32v4*)(grp + MX_GROUP_OPND + (rb0 + 32 * t) * 16);
 }
 
 // Scale registers of one stage from its group's bytes: byte s = this lane's
 // block of step s.  HALF = stage parity inside the group; sel picks the lane
 // half's bytes; mask clears the bytes of steps past K (their products then
 // vanish).
-template <int HALF, int TN>
-__device__ __forceinline__ void mx_stage_scales(const u32v4 (&d)[4 + TN], uint32_t sel, uint32_t mask,
-                                                uint32_t (&sa)[4], uint32_t (&sb)[TN]) {
+template <int HALF, int TM, int TN>
+__device__ __forceinline__ void mx_stage_scales(const u32v4 (&d)[TM + TN], uint32_t sel, uint32_t mask,
+                                                uint32_t (&sa)[TM], uint32_t (&sb)[TN]) {
 #pragma unroll
-  for (int t = 0; t < 4; t++) sa[t] = __builtin_amdgcn_perm(d[t][2 * HALF + 1], d[t][2 * HALF], sel) & mask;
+  for (int t = 0; t < TM; t++) sa[t] = __builtin_amdgcn_perm(d[t][2 * HALF + 1], d[t][2 * HALF], sel) & mask;
 #pragma unroll
   for (int t = 0; t < TN; t++)
-    sb[t] = __builtin_amdgcn_perm(d[4 + t][2 * HALF + 1], d[4 + t][2 * HALF], sel) & mask;
+    sb[t] = __builtin_amdgcn_perm(d[TM + t][2 * HALF + 1], d[TM + t][2 * HALF], sel) & mask;
 }
 
-template <int S, int TN>
-__device__ __forceinline__ void mx_mfma(v16f (&acc)[4][TN], const MxFrag<TN>& f, const uint32_t (&sa)[4],
+template <int S, int TM, int TN>
+__device__ __forceinline__ void mx_mfma(v16f (&acc)[TM][TN], const MxFrag<TM, TN>& f, const uint32_t (&sa)[TM],
                                         const uint32_t (&sb)[TN]) {
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < TM; i++) {
     const v8i a = __builtin_shufflevector(f.a[i], f.a[i], 0, 1, 2, 3, -1, -1, -1, -1);
 #pragma unroll
     for (int j = 0; j < TN; j++) {
@@ -434,26 +435,26 @@ __device__ __forceinline__ MxOperand mx_make_operand(const uint8_t* codes, const
 }
 
 // Code loads L0 .. L1-1 of this wave for absolute stage kt into stage buffer
-// st: loads 0..7 are A's (64 rows per wave), loads 8.. B's (16 TN rows per
-// wave, 2 TN loads).
-template <int L0, int L1, int TN>
+// st: loads 0 .. LA-1 are A's (8 LA rows per wave), the next LB are B's
+// (8 LB rows per wave).
+template <int L0, int L1, int LA, int LB>
 __device__ __forceinline__ void mx_issue_codes(const MxOperand& oa, const MxOperand& ob, uint8_t* st, int kt,
                                                uint32_t krow16, int w) {
   const int soff = kt * MX_ROW;
 #pragma unroll
   for (int L = L0; L < L1; L++) {
-    const int j = L < 8 ? L : L - 8;
-    const int rpw = L < 8 ? 64 : 16 * TN;
-    const MxOperand& o = L < 8 ? oa : ob;
+    const int j = L < LA ? L : L - LA;
+    const int rpw = L < LA ? 8 * LA : 8 * LB;
+    const MxOperand& o = L < LA ? oa : ob;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(o.codes,
-                                             (lds_void*)(st + (L < 8 ? 0 : MX_OPND) + (rpw * w + 8 * j) * MX_ROW),
+                                             (lds_void*)(st + (L < LA ? 0 : MX_OPND) + (rpw * w + 8 * j) * MX_ROW),
                                              16, o.code_off[j & 1] + (uint32_t)(j >> 1) * krow16, soff, 0, 0);
   }
 }
 
-// One output tile (256 x 64 TN), contraction stages kt0 .. kt1-1 (kt0 even).
-// Iteration a (stage a), each step = 4 TN MFMAs with the next step's
-// fragment reads under them:
+// One output tile (32 TM WM x 32 TN (4 / WM)), contraction stages kt0 ..
+// kt1-1 (kt0 even).  Iteration a (stage a), each step = TM TN MFMAs with the
+// next step's fragment reads under them:
 //   step 0: + loads 6..11 of stage a + 1
 //   step 1: + loads 12.. of stage a + 1, the scale piece of iteration a, and
 //           the scale bytes of stage a + 1 (when a + 1 opens a group)
@@ -466,28 +467,31 @@ __device__ __forceinline__ void mx_issue_codes(const MxOperand& oa, const MxOper
 // MFMAs queued behind it.  The body has no branches: loads for stages past
 // the end land in buffers that are never read again, and reads past the end
 // are never consumed.
-template <int TN>
+template <int TM, int TN, int WM>
 __device__ __forceinline__ void mx_tile(const GemmArgs& p, uint8_t* smem, int64_t m0, int64_t n0, int kt0, int kt1,
                                         float* Cz) {
-  constexpr int NL = 8 + 2 * TN;   // code loads per wave per stage
+  constexpr int WN = 4 / WM;                     // waves along N
+  constexpr int LA = TM * WM, LB = TN * WN;      // code loads per wave per stage (8 rows each)
+  constexpr int NL = LA + LB;
+  constexpr int P1 = NL < 6 ? NL : 6, P2 = NL < 12 ? NL : 12;   // load parts: [0, P1) [P1, P2) [P2, NL)
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63, h = l >> 5;
-  const int wm = w >> 1, wn = w & 1;
-  const int ra0 = wm * 128 + (l & 31), rb0 = wn * (32 * TN) + (l & 31);
+  const int wm = w / WN, wn = w % WN;
+  const int ra0 = wm * (32 * TM) + (l & 31), rb0 = wn * (32 * TN) + (l & 31);
   auto pos = [&](int c) { return ((c ^ ((l >> 1) & 7)) << 4); };   // chunk c of a row r with r % 32 == l % 32
   const uint32_t sel = h ? 0x07050301u : 0x06040200u;
   const int ksteps = (int)(p.K / 64);                              // 64-wide steps in the whole contraction
 
-  v16f acc[4][TN];
+  v16f acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < TM; i++)
 #pragma unroll
     for (int j = 0; j < TN; j++) acc[i][j] = (v16f){};
 
   if (kt1 > kt0) {
     const uint32_t krow16 = (uint32_t)(16 * (p.K / 2));
-    const MxOperand oa = mx_make_operand<256>(p.a, p.as, p.M, m0, p.K, w, l);
-    const MxOperand ob = mx_make_operand<64 * TN>(p.b, p.bs, p.N, n0, p.K, w, l);
+    const MxOperand oa = mx_make_operand<32 * TM * WM>(p.a, p.as, p.M, m0, p.K, w, l);
+    const MxOperand ob = mx_make_operand<32 * TN * WN>(p.b, p.bs, p.N, n0, p.K, w, l);
     auto stage = [&](int a) { return smem + (a & 1) * MX_STAGE; };
     auto group = [&](int G) { return smem + MX_GROUP_OFF + (G % MX_GROUPS) * 2 * MX_GROUP_OPND; };
     // scale-byte mask of absolute stage a: bytes of the 64-wide steps below K
@@ -510,47 +514,47 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& p, uint8_t* smem, int64_
     issue_piece(G0, 0);
     issue_piece(G0, 1);
     issue_piece(G0 + 1, 0);
-    mx_issue_codes<0, NL, TN>(oa, ob, stage(kt0), kt0, krow16, w);
-    mx_issue_codes<0, 6, TN>(oa, ob, stage(kt0 + 1), kt0 + 1, krow16, w);
-    wait_cnt<6, 15>();
+    mx_issue_codes<0, NL, LA, LB>(oa, ob, stage(kt0), kt0, krow16, w);
+    mx_issue_codes<0, P1, LA, LB>(oa, ob, stage(kt0 + 1), kt0 + 1, krow16, w);
+    wait_cnt<P1, 15>();
     block_barrier();
 
-    MxFrag<TN> f0, f1;
-    uint32_t sa[4], sb[TN];
-    u32v4 gd[4 + TN];
-    mx_read_group<TN>(group(G0), ra0, rb0, gd);
-    mx_stage_scales<0, TN>(gd, sel, mask_of(kt0), sa, sb);
-    mx_read_frag<TN>(stage(kt0), ra0, rb0, pos(h), f0);
+    MxFrag<TM, TN> f0, f1;
+    uint32_t sa[TM], sb[TN];
+    u32v4 gd[TM + TN];
+    mx_read_group<TM, TN>(group(G0), ra0, rb0, gd);
+    mx_stage_scales<0, TM, TN>(gd, sel, mask_of(kt0), sa, sb);
+    mx_read_frag<TM, TN>(stage(kt0), ra0, rb0, pos(h), f0);
     // one iteration; H = a & 1 (kt0 is even, the loop takes stages in pairs)
     auto iteration = [&](auto Hc, int a) {
       constexpr int H = decltype(Hc)::value;
-      constexpr int NM = 4 * TN;              // MFMAs per step
-      constexpr int NF = 4 + TN;              // fragment reads per step
+      constexpr int NM = TM * TN;             // MFMAs per step
+      constexpr int NF = TM + TN;             // fragment reads per step
       const uint8_t* st = stage(H);
-      mx_issue_codes<6, (NL < 12 ? NL : 12), TN>(oa, ob, stage(H ^ 1), a + 1, krow16, w);
-      mx_read_frag<TN>(st, ra0, rb0, pos(2 + h), f1);
-      mx_mfma<0, TN>(acc, f0, sa, sb);
-      mx_sched<(NL < 12 ? NL : 12) - 6, NF, NM>();
-      mx_issue_codes<(NL < 12 ? NL : 12), NL, TN>(oa, ob, stage(H ^ 1), a + 1, krow16, w);
+      mx_issue_codes<P1, P2, LA, LB>(oa, ob, stage(H ^ 1), a + 1, krow16, w);
+      mx_read_frag<TM, TN>(st, ra0, rb0, pos(2 + h), f1);
+      mx_mfma<0, TM, TN>(acc, f0, sa, sb);
+      mx_sched<P2 - P1, NF, NM>();
+      mx_issue_codes<P2, NL, LA, LB>(oa, ob, stage(H ^ 1), a + 1, krow16, w);
       // iteration a's scale piece: group (a + 3) / 2's A piece when a is odd,
       // group a / 2 + 1's B piece when a is even.  Group G is then complete at
       // the barrier of iteration 2G - 2, before stage 2G's scale bytes are
       // read in iteration 2G - 1, and its buffer last held group G - 3.
       issue_piece(H ? (a + 3) >> 1 : (a >> 1) + 1, H ^ 1);
-      if (H) mx_read_group<TN>(group((a + 1) >> 1), ra0, rb0, gd);   // stage a + 1 opens the next group
-      mx_read_frag<TN>(st, ra0, rb0, pos(4 + h), f0);
-      mx_mfma<1, TN>(acc, f1, sa, sb);
-      mx_sched<NL - (NL < 12 ? NL : 12) + 1, NF + (H ? 4 + TN : 0), NM>();
-      mx_read_frag<TN>(st, ra0, rb0, pos(6 + h), f1);
-      mx_mfma<2, TN>(acc, f0, sa, sb);
-      uint32_t sa_n[4], sb_n[TN];
-      mx_stage_scales<H ^ 1, TN>(gd, sel, mask_of(a + 1), sa_n, sb_n);
+      if (H) mx_read_group<TM, TN>(group((a + 1) >> 1), ra0, rb0, gd);   // stage a + 1 opens the next group
+      mx_read_frag<TM, TN>(st, ra0, rb0, pos(4 + h), f0);
+      mx_mfma<1, TM, TN>(acc, f1, sa, sb);
+      mx_sched<NL - P2 + 1, NF + (H ? TM + TN : 0), NM>();
+      mx_read_frag<TM, TN>(st, ra0, rb0, pos(6 + h), f1);
+      mx_mfma<2, TM, TN>(acc, f0, sa, sb);
+      uint32_t sa_n[TM], sb_n[TN];
+      mx_stage_scales<H ^ 1, TM, TN>(gd, sel, mask_of(a + 1), sa_n, sb_n);
       mx_sched<0, NF, NM>();
       wait_cnt<0, 0>();
       block_barrier();
-      mx_read_frag<TN>(stage(H ^ 1), ra0, rb0, pos(h), f0);
-      mx_issue_codes<0, 6, TN>(oa, ob, stage(H), a + 2, krow16, w);
-      mx_mfma<3, TN>(acc, f1, sa, sb);
+      mx_read_frag<TM, TN>(stage(H ^ 1), ra0, rb0, pos(h), f0);
+      mx_issue_codes<0, P1, LA, LB>(oa, ob, stage(H), a + 2, krow16, w);
+      mx_mfma<3, TM, TN>(acc, f1, sa, sb);
       // the fragment reads first, then the loads, over the MFMAs
 #pragma unroll
       for (int q = 0; q < NF; q++) {
@@ -558,14 +562,14 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& p, uint8_t* smem, int64_
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
       }
 #pragma unroll
-      for (int q = 0; q < 6; q++) {
+      for (int q = 0; q < P1; q++) {
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one buffer->LDS load
         if (NF + q < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
       }
-      if (NM > NF + 6) __builtin_amdgcn_sched_group_barrier(0x008, NM - NF - 6, 0);
+      if (NM > NF + P1) __builtin_amdgcn_sched_group_barrier(0x008, NM - NF - P1, 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int t = 0; t < 4; t++) sa[t] = sa_n[t];
+      for (int t = 0; t < TM; t++) sa[t] = sa_n[t];
 #pragma unroll
       for (int t = 0; t < TN; t++) sb[t] = sb_n[t];
     };
@@ -577,7 +581,7 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& p, uint8_t* smem, int64_
     }
     wait_cnt<0, 0>();   // nothing may still write LDS when the workgroup exits
   }
-  store_tile_f32x4<4, TN>(p, Cz, m0 + wm * 128, n0 + wn * (32 * TN), acc);
+  store_tile_f32x4<TM, TN>(p, Cz, m0 + wm * (32 * TM), n0 + wn * (32 * TN), acc);
 }
 
 // Work items.  Workgroups are dispatched in id order to whichever compute
@@ -620,13 +624,29 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs p) {
   const int F = T - R;
   if (b >= R && b < R + F) {
     tm = mx_walk(p, xcd_gather(b - R, F), tn);
-    mx_tile<4>(p, smem, (int64_t)tm * BM, (int64_t)tn * BN, kt0, kt1, Cz);
+    mx_tile<4, 4, 2>(p, smem, (int64_t)tm * BM, (int64_t)tn * BN, kt0, kt1, Cz);
   } else {
     const int second = b >= R + F;
     const int i = second ? b - R - F : b;
     tm = mx_walk(p, F + xcd_gather(i, R), tn);
-    mx_tile<2>(p, smem, (int64_t)tm * BM, (int64_t)tn * BN + 128 * second, kt0, kt1, Cz);
+    mx_tile<4, 2, 2>(p, smem, (int64_t)tm * BM, (int64_t)tn * BN + 128 * second, kt0, kt1, Cz);
   }
+}
+
+// Narrow MXFP4 GEMM (M <= 32 TM <= 128: decode-shaped activations against
+// weights): 32 TM x 256 tiles, the four waves side by side along N, so no MFMA
+// work is spent on rows past M; these shapes stream the weights from HBM and
+// are split along K for enough workgroups.  Grid: (N tiles, splits).
+template <int TM>
+__global__ void __launch_bounds__(256, 1) gemm_mx_narrow_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[MX_LDS];
+  const int z = blockIdx.y;
+  const int pairs = (p.k_tiles + 1) >> 1;
+  const int kt0 = 2 * (int)((int64_t)pairs * z / p.splits);
+  int kt1 = 2 * (int)((int64_t)pairs * (z + 1) / p.splits);
+  if (kt1 > p.k_tiles) kt1 = p.k_tiles;
+  float* Cz = p.C + (int64_t)z * p.split_stride;
+  mx_tile<TM, 2, 1>(p, smem, 0, (int64_t)blockIdx.x * 256, kt0, kt1, Cz);
 }
 
 // ---------------------------------------------------------------------------
@@ -747,6 +767,18 @@ GemmPlan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
   const bool mx = fmt == FMT_MX;
   GemmPlan pl;
   pl.k_tiles = (K + (mx ? MX_BK : BK) - 1) / (mx ? MX_BK : BK);
+  pl.narrow_tm = 0;
+  if (mx && M <= 128) {
+    // narrow tiles (32 TM x 256), split along K (in stage pairs) until about
+    // two workgroups per compute unit
+    pl.narrow_tm = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
+    const int64_t tiles = (N + 255) / 256, pairs = (pl.k_tiles + 1) / 2;
+    int64_t s = 512 / tiles;
+    if (s > pairs) s = pairs;
+    if (s > 32) s = 32;
+    pl.splits = s < 1 ? 1 : (int)s;
+    return pl;
+  }
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   // the MXFP4 kernel splits in pairs of stages (one scale group)
   const int64_t units = mx ? (pl.k_tiles + 1) / 2 : pl.k_tiles;
@@ -795,13 +827,21 @@ static hipError_t launch_gemm_common(bool nv, GemmArgs p, float* C, int64_t ldc,
   }
   p.rem = 0;
   const int64_t tiles = (int64_t)p.ntm * p.ntn;
-  if (!nv && plan.splits == 1) {
+  if (!nv && plan.splits == 1 && !plan.narrow_tm) {
     const int64_t cus = compute_units();
     if (tiles > cus && tiles % cus != 0) p.rem = (int)(tiles % cus);
   }
   dim3 grid((unsigned)(tiles + p.rem), (unsigned)plan.splits);
-  if (nv) hipLaunchKernelGGL(gemm_nv_kernel, grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(gemm_mx_kernel, grid, dim3(256), 0, stream, p);
+  if (nv) {
+    hipLaunchKernelGGL(gemm_nv_kernel, grid, dim3(256), 0, stream, p);
+  } else if (plan.narrow_tm) {
+    dim3 ngrid((unsigned)((p.N + 255) / 256), (unsigned)plan.splits);
+    if (plan.narrow_tm == 1) hipLaunchKernelGGL(gemm_mx_narrow_kernel<1>, ngrid, dim3(256), 0, stream, p);
+    else if (plan.narrow_tm == 2) hipLaunchKernelGGL(gemm_mx_narrow_kernel<2>, ngrid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL(gemm_mx_narrow_kernel<4>, ngrid, dim3(256), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(gemm_mx_kernel, grid, dim3(256), 0, stream, p);
+  }
   if (plan.splits > 1) {
     int64_t work = p.M * p.N;
     int64_t g = (work + 255) / 256;

@@ -28,6 +28,7 @@ hipError_t launch_dequantize(int fmt, int64_t rows, int64_t K, const uint8_t* co
 struct GemmPlan {
   int splits;
   int64_t k_tiles;     // contraction tiles of the kernel's K step
+  int narrow_tm;       // MXFP4 with M <= 128: rows per narrow tile / 32 (1, 2 or 4); 0 = wide tiles
 };
 GemmPlan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K);
 
