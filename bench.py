@@ -320,6 +320,31 @@ def sweep(args):
             rows.append((cfg, "gemm", gname, f"{Mg}x{Ng}x{Kg}", t * 1e6, tf, "TFLOP/s",
                          bound + ("-fp16" if fmt == "nv" and bound == "mfma" else ""), bound_t / t))
             del C, ws
+        if cfg == 3:
+            # decode with the activation quantization fused into the GEMM,
+            # against the two launches it replaces (quantize, then GEMM)
+            for gname, xname, wname in (("decode up", "x_dec_up", "W_up"), ("decode down", "x_dec_down", "W_down")):
+                x, qw, qx = tens[xname], qs[(wname, "rtn", 1)], qs[(xname, "rtn", 1)]
+                Mg, Kg = x.shape
+                Ng = qw.rows
+                C = torch.empty((Mg, Ng), dtype=torch.float32, device=dev)
+                wsb = mx.mxfp4_quantize_gemm_workspace_bytes(Mg, Kg, had, qw)
+                ws = torch.empty(max(wsb, 4), dtype=torch.uint8, device=dev)
+                gws = torch.empty(max(mx.mxfp4_gemm_workspace_bytes(qx, qw), 4), dtype=torch.uint8, device=dev)
+                flops = 2.0 * Mg * Ng * Kg
+                nbytes = Mg * Kg * 2.0 + Ng * Kg * (0.5 + 1.0 / bs) + 4.0 * Mg * Ng
+                bound_t = max(flops / (PEAK_FP4_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBPS * 1e9))
+                bound = "mfma" if flops / (PEAK_FP4_TFLOPS * 1e12) >= nbytes / (PEAK_HBM_GBPS * 1e9) else "hbm"
+                t_f = timed(lambda: mx.mxfp4_quantize_gemm(x, qw, had, out=C, workspace=ws), False)
+
+                def two():
+                    mx.mxfp4_quantize(x, fmt, "rtn", had, 1, 7, out=qx)
+                    mx.mxfp4_gemm(qx, qw, out=C, workspace=gws)
+                t_2 = timed(two, False)
+                for label, t in (("fused", t_f), ("two launches", t_2)):
+                    rows.append((cfg, "quantize+gemm", f"{gname} ({label})", f"{Mg}x{Ng}x{Kg}", t * 1e6,
+                                 flops / t / 1e12, "TFLOP/s", bound, bound_t / t))
+                del C, ws, gws
         del tens, qs
         torch.cuda.empty_cache()
     lines = ["| config | kernel | call | shape | time us | achieved | unit | bound | frac of roofline |",

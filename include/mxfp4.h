@@ -141,6 +141,40 @@ mxfp4_status mxfp4_gemm_workspace_bytes(const mxfp4_tensor *A, const mxfp4_tenso
 mxfp4_status mxfp4_gemm(const mxfp4_tensor *A, const mxfp4_tensor *B, float *C, int64_t ldc,
                         void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Workspace needed by mxfp4_quantize_gemm for activations [M, K] against B:
+ * the split-K partial sums when the quantization is fused into the GEMM,
+ * else room for the quantized activations (codes, then scales, each padded
+ * to 16 bytes) followed by the GEMM's own workspace.  Argument errors as for
+ * mxfp4_quantize_gemm. */
+mxfp4_status mxfp4_quantize_gemm_workspace_bytes(int64_t M, int64_t K, int hadamard, const mxfp4_tensor *B,
+                                                 size_t *bytes);
+
+/* Forward pass of an MXFP4 linear layer with online activation quantization
+ * ("Bridging the Gap Between Promise and Performance for Microscaling FP4
+ * Quantization", abstract: block-wise Hadamard rotations fused into the
+ * weights offline and computed on the fly for the activations, in front of
+ * FP4 GEMM kernels):
+ *   C[M, N] = Q(x) * B^T,  Q = mxfp4_quantize(x, MXFP4, RTN, hadamard, axis 1),
+ * bit for bit the result of mxfp4_quantize followed by mxfp4_gemm on the same
+ * input.  For decode-shaped activations (M <= 32) each GEMM workgroup
+ * quantizes the activation rows of its own contraction range in LDS, so the
+ * activations never go through memory as codes and the call is one GEMM
+ * launch (plus the split-K reduction); otherwise (more rows, whose repeated
+ * quantization in every column-tile workgroup would cost more than one
+ * quantizer pass, and the rare plans whose contraction split is too long for
+ * LDS) x is quantized into the workspace first.
+ * x: device, bf16 bit patterns [M, K], row-major, leading dimension ldx >= K.
+ * B: the pre-quantized weights [N, K] (MXFP4, B->k == K and B->hadamard ==
+ *    hadamard, else FORMAT_MISMATCH); B->codes 16-byte and B->scales 4-byte
+ *    aligned (INVALID_ARG otherwise).  K must be a multiple of 128
+ *    (UNSUPPORTED_SHAPE).
+ * C: device, FP32, row-major, ldc >= N.
+ * workspace: device, 16-byte aligned, at least
+ *    mxfp4_quantize_gemm_workspace_bytes (NULL if that is 0). */
+mxfp4_status mxfp4_quantize_gemm(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int hadamard,
+                                 const mxfp4_tensor *B, float *C, int64_t ldc,
+                                 void *workspace, size_t ws_bytes, hipStream_t stream);
+
 /* A static, human-readable description of a status code. */
 const char *mxfp4_status_string(int status);
 

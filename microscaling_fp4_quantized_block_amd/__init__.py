@@ -60,6 +60,10 @@ def _load_library() -> ctypes.CDLL:
     lib.mxfp4_gemm_workspace_bytes.argtypes = [P(MxTensorStruct), P(MxTensorStruct), P(sz)]
     lib.mxfp4_gemm.restype = i32
     lib.mxfp4_gemm.argtypes = [P(MxTensorStruct), P(MxTensorStruct), vp, i64, vp, sz, vp]
+    lib.mxfp4_quantize_gemm_workspace_bytes.restype = i32
+    lib.mxfp4_quantize_gemm_workspace_bytes.argtypes = [i64, i64, i32, P(MxTensorStruct), P(sz)]
+    lib.mxfp4_quantize_gemm.restype = i32
+    lib.mxfp4_quantize_gemm.argtypes = [vp, i64, i64, i64, i32, P(MxTensorStruct), vp, i64, vp, sz, vp]
     return lib
 
 
@@ -183,10 +187,41 @@ def mxfp4_gemm(qa: QTensor, qb: QTensor, out: Optional[torch.Tensor] = None,
     return out
 
 
+def mxfp4_quantize_gemm_workspace_bytes(M: int, K: int, hadamard: bool, qb: QTensor) -> int:
+    b = ctypes.c_size_t()
+    sb = qb.as_struct()
+    _check(lib.mxfp4_quantize_gemm_workspace_bytes(M, K, int(bool(hadamard)), ctypes.byref(sb), ctypes.byref(b)))
+    return b.value
+
+
+def mxfp4_quantize_gemm(x: torch.Tensor, qb: QTensor, hadamard: bool = False, out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C[M, N] = Q(x) B^T with x [M, K] bf16 quantized on the fly (MXFP4,
+    round-to-nearest, optional block Hadamard), the same bits as
+    mxfp4_gemm(mxfp4_quantize(x, "mx", "rtn", hadamard), qb)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
+        raise ValueError("x must be a 2-D bfloat16 CUDA/HIP tensor")
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit stride along its last dimension")
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, qb.rows), dtype=torch.float32, device=x.device)
+    ws_bytes = mxfp4_quantize_gemm_workspace_bytes(M, K, hadamard, qb)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    sb = qb.as_struct()
+    _check(lib.mxfp4_quantize_gemm(_ptr(x), M, K, x.stride(0), int(bool(hadamard)), ctypes.byref(sb), _ptr(out),
+                                   out.stride(0), _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                   _stream(x.device)))
+    return out
+
+
 quantize = mxfp4_quantize
 dequantize = mxfp4_dequantize
 gemm = mxfp4_gemm
+quantize_gemm = mxfp4_quantize_gemm
 
 __all__ = ["QTensor", "MxFp4Error", "mxfp4_tensor_bytes", "mxfp4_quantize_workspace_bytes", "mxfp4_quantize",
            "mxfp4_dequantize", "mxfp4_gemm_workspace_bytes", "mxfp4_gemm", "mxfp4_status_string",
-           "quantize", "dequantize", "gemm", "empty_qtensor", "lib", "LIB_PATH"]
+           "mxfp4_quantize_gemm_workspace_bytes", "mxfp4_quantize_gemm",
+           "quantize", "dequantize", "gemm", "quantize_gemm", "empty_qtensor", "lib", "LIB_PATH"]

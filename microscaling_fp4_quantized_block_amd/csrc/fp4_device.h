@@ -81,6 +81,60 @@ __device__ __forceinline__ float e8m0_value(uint32_t byte) {
 }
 
 // ---------------------------------------------------------------------------
+// Block Hadamard rotation ("Bridging the Gap Between Promise and Performance
+// for Microscaling FP4 Quantization", abstract: block-wise Hadamard
+// transforms).  Butterfly h: (x[i], x[i+h]) -> (x[i] + x[i+h], x[i] - x[i+h])
+// for i & h == 0, strides 1, 2, 4, 8, 16 in that order, then multiply by
+// RN_f32(1/sqrt(32)) = 0x3E3504F3.  Every evaluation of this butterfly tree in
+// IEEE binary32 gives the same bits, whatever the data layout.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kHadamardScaleBits = 0x3E3504F3u;
+
+// Full 32-point rotation of a block held in one lane (32 registers).
+__device__ __forceinline__ void fwht32_inlane(float v[32]) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; i++) {
+      if (i & h) continue;
+      float a = v[i], b = v[i + h];
+      v[i] = a + b;
+      v[i + h] = a - b;
+    }
+  }
+  const float c = __uint_as_float(kHadamardScaleBits);
+#pragma unroll
+  for (int i = 0; i < 32; i++) v[i] = v[i] * c;
+}
+
+// MXFP4 round-to-nearest of one 32-element block held in one lane: the E8M0
+// byte from the block absmax (an integer max over |binary32 bits|), then the
+// hardware FP4 conversion of y / 2^e (nearest-even, saturating); element j
+// lands in bits 4 (j % 8) .. +3 of codes[j / 8].  A block holding a NaN or an
+// infinity gets byte 0xFF and all-zero codes.
+__device__ __forceinline__ uint32_t mx_rtn_block32(const float y[32], uint32_t codes[4]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 32; j++) m = max(m, __float_as_uint(y[j]) & 0x7FFFFFFFu);
+  if (m >= 0x7F800000u) {
+    codes[0] = codes[1] = codes[2] = codes[3] = 0u;
+    return 0xFFu;
+  }
+  const uint32_t byte = mx_scale_byte_from_f32bits(m);
+  const float sc = e8m0_as_cvt_scale(byte);
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    uint32_t packed = 0;
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[8 * q + 0], y[8 * q + 1], sc, 0);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[8 * q + 2], y[8 * q + 3], sc, 1);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[8 * q + 4], y[8 * q + 5], sc, 2);
+    packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[8 * q + 6], y[8 * q + 7], sc, 3);
+    codes[q] = packed;
+  }
+  return byte;
+}
+
+// ---------------------------------------------------------------------------
 // E4M3 (bias 7, no infinities, 0x7F NaN).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float e4m3_value(uint32_t byte) {

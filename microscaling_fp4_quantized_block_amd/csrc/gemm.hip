@@ -80,6 +80,10 @@ struct GemmArgs {
   int splits;
   int ntm, ntn;
   int rem;                  // MXFP4: remainder tiles run as two 256 x 128 halves (see the kernel)
+  // fused activation quantization (MXFP4 narrow tiles): A comes in as bf16
+  const uint16_t* x;
+  int64_t ldx;
+  int x_vec;                // x 16-byte aligned and ldx a multiple of 8: 16-byte loads
 };
 
 // Tile order: consecutive workgroup ids go to consecutive XCDs, so gather
@@ -336,24 +340,27 @@ struct MxFrag {
   v4i a[TM], b[TN];
 };
 
-// Fragments of 64-wide step s of a stage for this lane: rows ra0 + 32t of A
-// and rb0 + 32t of B, chunk 2s + (lane half).
+// Fragments of 64-wide step s of a stage for this lane: rows ra0 + 32t of the
+// stage's A codes at sa and rb0 + 32t of its B codes at sb, chunk 2s + (lane
+// half).
 template <int TM, int TN>
-__device__ __forceinline__ void mx_read_frag(const uint8_t* st, int ra0, int rb0, int pos_byte, MxFrag<TM, TN>& f) {
+__device__ __forceinline__ void mx_read_frag(const uint8_t* sa, const uint8_t* sb, int ra0, int rb0, int pos_byte,
+                                             MxFrag<TM, TN>& f) {
 #pragma unroll
-  for (int t = 0; t < TM; t++) f.a[t] = *(const v4i*)(st + (ra0 + 32 * t) * MX_ROW + pos_byte);
+  for (int t = 0; t < TM; t++) f.a[t] = *(const v4i*)(sa + (ra0 + 32 * t) * MX_ROW + pos_byte);
 #pragma unroll
-  for (int t = 0; t < TN; t++) f.b[t] = *(const v4i*)(st + MX_OPND + (rb0 + 32 * t) * MX_ROW + pos_byte);
+  for (int t = 0; t < TN; t++) f.b[t] = *(const v4i*)(sb + (rb0 + 32 * t) * MX_ROW + pos_byte);
 }
 
-// The 16 scale bytes of this lane's rows (A rows ra0 + 32t, then B rows
-// rb0 + 32t) in one group.
+// The 16 scale bytes of this lane's rows in one group (A rows ra0 + 32t of
+// the A group at ga, then B rows rb0 + 32t of the B group at gb).
 template <int TM, int TN>
-__device__ __forceinline__ void mx_read_group(const uint8_t* grp, int ra0, int rb0, u32v4 (&d)[TM + TN]) {
+__device__ __forceinline__ void mx_read_group(const uint8_t* ga, const uint8_t* gb, int ra0, int rb0,
+                                              u32v4 (&d)[TM + TN]) {
 #pragma unroll
-  for (int t = 0; t < TM; t++) d[t] = *(const u32v4*)(grp + (ra0 + 32 * t) * 16);
+  for (int t = 0; t < TM; t++) d[t] = *(const u32v4*)(ga + (ra0 + 32 * t) * 16);
 #pragma unroll
-  for (int t = 0; t < TN; t++) d[TM + t] = *(const u32v4*)(grp + MX_GROUP_OPND + (rb0 + 32 * t) * 16);
+  for (int t = 0; t < TN; t++) d[TM + t] = *(const u32v4*)(gb + (rb0 + 32 * t) * 16);
 }
 
 // Scale registers of one stage from its group's bytes: byte s = this lane's
@@ -452,6 +459,63 @@ __device__ __forceinline__ void mx_issue_codes(const MxOperand& oa, const MxOper
   }
 }
 
+// Fused activation quantization for the narrow tiles: stages kt0 ..
+// kt0 + nsp - 1 of rows 0 .. 32 TM - 1 of the bf16 input p.x [M, K] (row
+// stride p.ldx), quantized to MXFP4 with round-to-nearest per 32-block (block
+// Hadamard first when HAD): the same codes and scale bytes as the quantizer
+// writes for this input.  Block i of the range is chunk c = i % 8 of row
+// r = (i / 8) % Mr in stage st = i / (8 Mr), Mr = min(M, 32 TM) (the rows past
+// M are written as zeros separately, so that every wave gets its share of
+// the real blocks).  Stage st's codes go to
+// aslot(st) in the stage layout (row r at r * 128, chunk c at
+// c ^ ((r >> 1) & 7)), its scale bytes to byte 8 (st % 2) + c of row r's 16
+// in ascl(st / 2).  Rows past M and blocks past K come out as zero codes with
+// scale byte 0, which is what the code loads of the unfused path read there.
+struct MxXBlock {
+  uint32_t w[16];      // 32 bf16 values, element 2j in the low half of w[j]
+  int r, c, st;
+  bool ok;             // inside M and K (else the block is zero)
+};
+
+__device__ __forceinline__ void mx_fill_load(const GemmArgs& p, int kt0, int i, int Mr, MxXBlock& b) {
+  b.c = i & 7;
+  b.st = (i >> 3) / Mr;
+  b.r = (i >> 3) - b.st * Mr;
+  const int64_t k = (int64_t)(kt0 + b.st) * MX_BK + 32 * b.c;
+  b.ok = k < p.K;
+  if (!b.ok) return;
+  const uint16_t* src = p.x + (int64_t)b.r * p.ldx + k;
+  if (p.x_vec) {
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const u32v4 v = *(const u32v4*)(src + 8 * q);
+#pragma unroll
+      for (int j = 0; j < 4; j++) b.w[4 * q + j] = v[j];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; j++) b.w[j] = (uint32_t)src[2 * j] | ((uint32_t)src[2 * j + 1] << 16);
+  }
+}
+
+template <bool HAD, typename AS, typename AG>
+__device__ __forceinline__ void mx_fill_store(const MxXBlock& b, AS&& aslot, AG&& ascl) {
+  uint32_t cw[4] = {0u, 0u, 0u, 0u};
+  uint32_t byte = 0u;
+  if (b.ok) {
+    float y[32];
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      y[2 * j] = __uint_as_float(b.w[j] << 16);
+      y[2 * j + 1] = __uint_as_float(b.w[j] & 0xFFFF0000u);
+    }
+    if (HAD) fwht32_inlane(y);
+    byte = mx_rtn_block32(y, cw);
+  }
+  *(u32v4*)(aslot(b.st) + b.r * MX_ROW + ((b.c ^ ((b.r >> 1) & 7)) << 4)) = (u32v4){cw[0], cw[1], cw[2], cw[3]};
+  ascl(b.st >> 1)[b.r * 16 + 8 * (b.st & 1) + b.c] = (uint8_t)byte;
+}
+
 // One output tile (32 TM WM x 32 TN (4 / WM)), contraction stages kt0 ..
 // kt1-1 (kt0 even).  Iteration a (stage a), each step = TM TN MFMAs with the
 // next step's fragment reads under them:
@@ -467,12 +531,21 @@ __device__ __forceinline__ void mx_issue_codes(const MxOperand& oa, const MxOper
 // MFMAs queued behind it.  The body has no branches: loads for stages past
 // the end land in buffers that are never read again, and reads past the end
 // are never consumed.
-template <int TM, int TN, int WM>
+//
+// FA (fused activation quantization, narrow tiles only): A is not loaded as
+// codes but quantized here from the bf16 input p.x (MXFP4 round-to-nearest,
+// with the block Hadamard when HAD) for the whole contraction range kt0 ..
+// kt1 before the main loop, into A slots that take the place of the (unused)
+// A halves of the two stage buffers, with its scale bytes in the A halves of
+// the scale-group buffers.  The codes and scale bytes are those the
+// quantizer writes for the same input, so the products are the same.
+template <int TM, int TN, int WM, bool FA = false, bool HAD = false>
 __device__ __forceinline__ void mx_tile(const GemmArgs& p, uint8_t* smem, int64_t m0, int64_t n0, int kt0, int kt1,
                                         float* Cz) {
   constexpr int WN = 4 / WM;                     // waves along N
-  constexpr int LA = TM * WM, LB = TN * WN;      // code loads per wave per stage (8 rows each)
-  constexpr int NL = LA + LB;
+  constexpr int LA = TM * WM, LB = TN * WN;      // code row blocks per wave per stage (8 rows each)
+  constexpr int LAL = FA ? 0 : LA;               // A code loads per wave per stage
+  constexpr int NL = LAL + LB;
   constexpr int P1 = NL < 6 ? NL : 6, P2 = NL < 12 ? NL : 12;   // load parts: [0, P1) [P1, P2) [P2, NL)
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63, h = l >> 5;
@@ -490,10 +563,33 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& p, uint8_t* smem, int64_
 
   if (kt1 > kt0) {
     const uint32_t krow16 = (uint32_t)(16 * (p.K / 2));
-    const MxOperand oa = mx_make_operand<32 * TM * WM>(p.a, p.as, p.M, m0, p.K, w, l);
+    // (FA: no A codes are loaded; the descriptor only lends its scale row
+    // offset, which is the same for both operands)
+    const MxOperand oa = mx_make_operand<32 * TM * WM>(FA ? p.b : p.a, FA ? p.bs : p.as, FA ? p.N : p.M, m0, p.K,
+                                                       w, l);
     const MxOperand ob = mx_make_operand<32 * TN * WN>(p.b, p.bs, p.N, n0, p.K, w, l);
     auto stage = [&](int a) { return smem + (a & 1) * MX_STAGE; };
     auto group = [&](int G) { return smem + MX_GROUP_OFF + (G % MX_GROUPS) * 2 * MX_GROUP_OPND; };
+    // FA: A codes of stage kt0 + i in slot i (32 TM rows x 128 bytes, the
+    // stage layout), slots filling the A half of stage buffer 0, then of
+    // stage buffer 1; A scales of group G0 + j in the A halves of the group
+    // buffers, 32 TM rows x 16 bytes each
+    constexpr int A_SLOT = 32 * TM * MX_ROW, A_GSLOT = 32 * TM * 16, A_GPER = MX_GROUP_OPND / A_GSLOT;
+    auto aslot = [&](int i) -> uint8_t* {
+      const int off = i * A_SLOT;
+      return off < MX_OPND ? smem + off : smem + MX_STAGE + (off - MX_OPND);
+    };
+    auto ascl = [&](int j) -> uint8_t* {
+      return smem + MX_GROUP_OFF + (j / A_GPER) * 2 * MX_GROUP_OPND + (j % A_GPER) * A_GSLOT;
+    };
+    auto abuf = [&](int a) -> const uint8_t* {
+      if constexpr (FA) return aslot(a - kt0);
+      else return stage(a);
+    };
+    auto agrp = [&](int G) -> const uint8_t* {
+      if constexpr (FA) return ascl(G - (kt0 >> 1));
+      else return group(G);
+    };
     // scale-byte mask of absolute stage a: bytes of the 64-wide steps below K
     auto mask_of = [&](int a) -> uint32_t {
       const int v = min(max(ksteps - 4 * a, 0), 4);
@@ -511,49 +607,87 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& p, uint8_t* smem, int64_
     // of iteration kt0 - 1), stage kt0, and the first part of stage kt0 + 1
     // (iteration kt0 issues the rest)
     const int G0 = kt0 >> 1;
-    issue_piece(G0, 0);
+    // FA: quantize A for stages kt0 .. kt0 + nsp - 1 (nsp = the stage count
+    // rounded up to the loop's pairs; stages past K come out as zero codes);
+    // the inputs of this thread's first two blocks are loaded ahead of the B
+    // loads (vmcnt counts in order: loads issued after the B loads would wait
+    // for them)
+    const int nsp = (kt1 - kt0 + 1) & ~1;
+    const int Mr = p.M < 32 * TM ? (int)p.M : 32 * TM;   // rows of A that exist
+    const int nblk = nsp * Mr * 8;
+    constexpr int XPRE = 4;                      // blocks per thread loaded ahead
+    MxXBlock xb[XPRE];
+    if constexpr (FA) {
+#pragma unroll
+      for (int q = 0; q < XPRE; q++) {
+        xb[q].ok = false;
+        if ((int)threadIdx.x + 256 * q < nblk) mx_fill_load(p, kt0, threadIdx.x + 256 * q, Mr, xb[q]);
+      }
+    }
+    if (!FA) issue_piece(G0, 0);
     issue_piece(G0, 1);
-    issue_piece(G0 + 1, 0);
-    mx_issue_codes<0, NL, LA, LB>(oa, ob, stage(kt0), kt0, krow16, w);
-    mx_issue_codes<0, P1, LA, LB>(oa, ob, stage(kt0 + 1), kt0 + 1, krow16, w);
-    wait_cnt<P1, 15>();
+    if (!FA) issue_piece(G0 + 1, 0);
+    mx_issue_codes<0, NL, LAL, LB>(oa, ob, stage(kt0), kt0, krow16, w);
+    mx_issue_codes<0, P1, LAL, LB>(oa, ob, stage(kt0 + 1), kt0 + 1, krow16, w);
+    if constexpr (FA) {
+#pragma unroll
+      for (int q = 0; q < XPRE; q++)
+        if ((int)threadIdx.x + 256 * q < nblk) mx_fill_store<HAD>(xb[q], aslot, ascl);
+      for (int i = threadIdx.x + 256 * XPRE; i < nblk; i += 256) {
+        mx_fill_load(p, kt0, i, Mr, xb[0]);
+        mx_fill_store<HAD>(xb[0], aslot, ascl);
+      }
+      // rows Mr .. 32 TM - 1: zero codes, scale byte 0
+      const int zr = 32 * TM - Mr;
+      for (int i = threadIdx.x; i < nsp * zr * 8; i += 256) {
+        MxXBlock z;
+        z.ok = false;
+        z.c = i & 7;
+        z.st = (i >> 3) / zr;
+        z.r = Mr + (i >> 3) - z.st * zr;
+        mx_fill_store<HAD>(z, aslot, ascl);
+      }
+    }
+    wait_cnt<P1, FA ? 0 : 15>();
     block_barrier();
 
     MxFrag<TM, TN> f0, f1;
     uint32_t sa[TM], sb[TN];
     u32v4 gd[TM + TN];
-    mx_read_group<TM, TN>(group(G0), ra0, rb0, gd);
+    mx_read_group<TM, TN>(agrp(G0), group(G0) + MX_GROUP_OPND, ra0, rb0, gd);
     mx_stage_scales<0, TM, TN>(gd, sel, mask_of(kt0), sa, sb);
-    mx_read_frag<TM, TN>(stage(kt0), ra0, rb0, pos(h), f0);
+    mx_read_frag<TM, TN>(abuf(kt0), stage(kt0) + MX_OPND, ra0, rb0, pos(h), f0);
     // one iteration; H = a & 1 (kt0 is even, the loop takes stages in pairs)
     auto iteration = [&](auto Hc, int a) {
       constexpr int H = decltype(Hc)::value;
       constexpr int NM = TM * TN;             // MFMAs per step
       constexpr int NF = TM + TN;             // fragment reads per step
-      const uint8_t* st = stage(H);
-      mx_issue_codes<P1, P2, LA, LB>(oa, ob, stage(H ^ 1), a + 1, krow16, w);
-      mx_read_frag<TM, TN>(st, ra0, rb0, pos(2 + h), f1);
+      const uint8_t* st = stage(H) + MX_OPND;   // this stage's B codes
+      const uint8_t* sta = abuf(a);             // and its A codes
+      mx_issue_codes<P1, P2, LAL, LB>(oa, ob, stage(H ^ 1), a + 1, krow16, w);
+      mx_read_frag<TM, TN>(sta, st, ra0, rb0, pos(2 + h), f1);
       mx_mfma<0, TM, TN>(acc, f0, sa, sb);
       mx_sched<P2 - P1, NF, NM>();
-      mx_issue_codes<P2, NL, LA, LB>(oa, ob, stage(H ^ 1), a + 1, krow16, w);
+      mx_issue_codes<P2, NL, LAL, LB>(oa, ob, stage(H ^ 1), a + 1, krow16, w);
       // iteration a's scale piece: group (a + 3) / 2's A piece when a is odd,
       // group a / 2 + 1's B piece when a is even.  Group G is then complete at
       // the barrier of iteration 2G - 2, before stage 2G's scale bytes are
       // read in iteration 2G - 1, and its buffer last held group G - 3.
-      issue_piece(H ? (a + 3) >> 1 : (a >> 1) + 1, H ^ 1);
-      if (H) mx_read_group<TM, TN>(group((a + 1) >> 1), ra0, rb0, gd);   // stage a + 1 opens the next group
-      mx_read_frag<TM, TN>(st, ra0, rb0, pos(4 + h), f0);
+      if (!FA || !H) issue_piece(H ? (a + 3) >> 1 : (a >> 1) + 1, H ^ 1);
+      if (H)   // stage a + 1 opens the next group
+        mx_read_group<TM, TN>(agrp((a + 1) >> 1), group((a + 1) >> 1) + MX_GROUP_OPND, ra0, rb0, gd);
+      mx_read_frag<TM, TN>(sta, st, ra0, rb0, pos(4 + h), f0);
       mx_mfma<1, TM, TN>(acc, f1, sa, sb);
       mx_sched<NL - P2 + 1, NF + (H ? TM + TN : 0), NM>();
-      mx_read_frag<TM, TN>(st, ra0, rb0, pos(6 + h), f1);
+      mx_read_frag<TM, TN>(sta, st, ra0, rb0, pos(6 + h), f1);
       mx_mfma<2, TM, TN>(acc, f0, sa, sb);
       uint32_t sa_n[TM], sb_n[TN];
       mx_stage_scales<H ^ 1, TM, TN>(gd, sel, mask_of(a + 1), sa_n, sb_n);
       mx_sched<0, NF, NM>();
       wait_cnt<0, 0>();
       block_barrier();
-      mx_read_frag<TM, TN>(stage(H ^ 1), ra0, rb0, pos(h), f0);
-      mx_issue_codes<0, P1, LA, LB>(oa, ob, stage(H), a + 2, krow16, w);
+      mx_read_frag<TM, TN>(abuf(a + 1), stage(H ^ 1) + MX_OPND, ra0, rb0, pos(h), f0);
+      mx_issue_codes<0, P1, LAL, LB>(oa, ob, stage(H), a + 2, krow16, w);
       mx_mfma<3, TM, TN>(acc, f1, sa, sb);
       // the fragment reads first, then the loads, over the MFMAs
 #pragma unroll
@@ -647,6 +781,26 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_narrow_kernel(GemmArgs p) {
   if (kt1 > p.k_tiles) kt1 = p.k_tiles;
   float* Cz = p.C + (int64_t)z * p.split_stride;
   mx_tile<TM, 2, 1>(p, smem, 0, (int64_t)blockIdx.x * 256, kt0, kt1, Cz);
+}
+
+// Narrow MXFP4 GEMM whose A operand is quantized inside the kernel from the
+// bf16 activations (online activation quantization, "Bridging the Gap Between
+// Promise and Performance for Microscaling FP4 Quantization", abstract:
+// activations rotated and quantized on the fly in front of FP4 GEMMs whose
+// weights were rotated offline).  Same grid, split and tile pipeline as
+// gemm_mx_narrow_kernel, so the result equals quantize-then-GEMM bit for bit.
+// Each workgroup quantizes the activation rows for its own contraction range
+// (at most 16 / TM stages; the planner checks, and uses it for TM = 1 only).
+template <int TM, bool HAD>
+__global__ void __launch_bounds__(256, 1) gemm_mx_fused_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[MX_LDS];
+  const int z = blockIdx.y;
+  const int pairs = (p.k_tiles + 1) >> 1;
+  const int kt0 = 2 * (int)((int64_t)pairs * z / p.splits);
+  int kt1 = 2 * (int)((int64_t)pairs * (z + 1) / p.splits);
+  if (kt1 > p.k_tiles) kt1 = p.k_tiles;
+  float* Cz = p.C + (int64_t)z * p.split_stride;
+  mx_tile<TM, 2, 1, true, HAD>(p, smem, 0, (int64_t)blockIdx.x * 256, kt0, kt1, Cz);
 }
 
 // ---------------------------------------------------------------------------
@@ -769,12 +923,14 @@ GemmPlan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
   pl.k_tiles = (K + (mx ? MX_BK : BK) - 1) / (mx ? MX_BK : BK);
   pl.narrow_tm = 0;
   if (mx && M <= 128) {
-    // narrow tiles (32 TM x 256), split along K (in stage pairs) until about
-    // two workgroups per compute unit
+    // narrow tiles (32 TM x 256), split along K (in stage pairs) into at most
+    // one workgroup per compute unit, each split at least two pairs long
+    // (measured on the decode shapes: more, shorter splits pay the prologue
+    // latency more often than they gain in parallel streams)
     pl.narrow_tm = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
     const int64_t tiles = (N + 255) / 256, pairs = (pl.k_tiles + 1) / 2;
-    int64_t s = 512 / tiles;
-    if (s > pairs) s = pairs;
+    int64_t s = 256 / tiles;
+    if (s > pairs / 2) s = pairs / 2;
     if (s > 32) s = 32;
     pl.splits = s < 1 ? 1 : (int)s;
     return pl;
@@ -811,7 +967,7 @@ static int compute_units() {
 }
 
 static hipError_t launch_gemm_common(bool nv, GemmArgs p, float* C, int64_t ldc, float* workspace,
-                                     const GemmPlan& plan, hipStream_t stream) {
+                                     const GemmPlan& plan, hipStream_t stream, int fused_had = -1) {
   p.ntm = (int)((p.M + BM - 1) / BM);
   p.ntn = (int)((p.N + BN - 1) / BN);
   p.k_tiles = (int)plan.k_tiles;
@@ -834,6 +990,11 @@ static hipError_t launch_gemm_common(bool nv, GemmArgs p, float* C, int64_t ldc,
   dim3 grid((unsigned)(tiles + p.rem), (unsigned)plan.splits);
   if (nv) {
     hipLaunchKernelGGL(gemm_nv_kernel, grid, dim3(256), 0, stream, p);
+  } else if (plan.narrow_tm && fused_had >= 0) {
+    dim3 ngrid((unsigned)((p.N + 255) / 256), (unsigned)plan.splits);
+    // fused plans have 32-row tiles (fused_plan_ok)
+    if (fused_had) hipLaunchKernelGGL((gemm_mx_fused_kernel<1, true>), ngrid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((gemm_mx_fused_kernel<1, false>), ngrid, dim3(256), 0, stream, p);
   } else if (plan.narrow_tm) {
     dim3 ngrid((unsigned)((p.N + 255) / 256), (unsigned)plan.splits);
     if (plan.narrow_tm == 1) hipLaunchKernelGGL(gemm_mx_narrow_kernel<1>, ngrid, dim3(256), 0, stream, p);
@@ -860,6 +1021,30 @@ hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const
   p.a_ts = nullptr; p.b_ts = nullptr;
   p.M = M; p.N = N; p.K = K;
   return launch_gemm_common(false, p, C, ldc, workspace, plan, stream);
+}
+
+bool fused_plan_ok(const GemmPlan& plan) {
+  // up to 32 activation rows: with more, every column-tile workgroup repeats
+  // the quantization of more rows than a separate quantizer pass costs
+  // (measured: 64 and 128 rows against 14336 x 4096 and 4096 x 14336 weights
+  // ran 15-35 % slower fused than quantize-then-GEMM)
+  if (plan.narrow_tm != 1) return false;
+  const int64_t pairs = (plan.k_tiles + 1) / 2;
+  const int64_t stages = 2 * ((pairs + plan.splits - 1) / plan.splits);   // most stages of one split
+  return stages <= 16 / plan.narrow_tm;
+}
+
+hipError_t launch_gemm_mx_fused(const uint16_t* x, int64_t ldx, int hadamard, const uint8_t* b_codes,
+                                const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, float* C, int64_t ldc,
+                                float* workspace, const GemmPlan& plan, hipStream_t stream) {
+  GemmArgs p{};
+  p.a = nullptr; p.as = nullptr; p.b = b_codes; p.bs = b_scales;
+  p.a_ts = nullptr; p.b_ts = nullptr;
+  p.M = M; p.N = N; p.K = K;
+  p.x = x;
+  p.ldx = ldx;
+  p.x_vec = (((uintptr_t)x & 15) == 0 && (ldx % 8) == 0) ? 1 : 0;
+  return launch_gemm_common(false, p, C, ldc, workspace, plan, stream, hadamard ? 1 : 0);
 }
 
 hipError_t launch_gemm_nv(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,

@@ -133,4 +133,65 @@ mxfp4_status mxfp4_gemm(const mxfp4_tensor* A, const mxfp4_tensor* B, float* C, 
   return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
 }
 
+// Online activation quantization + GEMM: fused into the narrow GEMM when the
+// plan allows, else quantize into the workspace, then the GEMM.
+static mxfp4_status check_quantize_gemm(int64_t M, int64_t K, int hadamard, const mxfp4_tensor* B) {
+  if (!B || M < 0 || K < 0 || B->rows < 0 || B->k < 0 || (hadamard != 0 && hadamard != 1) || !fmt_ok(B->fmt))
+    return MXFP4_ERR_INVALID_ARG;
+  if (B->fmt != MXFP4_FMT_MX || B->k != K || B->hadamard != hadamard) return MXFP4_ERR_FORMAT_MISMATCH;
+  if (K % 128 != 0) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  if (M > 0 && K > kMaxElems / M) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  return MXFP4_OK;
+}
+
+static size_t align16(size_t n) { return (n + 15) & ~(size_t)15; }
+
+static size_t quantize_gemm_ws(int64_t M, int64_t N, int64_t K, bool* fused) {
+  const mxfp4::GemmPlan pl = mxfp4::plan_gemm(MXFP4_FMT_MX, M, N, K);
+  const size_t gemm_ws = pl.splits > 1 ? (size_t)pl.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
+  *fused = mxfp4::fused_plan_ok(pl);
+  if (*fused) return gemm_ws;
+  return align16((size_t)M * (size_t)(K / 2)) + align16((size_t)M * (size_t)(K / 32)) + gemm_ws;
+}
+
+mxfp4_status mxfp4_quantize_gemm_workspace_bytes(int64_t M, int64_t K, int hadamard, const mxfp4_tensor* B,
+                                                 size_t* bytes) {
+  if (!bytes) return MXFP4_ERR_INVALID_ARG;
+  mxfp4_status s = check_quantize_gemm(M, K, hadamard, B);
+  if (s != MXFP4_OK) return s;
+  bool fused;
+  *bytes = (M == 0 || B->rows == 0) ? 0 : quantize_gemm_ws(M, B->rows, K, &fused);
+  return MXFP4_OK;
+}
+
+mxfp4_status mxfp4_quantize_gemm(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int hadamard,
+                                 const mxfp4_tensor* B, float* C, int64_t ldc, void* workspace, size_t ws_bytes,
+                                 hipStream_t stream) {
+  mxfp4_status s = check_quantize_gemm(M, K, hadamard, B);
+  if (s != MXFP4_OK) return s;
+  const int64_t N = B->rows;
+  if (ldx < K || ldx < 1 || ldc < N || ldc < 1) return MXFP4_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return MXFP4_OK;
+  if (!x || !C || !B->codes || !B->scales) return MXFP4_ERR_INVALID_ARG;
+  if (!aligned(x, 2) || !aligned(B->codes, 16) || !aligned(B->scales, 4)) return MXFP4_ERR_INVALID_ARG;
+  bool fused;
+  const size_t need = quantize_gemm_ws(M, N, K, &fused);
+  if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 16))) return MXFP4_ERR_WORKSPACE;
+  const mxfp4::GemmPlan pl = mxfp4::plan_gemm(MXFP4_FMT_MX, M, N, K);
+  hipError_t e;
+  if (fused) {
+    e = mxfp4::launch_gemm_mx_fused(x, ldx, hadamard, B->codes, B->scales, M, N, K, C, ldc, (float*)workspace, pl,
+                                    stream);
+  } else {
+    uint8_t* a_codes = (uint8_t*)workspace;
+    uint8_t* a_scales = a_codes + align16((size_t)M * (size_t)(K / 2));
+    float* gemm_ws = (float*)(a_scales + align16((size_t)M * (size_t)(K / 32)));
+    e = mxfp4::launch_quantize(x, M, K, ldx, MXFP4_FMT_MX, MXFP4_RTN, hadamard, 1, 0, a_codes, a_scales, nullptr,
+                               nullptr, stream);
+    if (e == hipSuccess)
+      e = mxfp4::launch_gemm_mx(a_codes, a_scales, B->codes, B->scales, M, N, K, C, ldc, gemm_ws, pl, stream);
+  }
+  return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
+}
+
 }  // extern "C"

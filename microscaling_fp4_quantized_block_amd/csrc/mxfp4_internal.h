@@ -36,6 +36,14 @@ hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const
                           const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, float* C, int64_t ldc,
                           float* workspace, const GemmPlan& plan, hipStream_t stream);
 
+// Fused activation quantization + MXFP4 GEMM (narrow plans with 32-row tiles,
+// M <= 32, whose splits hold at most 16 stages): A = Q_MX,RTN(x [M, K] bf16,
+// row stride ldx, block Hadamard when hadamard), C = A * B^T.
+bool fused_plan_ok(const GemmPlan& plan);
+hipError_t launch_gemm_mx_fused(const uint16_t* x, int64_t ldx, int hadamard, const uint8_t* b_codes,
+                                const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, float* C, int64_t ldc,
+                                float* workspace, const GemmPlan& plan, hipStream_t stream);
+
 hipError_t launch_gemm_nv(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
                           const uint8_t* b_codes, const uint8_t* b_scales, const float* b_ts, int64_t M,
                           int64_t N, int64_t K, float* C, int64_t ldc, float* workspace, const GemmPlan& plan,

@@ -27,12 +27,9 @@
 namespace mxfp4 {
 
 // ---------------------------------------------------------------------------
-// Hadamard helpers.  Butterfly h: (x[i], x[i+h]) -> (x[i] + x[i+h], x[i] - x[i+h])
-// for i & h == 0, strides 1, 2, 4, 8, 16 in that order, then multiply by
-// RN_f32(1/sqrt(32)) = 0x3E3504F3.
+// Hadamard helpers (the butterfly order and the scale constant are given with
+// fwht32_inlane in fp4_device.h).
 // ---------------------------------------------------------------------------
-constexpr uint32_t kHadamardScaleBits = 0x3E3504F3u;
-
 // in-lane stages (h = 1, 2, 4) on 8 consecutive elements
 __device__ __forceinline__ void fwht8_inlane(float v[8]) {
 #pragma unroll
@@ -65,23 +62,6 @@ __device__ __forceinline__ void fwht32_quad(float v[8], uint32_t p) {
   const float c = __uint_as_float(kHadamardScaleBits);
 #pragma unroll
   for (int i = 0; i < 8; i++) v[i] = v[i] * c;
-}
-
-// Full 32-point rotation of a column held in one lane (32 registers).
-__device__ __forceinline__ void fwht32_inlane(float v[32]) {
-#pragma unroll
-  for (int h = 1; h < 32; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 32; i++) {
-      if (i & h) continue;
-      float a = v[i], b = v[i + h];
-      v[i] = a + b;
-      v[i + h] = a - b;
-    }
-  }
-  const float c = __uint_as_float(kHadamardScaleBits);
-#pragma unroll
-  for (int i = 0; i < 32; i++) v[i] = v[i] * c;
 }
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -149,3 +149,50 @@ def test_gemm_workspace_query_matches_split_plan(mx):
 def test_nv_gemm_needs_k_multiple_of_128(mx):
     g = lambda A, B: mx.lib.mxfp4_gemm(ctypes.byref(A), ctypes.byref(B), FAKE, 32, None, 0, None)
     assert g(desc(mx, fmt=1, k=192), desc(mx, fmt=1, rows=32, k=192)) == SHAPE
+
+
+def qgemm(mx, M=16, K=256, ldx=256, had=0, B=None, C=FAKE, ldc=64, ws=None, wsb=0, x=FAKE):
+    if B is None:
+        B = desc(mx, had=had, rows=64, k=K)
+    return mx.lib.mxfp4_quantize_gemm(x, M, K, ldx, had, ctypes.byref(B) if B != "null" else None, C, ldc, ws, wsb,
+                                      None)
+
+
+def qgemm_ws(mx, M, K, had, B):
+    b = ctypes.c_size_t()
+    s = mx.lib.mxfp4_quantize_gemm_workspace_bytes(M, K, had, ctypes.byref(B), ctypes.byref(b))
+    return s, b.value
+
+
+def test_quantize_gemm_rejects_bad_arguments(mx):
+    assert qgemm(mx, B="null") == INVALID
+    assert qgemm(mx, had=2, B=desc(mx, rows=64)) == INVALID
+    assert qgemm(mx, B=desc(mx, fmt=1, rows=64)) == MISMATCH            # weights must be MXFP4
+    assert qgemm(mx, B=desc(mx, rows=64, k=512)) == MISMATCH            # contraction lengths differ
+    assert qgemm(mx, had=1, B=desc(mx, had=0, rows=64)) == MISMATCH     # rotation must match the weights'
+    assert qgemm(mx, K=96, ldx=96, B=desc(mx, rows=64, k=96)) == SHAPE  # k % 128
+    assert qgemm(mx, ldx=100) == INVALID                                 # ldx < K
+    assert qgemm(mx, ldc=63) == INVALID                                  # ldc < N
+    assert qgemm(mx, x=None) == INVALID
+    assert qgemm(mx, C=None) == INVALID
+    assert qgemm(mx, B=desc(mx, rows=64, codes=FAKE + 8)) == INVALID    # weight codes must be 16-byte aligned
+    assert qgemm(mx, M=0) == OK                                          # empty output: no-op
+    # a decode shape with a split contraction needs its workspace
+    B = desc(mx, rows=14336, k=4096)
+    assert qgemm(mx, M=16, K=4096, ldx=4096, B=B, ldc=14336) == WORKSPACE
+
+
+def test_quantize_gemm_workspace_bytes(mx):
+    # decode 16 x 14336 x 4096: fused into the narrow GEMM (56 column tiles,
+    # 8 stage pairs -> 4 splits of 2 pairs); only the split partial sums
+    assert qgemm_ws(mx, 16, 4096, 0, desc(mx, rows=14336, k=4096)) == (OK, 4 * 16 * 14336 * 4)
+    assert qgemm_ws(mx, 16, 4096, 1, desc(mx, had=1, rows=14336, k=4096)) == (OK, 4 * 16 * 14336 * 4)
+    # wide activations: quantized codes and scales (16-byte padded), no split
+    assert qgemm_ws(mx, 300, 1024, 0, desc(mx, rows=512, k=1024)) == (OK, 300 * 512 + 300 * 32)
+    # a narrow plan whose splits are too long for LDS (128 rows -> 4 stages
+    # per split at most; 256 column tiles leave one split of 32 stages): two
+    # steps, codes + scales, no split partials
+    assert qgemm_ws(mx, 128, 8192, 0, desc(mx, rows=65536, k=8192)) == (OK, 128 * 4096 + 128 * 256)
+    # 16 column tiles over 28 stage pairs: 14 splits of 2 pairs, fused
+    assert qgemm_ws(mx, 16, 14336, 1, desc(mx, had=1, rows=4096, k=14336)) == (OK, 14 * 16 * 4096 * 4)
+    assert qgemm_ws(mx, 16, 4096, 0, desc(mx, fmt=1, rows=64, k=4096))[0] == MISMATCH
