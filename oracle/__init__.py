@@ -75,6 +75,8 @@ def _load():
     lib.mxo_dequantize.argtypes = [i32, i64, i64, vp, vp, vp, vp, i64]
     lib.mxo_gemm.restype = i32
     lib.mxo_gemm.argtypes = [i32, i64, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64, vp, vp]
+    lib.mxo_noise_stats.restype = i32
+    lib.mxo_noise_stats.argtypes = [vp, i64, i64, i64, i32, i32, i32, vp, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -199,3 +201,26 @@ def gemm(fmt: str, a, b, rows=None, cols=None):
     if rc != 0:
         raise ValueError("oracle gemm rejected its arguments")
     return Cm, Sm
+
+
+def noise_stats(x_bits: np.ndarray, q, fmt: str = "mx", hadamard: bool = False, axis: int = 1):
+    """Signal and quantization noise of a quantized operand (the quantities of
+    the sqrt(3) threshold of "FP4 All the Way", abstract).
+
+    x_bits: the [R, C] bf16 input (uint16 patterns); q = (codes, scales,
+    tensor_scale) its quantization with this fmt / hadamard / axis.  Returns
+    (sum y^2, sum (Q(y) - y)^2, elements left out) in binary64, y = the
+    contraction rows (rotated when hadamard), Q(y) the exactly dequantized
+    value; blocks with a NaN scale byte are left out.
+    """
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    R, C = x.shape
+    codes = np.ascontiguousarray(q[0], dtype=np.uint8)
+    scales = np.ascontiguousarray(q[1], dtype=np.uint8)
+    ts = np.array([q[2] if q[2] is not None else 1.0], dtype=np.float32)
+    out = np.zeros(3, dtype=np.float64)
+    rc = _load().mxo_noise_stats(_ptr(x), R, C, C, FMT[fmt], int(bool(hadamard)), int(axis), _ptr(codes),
+                                 _ptr(scales), _ptr(ts), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle noise_stats rejected its arguments")
+    return float(out[0]), float(out[1]), float(out[2])

@@ -451,3 +451,71 @@ int mxo_gemm(int fmt, int64_t K,
     free(arows);
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* Quantization noise against the signal, the quantities of the         */
+/* threshold in [FQT] abstract (quantized training loses effectiveness  */
+/* once the gradient norm falls below about sqrt(3) times the            */
+/* quantization noise).  READING: the signal is the quantized operand   */
+/* itself, y = the contraction rows of x (rotated when hadamard), and   */
+/* the noise is Q(y) - y with Q(y) the exactly dequantized value        */
+/* (E2M1 * scale, NV: * tensor scale, exact in binary64).  Blocks with  */
+/* a non-finite element (NaN scale byte) are left out and counted.      */
+/*   out[0] = sum y^2, out[1] = sum (Q(y) - y)^2   (binary64, row order) */
+/*   out[2] = number of elements left out.                               */
+/* ------------------------------------------------------------------ */
+int mxo_noise_stats(const uint16_t *x, int64_t R, int64_t C, int64_t ldx,
+                    int fmt, int hadamard, int axis,
+                    const uint8_t *codes, const uint8_t *scales, const float *tensor_scale,
+                    double *out)
+{
+    if (!x || !codes || !scales || !out || R < 0 || C < 0 || ldx < C) return -1;
+    if ((fmt != FMT_MX && fmt != FMT_NV) || (axis != 0 && axis != 1)) return -1;
+    if (fmt == FMT_NV && !tensor_scale) return -1;
+    const int bs = (fmt == FMT_MX) ? 32 : 16;
+    const int64_t rows = (axis == 1) ? R : C;
+    const int64_t K = (axis == 1) ? C : R;
+    if (K % bs != 0 || (hadamard && K % 32 != 0)) return -1;
+    out[0] = out[1] = out[2] = 0.0;
+    if (rows == 0 || K == 0) return 0;
+    double *row_s0 = (double *)calloc((size_t)rows, sizeof(double));
+    double *row_s1 = (double *)calloc((size_t)rows, sizeof(double));
+    double *row_n = (double *)calloc((size_t)rows, sizeof(double));
+    #pragma omp parallel
+    {
+        float *v = (float *)malloc(sizeof(float) * K);
+        #pragma omp for
+        for (int64_t i = 0; i < rows; i++) {
+            load_contraction_row(x, ldx, axis, i, K, hadamard, v);
+            double s0 = 0.0, s1 = 0.0, n = 0.0;
+            for (int64_t b = 0; b < K / bs; b++) {
+                int sbyte = scales[i * (K / bs) + b];
+                int nan_scale = (fmt == FMT_MX) ? (sbyte == 0xFF) : ((sbyte & 0x7F) == 0x7F);
+                if (nan_scale) { n += bs; continue; }
+                for (int j = 0; j < bs; j++) {
+                    int64_t k = b * bs + j;
+                    int code = (codes[i * (K / 2) + k / 2] >> (4 * (k & 1))) & 0xF;
+                    double q = mxo_e2m1_value(code) * (fmt == FMT_MX ? mxo_e8m0_value(sbyte)
+                                                                      : mxo_e4m3_value(sbyte) * (double)tensor_scale[0]);
+                    double yk = (double)v[k];
+                    double d = q - yk;
+                    s0 += yk * yk;
+                    s1 += d * d;
+                }
+            }
+            row_s0[i] = s0;
+            row_s1[i] = s1;
+            row_n[i] = n;
+        }
+        free(v);
+    }
+    for (int64_t i = 0; i < rows; i++) {
+        out[0] += row_s0[i];
+        out[1] += row_s1[i];
+        out[2] += row_n[i];
+    }
+    free(row_s0);
+    free(row_s1);
+    free(row_n);
+    return 0;
+}
