@@ -175,6 +175,32 @@ mxfp4_status mxfp4_quantize_gemm(const uint16_t *x, int64_t M, int64_t K, int64_
                                  const mxfp4_tensor *B, float *C, int64_t ldc,
                                  void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Workspace needed by mxfp4_quantization_noise for the quantized operand q
+ * (three doubles per workgroup of the pass; never 0). */
+mxfp4_status mxfp4_quantization_noise_workspace_bytes(const mxfp4_tensor *q, size_t *bytes);
+
+/* The two norms of the sqrt(3) threshold of "FP4 All the Way", abstract
+ * (quantized training loses effectiveness once the gradient norm falls below
+ * about sqrt(3) times the quantization noise), for a tensor q that
+ * mxfp4_quantize made from x with this axis:
+ *   stats[0] = sum y^2            (the signal),
+ *   stats[1] = sum (Q(y) - y)^2   (the quantization noise),
+ *   stats[2] = number of elements left out,
+ * over the elements y of the quantized operand (the contraction rows of x,
+ * rotated when q->hadamard), Q(y) the exactly dequantized value (E2M1 x
+ * scale, NVFP4 x tensor scale), in binary64; blocks with a NaN scale byte
+ * are left out.  The ratio sqrt(stats[0] / stats[1]) is the one the page
+ * compares with sqrt(3).  The sums come from per-workgroup partials added in
+ * a fixed order: the same inputs give the same bits.
+ * x: device bf16 [R, C] with (R, C) = (q->rows, q->k) for axis 1 and
+ *    (q->k, q->rows) for axis 0, leading dimension ldx >= C.
+ * stats: device, 3 doubles (8-byte aligned).
+ * workspace: device, 8-byte aligned, at least
+ *    mxfp4_quantization_noise_workspace_bytes. */
+mxfp4_status mxfp4_quantization_noise(const uint16_t *x, int64_t ldx, int axis, const mxfp4_tensor *q,
+                                      double *stats, void *workspace, size_t ws_bytes,
+                                      hipStream_t stream);
+
 /* A static, human-readable description of a status code. */
 const char *mxfp4_status_string(int status);
 

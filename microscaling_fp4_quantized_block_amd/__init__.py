@@ -64,6 +64,10 @@ def _load_library() -> ctypes.CDLL:
     lib.mxfp4_quantize_gemm_workspace_bytes.argtypes = [i64, i64, i32, P(MxTensorStruct), P(sz)]
     lib.mxfp4_quantize_gemm.restype = i32
     lib.mxfp4_quantize_gemm.argtypes = [vp, i64, i64, i64, i32, P(MxTensorStruct), vp, i64, vp, sz, vp]
+    lib.mxfp4_quantization_noise_workspace_bytes.restype = i32
+    lib.mxfp4_quantization_noise_workspace_bytes.argtypes = [P(MxTensorStruct), P(sz)]
+    lib.mxfp4_quantization_noise.restype = i32
+    lib.mxfp4_quantization_noise.argtypes = [vp, i64, i32, P(MxTensorStruct), vp, vp, sz, vp]
     return lib
 
 
@@ -216,6 +220,40 @@ def mxfp4_quantize_gemm(x: torch.Tensor, qb: QTensor, hadamard: bool = False, ou
     return out
 
 
+def mxfp4_quantization_noise_workspace_bytes(q: QTensor) -> int:
+    b = ctypes.c_size_t()
+    sq = q.as_struct()
+    _check(lib.mxfp4_quantization_noise_workspace_bytes(ctypes.byref(sq), ctypes.byref(b)))
+    return b.value
+
+
+def mxfp4_quantization_noise(x: torch.Tensor, q: QTensor, axis: int = 1, out: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Device float64 [3]: sum y^2, sum (Q(y) - y)^2 and the number of
+    elements left out (NaN blocks), y the elements of q's operand (x's
+    contraction rows, rotated when q is), Q(y) their dequantized values."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bfloat16 CUDA/HIP tensor with unit stride along its last dimension")
+    if out is None:
+        out = torch.empty(3, dtype=torch.float64, device=x.device)
+    ws_bytes = mxfp4_quantization_noise_workspace_bytes(q)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    sq = q.as_struct()
+    _check(lib.mxfp4_quantization_noise(_ptr(x), x.stride(0), int(axis), ctypes.byref(sq), _ptr(out),
+                                        _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return out
+
+
+def gradient_noise_ratio(x: torch.Tensor, q: QTensor, axis: int = 1):
+    """(ratio, below): ratio = ||y|| / ||Q(y) - y|| for the quantized operand,
+    and whether it falls below sqrt(3), the threshold under which quantized
+    training loses effectiveness ("FP4 All the Way", abstract)."""
+    s = mxfp4_quantization_noise(x, q, axis).cpu().tolist()
+    ratio = float("inf") if s[1] == 0.0 else (s[0] / s[1]) ** 0.5
+    return ratio, ratio < 3.0 ** 0.5
+
+
 quantize = mxfp4_quantize
 dequantize = mxfp4_dequantize
 gemm = mxfp4_gemm
@@ -224,4 +262,5 @@ quantize_gemm = mxfp4_quantize_gemm
 __all__ = ["QTensor", "MxFp4Error", "mxfp4_tensor_bytes", "mxfp4_quantize_workspace_bytes", "mxfp4_quantize",
            "mxfp4_dequantize", "mxfp4_gemm_workspace_bytes", "mxfp4_gemm", "mxfp4_status_string",
            "mxfp4_quantize_gemm_workspace_bytes", "mxfp4_quantize_gemm",
+           "mxfp4_quantization_noise_workspace_bytes", "mxfp4_quantization_noise", "gradient_noise_ratio",
            "quantize", "dequantize", "gemm", "quantize_gemm", "empty_qtensor", "lib", "LIB_PATH"]

@@ -134,6 +134,15 @@ __device__ __forceinline__ uint32_t mx_rtn_block32(const float y[32], uint32_t c
   return byte;
 }
 
+// E2M1 code -> value (OCP layout: bit 3 sign, bits 2:1 exponent with bias 1,
+// bit 0 mantissa; exponent 0 is subnormal), exact in binary32.
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  // magnitude table {0, .5, 1, 1.5, 2, 3, 4, 6} in binary32 bit patterns
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  float mag = e == 0 ? 0.5f * (float)m : __uint_as_float(((e + 126u) << 23) | (m << 22));
+  return (c & 8u) ? -mag : mag;
+}
+
 // ---------------------------------------------------------------------------
 // E4M3 (bias 7, no infinities, 0x7F NaN).
 // ---------------------------------------------------------------------------

@@ -194,4 +194,39 @@ mxfp4_status mxfp4_quantize_gemm(const uint16_t* x, int64_t M, int64_t K, int64_
   return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
 }
 
+static mxfp4_status check_noise_operand(const mxfp4_tensor* q) {
+  if (!q || !fmt_ok(q->fmt) || q->rows < 0 || q->k < 0 || (q->hadamard != 0 && q->hadamard != 1))
+    return MXFP4_ERR_INVALID_ARG;
+  if (q->k % block_of(q->fmt) != 0 || (q->hadamard && q->k % 32 != 0)) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  if (q->rows > 0 && q->k > kMaxElems / q->rows) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  return MXFP4_OK;
+}
+
+mxfp4_status mxfp4_quantization_noise_workspace_bytes(const mxfp4_tensor* q, size_t* bytes) {
+  if (!bytes) return MXFP4_ERR_INVALID_ARG;
+  mxfp4_status s = check_noise_operand(q);
+  if (s != MXFP4_OK) return s;
+  *bytes = mxfp4::noise_workspace_bytes(q->fmt, q->hadamard, q->rows, q->k);
+  return MXFP4_OK;
+}
+
+mxfp4_status mxfp4_quantization_noise(const uint16_t* x, int64_t ldx, int axis, const mxfp4_tensor* q,
+                                      double* stats, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  mxfp4_status s = check_noise_operand(q);
+  if (s != MXFP4_OK) return s;
+  if (axis != 0 && axis != 1) return MXFP4_ERR_INVALID_ARG;
+  const int64_t C = axis == 1 ? q->k : q->rows;   // columns of the input x [R, C]
+  if (ldx < C || ldx < 1 || !stats) return MXFP4_ERR_INVALID_ARG;
+  if (q->rows > 0 && q->k > 0) {
+    if (!x || !q->codes || !q->scales || (q->fmt == MXFP4_FMT_NV && !q->tensor_scale)) return MXFP4_ERR_INVALID_ARG;
+    if (!aligned(x, 2)) return MXFP4_ERR_INVALID_ARG;
+  }
+  if (!aligned(stats, 8)) return MXFP4_ERR_INVALID_ARG;
+  const size_t need = mxfp4::noise_workspace_bytes(q->fmt, q->hadamard, q->rows, q->k);
+  if (!workspace || ws_bytes < need || !aligned(workspace, 8)) return MXFP4_ERR_WORKSPACE;
+  hipError_t e = mxfp4::launch_noise(x, ldx, axis, q->fmt, q->hadamard, q->rows, q->k, q->codes, q->scales,
+                                     q->tensor_scale, stats, (double*)workspace, stream);
+  return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
+}
+
 }  // extern "C"

@@ -49,4 +49,11 @@ hipError_t launch_gemm_nv(const uint8_t* a_codes, const uint8_t* a_scales, const
                           int64_t N, int64_t K, float* C, int64_t ldc, float* workspace, const GemmPlan& plan,
                           hipStream_t stream);
 
+// Signal and quantization-noise sums of a quantized operand (noise.hip):
+// workspace = 3 doubles per workgroup of the pass.
+size_t noise_workspace_bytes(int fmt, int hadamard, int64_t rows, int64_t K);
+hipError_t launch_noise(const uint16_t* x, int64_t ldx, int axis, int fmt, int hadamard, int64_t rows, int64_t K,
+                        const uint8_t* codes, const uint8_t* scales, const float* ts, double* stats,
+                        double* partials, hipStream_t stream);
+
 }  // namespace mxfp4

@@ -717,13 +717,6 @@ hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
 // Dequantize: value = E2M1(code) * scale (NVFP4: RN(RN(E2M1 * s_b) * s_t)).
 // Lane = 8 elements (one 32-bit word of codes).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float e2m1_value(uint32_t c) {
-  // magnitude table {0, .5, 1, 1.5, 2, 3, 4, 6} in binary32 bit patterns
-  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
-  float mag = e == 0 ? 0.5f * (float)m : __uint_as_float(((e + 126u) << 23) | (m << 22));
-  return (c & 8u) ? -mag : mag;
-}
-
 template <int FMT>
 __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales,

@@ -196,3 +196,37 @@ def test_quantize_gemm_workspace_bytes(mx):
     # 16 column tiles over 28 stage pairs: 14 splits of 2 pairs, fused
     assert qgemm_ws(mx, 16, 14336, 1, desc(mx, had=1, rows=4096, k=14336)) == (OK, 14 * 16 * 4096 * 4)
     assert qgemm_ws(mx, 16, 4096, 0, desc(mx, fmt=1, rows=64, k=4096))[0] == MISMATCH
+
+
+def noise(mx, q=None, ldx=256, axis=1, x=FAKE, stats=FAKE, ws=FAKE, wsb=1 << 20):
+    if q is None:
+        q = desc(mx)
+    return mx.lib.mxfp4_quantization_noise(x, ldx, axis, ctypes.byref(q) if q != "null" else None, stats, ws, wsb,
+                                           None)
+
+
+def test_quantization_noise_rejects_bad_arguments(mx):
+    assert noise(mx, q="null") == INVALID
+    assert noise(mx, axis=2) == INVALID
+    assert noise(mx, q=desc(mx, fmt=2)) == INVALID
+    assert noise(mx, q=desc(mx, k=48)) == SHAPE                  # MX block of 32
+    assert noise(mx, q=desc(mx, fmt=1, had=1, k=48)) == SHAPE    # rotation needs k % 32
+    assert noise(mx, ldx=100) == INVALID                         # axis 1: x is [rows, k], ldx >= k
+    assert noise(mx, axis=0, ldx=63) == INVALID                  # axis 0: x is [k, rows], ldx >= rows
+    assert noise(mx, x=None) == INVALID
+    assert noise(mx, stats=None) == INVALID
+    assert noise(mx, stats=FAKE + 4) == INVALID                  # stats are doubles
+    assert noise(mx, q=desc(mx, fmt=1, ts=None)) == INVALID
+    assert noise(mx, ws=None) == WORKSPACE
+    assert noise(mx, wsb=8) == WORKSPACE
+
+
+def test_quantization_noise_workspace_bytes(mx):
+    b = ctypes.c_size_t()
+    f = lambda q: (mx.lib.mxfp4_quantization_noise_workspace_bytes(ctypes.byref(q), ctypes.byref(b)), b.value)
+    # three doubles per workgroup; a workgroup covers 256 units of 32 elements, at most 2048 workgroups
+    assert f(desc(mx, rows=64, k=256)) == (OK, 2 * 24)
+    assert f(desc(mx, rows=50432, k=3072)) == (OK, 2048 * 24)
+    assert f(desc(mx, fmt=1, rows=10, k=48)) == (OK, 24)        # NVFP4, units of 16: one workgroup
+    assert f(desc(mx, rows=0, k=0)) == (OK, 24)
+    assert mx.lib.mxfp4_quantization_noise_workspace_bytes(None, ctypes.byref(b)) == INVALID
