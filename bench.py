@@ -320,6 +320,22 @@ def sweep(args):
             rows.append((cfg, "gemm", gname, f"{Mg}x{Ng}x{Kg}", t * 1e6, tf, "TFLOP/s",
                          bound + ("-fp16" if fmt == "nv" and bound == "mfma" else ""), bound_t / t))
             del C, ws
+        if cfg in (4, 5):
+            # signal / noise sums of the stochastically rounded gradient
+            # operands (one pass over x, codes and scales)
+            for (name, rnd, axis), q in qs.items():
+                if rnd != "sr" or not name.startswith("dY"):
+                    continue
+                x = tens[name]
+                st = torch.empty(3, dtype=torch.float64, device=dev)
+                ws = torch.empty(mx.mxfp4_quantization_noise_workspace_bytes(q), dtype=torch.uint8, device=dev)
+                t = timed(lambda: mx.mxfp4_quantization_noise(x, q, axis, out=st, workspace=ws), True)
+                R, Cc = x.shape
+                nbytes = R * Cc * (2.0 + 0.5 + 1.0 / bs)
+                gbps = nbytes / t / 1e9
+                rows.append((cfg, "noise", f"{name} {rnd} axis{axis}", f"{R}x{Cc}", t * 1e6, gbps, "GB/s", "hbm",
+                             gbps / PEAK_HBM_GBPS))
+                del st, ws
         if cfg == 3:
             # decode with the activation quantization fused into the GEMM,
             # against the two launches it replaces (quantize, then GEMM)

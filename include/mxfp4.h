@@ -194,6 +194,7 @@ mxfp4_status mxfp4_quantization_noise_workspace_bytes(const mxfp4_tensor *q, siz
  * a fixed order: the same inputs give the same bits.
  * x: device bf16 [R, C] with (R, C) = (q->rows, q->k) for axis 1 and
  *    (q->k, q->rows) for axis 0, leading dimension ldx >= C.
+ * q->codes must be 8-byte aligned (INVALID_ARG otherwise).
  * stats: device, 3 doubles (8-byte aligned).
  * workspace: device, 8-byte aligned, at least
  *    mxfp4_quantization_noise_workspace_bytes. */

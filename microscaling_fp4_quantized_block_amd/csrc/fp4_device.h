@@ -47,6 +47,23 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
 }
 
 // ---------------------------------------------------------------------------
+// Division of a 32-bit index by a divisor fixed for the launch
+// (Granlund & Montgomery: q = (umulhi(n, m) + n) >> s, the sum in 64 bits).
+struct FastDiv {
+  uint32_t d, m, s;
+};
+static FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while ((1ull << s) < d) s++;
+  const uint64_t m = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
+  return FastDiv{d, (uint32_t)m, s};
+}
+__device__ __forceinline__ uint32_t fastdiv(uint32_t n, const FastDiv& f) {
+  const uint32_t hi = __umulhi(n, f.m);
+  return (uint32_t)(((uint64_t)hi + n) >> f.s);
+}
+
+// ---------------------------------------------------------------------------
 // MXFP4 shared scale: the smallest e with 6 * 2^e >= amax, clamped to
 // [-127, 127]; returned as the E8M0 byte e + 127.  `abits` is the IEEE
 // binary32 pattern of amax >= 0 (finite).  For a normal amax = (1 + f) 2^E:

@@ -219,7 +219,7 @@ mxfp4_status mxfp4_quantization_noise(const uint16_t* x, int64_t ldx, int axis, 
   if (ldx < C || ldx < 1 || !stats) return MXFP4_ERR_INVALID_ARG;
   if (q->rows > 0 && q->k > 0) {
     if (!x || !q->codes || !q->scales || (q->fmt == MXFP4_FMT_NV && !q->tensor_scale)) return MXFP4_ERR_INVALID_ARG;
-    if (!aligned(x, 2)) return MXFP4_ERR_INVALID_ARG;
+    if (!aligned(x, 2) || !aligned(q->codes, 8)) return MXFP4_ERR_INVALID_ARG;
   }
   if (!aligned(stats, 8)) return MXFP4_ERR_INVALID_ARG;
   const size_t need = mxfp4::noise_workspace_bytes(q->fmt, q->hadamard, q->rows, q->k);

@@ -8,7 +8,8 @@
 // value (E2M1 x scale, NVFP4 x tensor scale; exact in binary64), and
 //   stats[0] = sum y^2, stats[1] = sum (Q(y) - y)^2,
 //   stats[2] = elements of blocks with a NaN scale byte (left out),
-// all in binary64.  Each workgroup writes its three partial sums, and one
+// all in binary64 (squares accumulated with fused multiply-adds).  Each
+// workgroup writes its three partial sums, and one
 // workgroup adds the partials in a fixed order, so the result does not
 // depend on scheduling.
 //
@@ -30,6 +31,8 @@ struct NoiseArgs {
   const uint8_t* scales;
   const float* ts;          // NVFP4 tensor scale (device)
   int64_t units;            // rows * K / U
+  FastDiv div;              // by K / U (axis 1) or rows (axis 0), when units < 2^31
+  int small;                // units < 2^31: 32-bit unit indices
   int vec;                  // axis 1: x 16-byte aligned and ldx % 8 == 0
   double* partials;         // 3 per workgroup
 };
@@ -60,8 +63,14 @@ __global__ void __launch_bounds__(256) noise_kernel(NoiseArgs a) {
   double s0 = 0.0, s1 = 0.0, n = 0.0;
   for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < a.units; u += (int64_t)gridDim.x * 256) {
     int64_t i, b;
-    if (AXIS == 1) { i = u / nu; b = u - i * nu; }
-    else { b = u / a.rows; i = u - b * a.rows; }
+    if (a.small) {
+      const uint32_t qd = fastdiv((uint32_t)u, a.div), rm = (uint32_t)u - qd * a.div.d;
+      if (AXIS == 1) { i = qd; b = rm; } else { b = qd; i = rm; }
+    } else if (AXIS == 1) {
+      i = u / nu; b = u - i * nu;
+    } else {
+      b = u / a.rows; i = u - b * a.rows;
+    }
     const int64_t k0 = b * U;
     float y[U];
     if (AXIS == 1) {
@@ -86,7 +95,28 @@ __global__ void __launch_bounds__(256) noise_kernel(NoiseArgs a) {
       for (int j = 0; j < U; j++) y[j] = __uint_as_float((uint32_t)src[(int64_t)j * a.ldx] << 16);
     }
     if constexpr (HAD) fwht32_inlane(y);
-    const uint8_t* crow = a.codes + i * (a.K / 2) + k0 / 2;
+    // codes: U / 2 bytes, 8-byte aligned (K / 2 and k0 / 2 are multiples of 8)
+    uint32_t cw[U / 8];
+    {
+      const uint2* cp = (const uint2*)(a.codes + i * (a.K / 2) + k0 / 2);
+#pragma unroll
+      for (int q = 0; q < U / 16; q++) {
+        const uint2 v = cp[q];
+        cw[2 * q] = v.x;
+        cw[2 * q + 1] = v.y;
+      }
+    }
+    // E2M1 codes -> exact binary32 values (hardware convert, unit scale)
+    float g[U];
+#pragma unroll
+    for (int q = 0; q < U / 8; q++) {
+      const f32x2 g0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[q], 1.0f, 0);
+      const f32x2 g1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[q], 1.0f, 1);
+      const f32x2 g2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[q], 1.0f, 2);
+      const f32x2 g3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[q], 1.0f, 3);
+      g[8 * q + 0] = g0[0]; g[8 * q + 1] = g0[1]; g[8 * q + 2] = g1[0]; g[8 * q + 3] = g1[1];
+      g[8 * q + 4] = g2[0]; g[8 * q + 5] = g2[1]; g[8 * q + 6] = g3[0]; g[8 * q + 7] = g3[1];
+    }
     const uint8_t* srow = a.scales + i * (a.K / BS) + k0 / BS;
 #pragma unroll
     for (int blk = 0; blk < U / BS; blk++) {
@@ -98,16 +128,13 @@ __global__ void __launch_bounds__(256) noise_kernel(NoiseArgs a) {
       }
       const double sc = (FMT == FMT_MX) ? (double)e8m0_value(sb) : (double)e4m3_value(sb) * st;
 #pragma unroll
-      for (int j = 0; j < BS; j += 2) {
-        const uint32_t byte = crow[(blk * BS + j) / 2];
-#pragma unroll
-        for (int h = 0; h < 2; h++) {
-          const double q = (double)e2m1_value((byte >> (4 * h)) & 0xFu) * sc;
-          const double yv = (double)y[blk * BS + j + h];
-          const double d = q - yv;
-          s0 += yv * yv;
-          s1 += d * d;
-        }
+      for (int j = 0; j < BS; j++) {
+        const int e = blk * BS + j;
+        const double q = (double)g[e] * sc;
+        const double yv = (double)y[e];
+        const double d = q - yv;
+        s0 = __builtin_fma(yv, yv, s0);      // yv * yv is exact: the same as a multiply and an add
+        s1 = __builtin_fma(d, d, s1);
       }
     }
   }
@@ -127,7 +154,9 @@ __global__ void __launch_bounds__(256) noise_finalize_kernel(const double* __res
   block_sum3(a, b, c, stats);
 }
 
-constexpr int kNoiseMaxWGs = 2048;
+// One unit per thread up to 2^16 workgroups (16.7 M units), so that many
+// loads are in flight; larger operands loop.
+constexpr int kNoiseMaxWGs = 65536;
 
 static int noise_unit(int fmt, int hadamard, int64_t K) {
   return (fmt == FMT_NV && !hadamard && K % 32 != 0) ? 16 : 32;
@@ -175,6 +204,8 @@ hipError_t launch_noise(const uint16_t* x, int64_t ldx, int axis, int fmt, int h
   a.ts = ts;
   const int u = noise_unit(fmt, hadamard, K);
   a.units = rows * (K / u);
+  a.small = a.units < ((int64_t)1 << 31) ? 1 : 0;
+  a.div = make_fastdiv(a.small ? (uint32_t)(axis == 1 ? K / u : (rows > 0 ? rows : 1)) : 1u);
   a.vec = (((uintptr_t)x & 15) == 0 && ldx % 8 == 0) ? 1 : 0;
   a.partials = partials;
   const int64_t g = noise_wgs(fmt, hadamard, rows, K);

@@ -90,22 +90,6 @@ __device__ __forceinline__ void nv_block_scale(float amax, float st, uint32_t& b
   inv = byte ? __fdiv_rn(1.0f, d) : 0.0f;
 }
 
-// Division of a 32-bit index by a divisor fixed for the launch
-// (Granlund & Montgomery: q = (umulhi(n, m) + n) >> s, the sum in 64 bits).
-struct FastDiv {
-  uint32_t d, m, s;
-};
-static FastDiv make_fastdiv(uint32_t d) {
-  uint32_t s = 0;
-  while ((1ull << s) < d) s++;
-  const uint64_t m = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
-  return FastDiv{d, (uint32_t)m, s};
-}
-__device__ __forceinline__ uint32_t fastdiv(uint32_t n, const FastDiv& f) {
-  const uint32_t hi = __umulhi(n, f.m);
-  return (uint32_t)(((uint64_t)hi + n) >> f.s);
-}
-
 // ---------------------------------------------------------------------------
 // Encoding of 8 consecutive contraction elements of one block into a 32-bit
 // word of codes (element j in bits 4j+3..4j), given the block's scale byte.

@@ -217,6 +217,7 @@ def test_quantization_noise_rejects_bad_arguments(mx):
     assert noise(mx, stats=None) == INVALID
     assert noise(mx, stats=FAKE + 4) == INVALID                  # stats are doubles
     assert noise(mx, q=desc(mx, fmt=1, ts=None)) == INVALID
+    assert noise(mx, q=desc(mx, codes=FAKE + 4)) == INVALID      # codes are read as 8-byte words
     assert noise(mx, ws=None) == WORKSPACE
     assert noise(mx, wsb=8) == WORKSPACE
 
@@ -224,9 +225,10 @@ def test_quantization_noise_rejects_bad_arguments(mx):
 def test_quantization_noise_workspace_bytes(mx):
     b = ctypes.c_size_t()
     f = lambda q: (mx.lib.mxfp4_quantization_noise_workspace_bytes(ctypes.byref(q), ctypes.byref(b)), b.value)
-    # three doubles per workgroup; a workgroup covers 256 units of 32 elements, at most 2048 workgroups
+    # three doubles per workgroup; a workgroup covers 256 units of 32 elements, at most 65536 workgroups
     assert f(desc(mx, rows=64, k=256)) == (OK, 2 * 24)
-    assert f(desc(mx, rows=50432, k=3072)) == (OK, 2048 * 24)
+    assert f(desc(mx, rows=50432, k=3072)) == (OK, 18912 * 24)
+    assert f(desc(mx, rows=1 << 20, k=8192)) == (OK, 65536 * 24)
     assert f(desc(mx, fmt=1, rows=10, k=48)) == (OK, 24)        # NVFP4, units of 16: one workgroup
     assert f(desc(mx, rows=0, k=0)) == (OK, 24)
     assert mx.lib.mxfp4_quantization_noise_workspace_bytes(None, ctypes.byref(b)) == INVALID
