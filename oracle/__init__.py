@@ -75,6 +75,8 @@ def _load():
     lib.mxo_dequantize.argtypes = [i32, i64, i64, vp, vp, vp, vp, i64]
     lib.mxo_gemm.restype = i32
     lib.mxo_gemm.argtypes = [i32, i64, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64, vp, vp]
+    lib.mxo_quantize_mse.restype = i32
+    lib.mxo_quantize_mse.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, vp, vp, vp]
     lib.mxo_noise_stats.restype = i32
     lib.mxo_noise_stats.argtypes = [vp, i64, i64, i64, i32, i32, i32, vp, vp, vp, vp]
     _lib = lib
@@ -224,3 +226,22 @@ def noise_stats(x_bits: np.ndarray, q, fmt: str = "mx", hadamard: bool = False, 
     if rc != 0:
         raise ValueError("oracle noise_stats rejected its arguments")
     return float(out[0]), float(out[1]), float(out[2])
+
+
+def quantize_mse(x_bits: np.ndarray, fmt: str = "nv", hadamard: bool = False, axis: int = 1, iters: int = 2):
+    """Round-to-nearest quantization with MSE-fitted scales (the digest of the
+    MR-GPTQ paper, step 1): per-block scale search within a window below the
+    absmax scale, alternating with the least-squares tensor scale (NVFP4)
+    `iters` times.  Same return value as quantize()."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    R, C = x.shape
+    rows, K = (R, C) if axis == 1 else (C, R)
+    bs = BLOCK[fmt]
+    codes = np.zeros((rows, K // 2), dtype=np.uint8)
+    scales = np.zeros((rows, K // bs), dtype=np.uint8)
+    ts = np.zeros(1, dtype=np.float32) if fmt == "nv" else None
+    rc = _load().mxo_quantize_mse(_ptr(x), R, C, C, FMT[fmt], int(bool(hadamard)), int(axis), int(iters),
+                                  _ptr(codes), _ptr(scales), _ptr(ts))
+    if rc != 0:
+        raise ValueError("oracle quantize_mse rejected its arguments")
+    return codes, scales, (float(ts[0]) if ts is not None else None)

@@ -519,3 +519,196 @@ int mxo_noise_stats(const uint16_t *x, int64_t R, int64_t C, int64_t ldx,
     free(row_n);
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* MSE-optimal scales [DIG step 1: the quantization grid is fitted for  */
+/* mean squared error by optimizing, in turn, the scales of each block  */
+/* and the scale of the tensor].  READINGS (the page gives the idea,    */
+/* not the procedure):                                                  */
+/*  - round-to-nearest only (a forward / weight quantizer);             */
+/*  - block step: among a window of candidate scales the block keeps    */
+/*    the one with the smallest squared error sum (y - Q(y))^2 over its */
+/*    own elements, Q(y) the exactly dequantized value; MX candidates:  */
+/*    the absmax exponent e0, e0 - 1, e0 - 2 (>= -127); NV candidates:  */
+/*    the absmax E4M3 byte b0 and the 8 bytes below it (>= 1), scales   */
+/*    down to about half; a tie keeps the larger scale; elements are    */
+/*    encoded exactly as in the absmax quantizer for the chosen scale;  */
+/*  - a block's error is summed in binary64 in a fixed order: runs of 8 */
+/*    consecutive elements summed in turn, then (S0 + S1) + (S2 + S3)   */
+/*    for 32 elements, S0 + S1 for 16;                                  */
+/*  - tensor step (NV): with block bytes b and codes g fixed, the least */
+/*    squares tensor scale sum(y p) / sum(p^2), p = E4M3(b) E2M1(g),    */
+/*    both sums in binary64 in a fixed order (each unit of 32           */
+/*    contraction elements -- 16 for NV without rotation when K is not  */
+/*    a multiple of 32 -- in turn; each operand row over its units in   */
+/*    turn; rows in 256 contiguous ranges [t rows/256, (t+1) rows/256)  */
+/*    in turn; the 256 range sums in turn), blocks with a NaN scale left*/
+/*    out; the binary64 quotient rounded to binary32 and kept >= 2^-117;*/
+/*    unchanged when sum(y p) <= 0;                                     */
+/*  - schedule: block step with the absmax tensor scale, then `iters`   */
+/*    times (tensor step, block step).  MX has no tensor step.          */
+/* ------------------------------------------------------------------ */
+static double mse_tree(const double *d2, int n)
+{
+    double s[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int r = 0; r < n / 8; r++)
+        for (int j = 0; j < 8; j++) s[r] += d2[8 * r + j];
+    return n == 16 ? s[0] + s[1] : (s[0] + s[1]) + (s[2] + s[3]);
+}
+
+/* One block: scale byte and codes of the MSE choice. */
+static void mse_block(int fmt, const float *y, float st, int *byte_out, int *codes)
+{
+    const int bs = (fmt == FMT_MX) ? 32 : 16;
+    float amax = 0.0f;
+    int finite = 1;
+    for (int j = 0; j < bs; j++) {
+        if (!isfinite(y[j])) finite = 0;
+        else if (fabsf(y[j]) > amax) amax = fabsf(y[j]);
+    }
+    if (!finite) {
+        *byte_out = (fmt == FMT_MX) ? 0xFF : 0x7F;
+        for (int j = 0; j < bs; j++) codes[j] = 0;
+        return;
+    }
+    double d2[32];
+    int cand[32];
+    double best = INFINITY;
+    if (fmt == FMT_MX) {
+        int e0 = mxo_mx_scale_exponent(amax);
+        for (int e = e0; e >= e0 - 2 && e >= -127; e--) {
+            double step = ldexp(1.0, -e), sc = ldexp(1.0, e);
+            for (int j = 0; j < bs; j++) {
+                cand[j] = mxo_rtn_code((double)y[j] * step);
+                double d = (double)y[j] - mxo_e2m1_value(cand[j]) * sc;
+                d2[j] = d * d;
+            }
+            double E = mse_tree(d2, bs);
+            if (E < best) {
+                best = E;
+                *byte_out = e + 127;
+                for (int j = 0; j < bs; j++) codes[j] = cand[j];
+            }
+        }
+        return;
+    }
+    float den = 6.0f * st;
+    float r = amax / den;
+    int b0 = mxo_e4m3_round_up(r);
+    if (b0 == 0) {
+        *byte_out = 0;
+        for (int j = 0; j < bs; j++) codes[j] = mxo_rtn_code(copysign(0.0, (double)y[j]));
+        return;
+    }
+    for (int b = b0; b >= b0 - 8 && b >= 1; b--) {
+        float sb = (float)mxo_e4m3_value(b);
+        float d = sb * st;
+        float inv = 1.0f / d;
+        for (int j = 0; j < bs; j++) {
+            float q = y[j] * inv;
+            cand[j] = mxo_rtn_code((double)q);
+            double dd = (double)y[j] - mxo_e2m1_value(cand[j]) * (double)sb * (double)st;
+            d2[j] = dd * dd;
+        }
+        double E = mse_tree(d2, bs);
+        if (E < best) {
+            best = E;
+            *byte_out = b;
+            for (int j = 0; j < bs; j++) codes[j] = cand[j];
+        }
+    }
+}
+
+int mxo_quantize_mse(const uint16_t *x, int64_t R, int64_t C, int64_t ldx,
+                     int fmt, int hadamard, int axis, int iters,
+                     uint8_t *codes, uint8_t *scales, float *tensor_scale)
+{
+    if (!x || !codes || !scales || R < 0 || C < 0 || ldx < C || iters < 0) return -1;
+    if ((fmt != FMT_MX && fmt != FMT_NV) || (axis != 0 && axis != 1)) return -1;
+    if (fmt == FMT_NV && !tensor_scale) return -1;
+    const int bs = (fmt == FMT_MX) ? 32 : 16;
+    const int64_t rows = (axis == 1) ? R : C;
+    const int64_t K = (axis == 1) ? C : R;
+    if (K % bs != 0 || (hadamard && K % 32 != 0)) return -1;
+    if (rows == 0 || K == 0) {
+        if (fmt == FMT_NV) *tensor_scale = 1.0f;
+        return 0;
+    }
+    /* the operand, rotated once */
+    float *Y = (float *)malloc(sizeof(float) * (size_t)rows * (size_t)K);
+    if (!Y) return -1;
+    #pragma omp parallel for
+    for (int64_t i = 0; i < rows; i++) load_contraction_row(x, ldx, axis, i, K, hadamard, Y + i * K);
+    float st = 1.0f;
+    if (fmt == FMT_NV) {
+        float amax_t = 0.0f;
+        for (int64_t t = 0; t < rows * K; t++) {
+            float a = fabsf(Y[t]);
+            if (isfinite(a) && a > amax_t) amax_t = a;
+        }
+        st = mxo_nv_tensor_scale(amax_t);
+    }
+    const int unit = (fmt == FMT_NV && !hadamard && K % 32 != 0) ? 16 : 32;
+    double *row_num = (double *)malloc(sizeof(double) * (size_t)rows);
+    double *row_den = (double *)malloc(sizeof(double) * (size_t)rows);
+    for (int round = 0; round <= iters; round++) {
+        if (round > 0 && fmt == FMT_NV) {
+            /* tensor step from the previous block step's bytes and codes */
+            #pragma omp parallel for
+            for (int64_t i = 0; i < rows; i++) {
+                double rn = 0.0, rd = 0.0;
+                for (int64_t k0 = 0; k0 < K; k0 += unit) {
+                    double un = 0.0, ud = 0.0;
+                    for (int64_t k = k0; k < k0 + unit; k++) {
+                        int sbyte = scales[i * (K / bs) + k / bs];
+                        if ((sbyte & 0x7F) == 0x7F) continue;
+                        int code = (codes[i * (K / 2) + k / 2] >> (4 * (k & 1))) & 0xF;
+                        double p = mxo_e2m1_value(code) * mxo_e4m3_value(sbyte);
+                        un += (double)Y[i * K + k] * p;
+                        ud += p * p;
+                    }
+                    rn += un;
+                    rd += ud;
+                }
+                row_num[i] = rn;
+                row_den[i] = rd;
+            }
+            double num = 0.0, den = 0.0;
+            for (int64_t t = 0; t < 256; t++) {
+                double sn = 0.0, sd = 0.0;
+                for (int64_t i = t * rows / 256; i < (t + 1) * rows / 256; i++) {
+                    sn += row_num[i];
+                    sd += row_den[i];
+                }
+                num += sn;
+                den += sd;
+            }
+            if (num > 0.0 && den > 0.0) {
+                float s = (float)(num / den);
+                const float floor_st = ldexpf(1.0f, -117);
+                st = s < floor_st ? floor_st : s;
+            }
+        }
+        /* block step */
+        #pragma omp parallel for
+        for (int64_t i = 0; i < rows; i++) {
+            int cs[32];
+            for (int64_t b = 0; b < K / bs; b++) {
+                int byte = 0;
+                mse_block(fmt, Y + i * K + b * bs, st, &byte, cs);
+                scales[i * (K / bs) + b] = (uint8_t)byte;
+                for (int j = 0; j < bs; j++) {
+                    int64_t k = b * bs + j;
+                    uint8_t *cb = &codes[i * (K / 2) + k / 2];
+                    if ((k & 1) == 0) *cb = (uint8_t)((*cb & 0xF0) | cs[j]);
+                    else *cb = (uint8_t)((*cb & 0x0F) | (cs[j] << 4));
+                }
+            }
+        }
+    }
+    if (fmt == FMT_NV) *tensor_scale = st;
+    free(row_num);
+    free(row_den);
+    free(Y);
+    return 0;
+}
