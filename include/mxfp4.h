@@ -175,6 +175,35 @@ mxfp4_status mxfp4_quantize_gemm(const uint16_t *x, int64_t M, int64_t K, int64_
                                  const mxfp4_tensor *B, float *C, int64_t ldc,
                                  void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Workspace needed by mxfp4_quantize_mse (0 for MXFP4; NVFP4: the tensor
+ * amax partials, then 16 bytes per unit of 32 contraction elements and per
+ * operand row for the tensor-scale sums).  Errors as for mxfp4_quantize_mse. */
+mxfp4_status mxfp4_quantize_mse_workspace_bytes(int fmt, int hadamard, int64_t R, int64_t C, int axis,
+                                                size_t *bytes);
+
+/* Round-to-nearest quantization with scales fitted for mean squared error
+ * (the digest of the MR-GPTQ paper, step 1: the grid is fitted for MSE by
+ * optimizing the block scales and the tensor scale in turn).  As read here:
+ *   block step:  each block keeps, among candidate scales at and below its
+ *                absmax scale (MXFP4: exponents e0, e0 - 1, e0 - 2; NVFP4: the
+ *                absmax E4M3 byte and the 8 bytes below it), the one with the
+ *                smallest sum of (y - Q(y))^2 over its elements (binary64, runs
+ *                of 8 elements in turn, then (S0 + S1) + (S2 + S3) or S0 + S1),
+ *                a tie keeping the larger scale; elements are encoded as
+ *                mxfp4_quantize(RTN) encodes them for that scale;
+ *   tensor step: NVFP4 only, the least-squares tensor scale for the block
+ *                step's bytes and codes, sum(y p) / sum(p^2) with p = E4M3 x
+ *                E2M1 in binary64 in a fixed order, rounded to binary32;
+ *   schedule:    block step with the absmax tensor scale, then iters times
+ *                (tensor step, block step); iters in [0, 64], ignored for MXFP4.
+ * The output is an ordinary quantized tensor (mxfp4_gemm and
+ * mxfp4_dequantize take it as is); arguments and layout as mxfp4_quantize
+ * (RTN).  workspace: device, 16-byte aligned, at least
+ * mxfp4_quantize_mse_workspace_bytes (NULL if that is 0). */
+mxfp4_status mxfp4_quantize_mse(const uint16_t *x, int64_t R, int64_t C, int64_t ldx, int fmt, int hadamard,
+                                int axis, int iters, mxfp4_tensor *out, void *workspace, size_t ws_bytes,
+                                hipStream_t stream);
+
 /* Workspace needed by mxfp4_quantization_noise for the quantized operand q
  * (three doubles per workgroup of the pass; never 0). */
 mxfp4_status mxfp4_quantization_noise_workspace_bytes(const mxfp4_tensor *q, size_t *bytes);

@@ -64,6 +64,10 @@ def _load_library() -> ctypes.CDLL:
     lib.mxfp4_quantize_gemm_workspace_bytes.argtypes = [i64, i64, i32, P(MxTensorStruct), P(sz)]
     lib.mxfp4_quantize_gemm.restype = i32
     lib.mxfp4_quantize_gemm.argtypes = [vp, i64, i64, i64, i32, P(MxTensorStruct), vp, i64, vp, sz, vp]
+    lib.mxfp4_quantize_mse_workspace_bytes.restype = i32
+    lib.mxfp4_quantize_mse_workspace_bytes.argtypes = [i32, i32, i64, i64, i32, P(sz)]
+    lib.mxfp4_quantize_mse.restype = i32
+    lib.mxfp4_quantize_mse.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, P(MxTensorStruct), vp, sz, vp]
     lib.mxfp4_quantization_noise_workspace_bytes.restype = i32
     lib.mxfp4_quantization_noise_workspace_bytes.argtypes = [P(MxTensorStruct), P(sz)]
     lib.mxfp4_quantization_noise.restype = i32
@@ -220,6 +224,32 @@ def mxfp4_quantize_gemm(x: torch.Tensor, qb: QTensor, hadamard: bool = False, ou
     return out
 
 
+def mxfp4_quantize_mse_workspace_bytes(fmt: str, hadamard: bool, R: int, C: int, axis: int = 1) -> int:
+    b = ctypes.c_size_t()
+    _check(lib.mxfp4_quantize_mse_workspace_bytes(FMT[fmt], int(bool(hadamard)), R, C, axis, ctypes.byref(b)))
+    return b.value
+
+
+def mxfp4_quantize_mse(x: torch.Tensor, fmt: str = "nv", hadamard: bool = False, axis: int = 1, iters: int = 2,
+                       out: Optional[QTensor] = None, workspace: Optional[torch.Tensor] = None) -> QTensor:
+    """Round-to-nearest quantization with MSE-fitted block scales (and, for
+    NVFP4, a least-squares tensor scale, alternating iters times)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bfloat16 CUDA/HIP tensor with unit stride along its last dimension")
+    R, C = x.shape
+    rows, k = (R, C) if axis == 1 else (C, R)
+    if out is None:
+        out = empty_qtensor(fmt, rows, k, hadamard, x.device)
+    ws_bytes = mxfp4_quantize_mse_workspace_bytes(fmt, hadamard, R, C, axis)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    st = out.as_struct()
+    _check(lib.mxfp4_quantize_mse(_ptr(x), R, C, x.stride(0), FMT[fmt], int(bool(hadamard)), int(axis), int(iters),
+                                  ctypes.byref(st), _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                  _stream(x.device)))
+    return out
+
+
 def mxfp4_quantization_noise_workspace_bytes(q: QTensor) -> int:
     b = ctypes.c_size_t()
     sq = q.as_struct()
@@ -263,4 +293,5 @@ __all__ = ["QTensor", "MxFp4Error", "mxfp4_tensor_bytes", "mxfp4_quantize_worksp
            "mxfp4_dequantize", "mxfp4_gemm_workspace_bytes", "mxfp4_gemm", "mxfp4_status_string",
            "mxfp4_quantize_gemm_workspace_bytes", "mxfp4_quantize_gemm",
            "mxfp4_quantization_noise_workspace_bytes", "mxfp4_quantization_noise", "gradient_noise_ratio",
+           "mxfp4_quantize_mse_workspace_bytes", "mxfp4_quantize_mse",
            "quantize", "dequantize", "gemm", "quantize_gemm", "empty_qtensor", "lib", "LIB_PATH"]

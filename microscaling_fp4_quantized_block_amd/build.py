@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxfp4.so")
-SOURCES = ["quantize.hip", "gemm.hip", "noise.hip", "mxfp4_abi.cpp"]
+SOURCES = ["quantize.hip", "gemm.hip", "noise.hip", "mse.hip", "mxfp4_abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -229,4 +229,38 @@ mxfp4_status mxfp4_quantization_noise(const uint16_t* x, int64_t ldx, int axis, 
   return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
 }
 
+mxfp4_status mxfp4_quantize_mse_workspace_bytes(int fmt, int hadamard, int64_t R, int64_t C, int axis,
+                                                size_t* bytes) {
+  if (!fmt_ok(fmt) || (hadamard != 0 && hadamard != 1) || R < 0 || C < 0 || (axis != 0 && axis != 1) || !bytes)
+    return MXFP4_ERR_INVALID_ARG;
+  const int64_t k = axis == 1 ? C : R;
+  if (k % block_of(fmt) != 0 || (hadamard && k % 32 != 0)) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  if (R > 0 && C > kMaxElems / R) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  *bytes = mxfp4::quantize_mse_workspace_bytes(fmt, hadamard, R, C, axis);
+  return MXFP4_OK;
+}
+
+mxfp4_status mxfp4_quantize_mse(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int fmt, int hadamard,
+                                int axis, int iters, mxfp4_tensor* out, void* workspace, size_t ws_bytes,
+                                hipStream_t stream) {
+  if (!fmt_ok(fmt) || (hadamard != 0 && hadamard != 1) || (axis != 0 && axis != 1) || !out || iters < 0 ||
+      iters > 64)
+    return MXFP4_ERR_INVALID_ARG;
+  if (R < 0 || C < 0 || ldx < C || ldx < 1) return MXFP4_ERR_INVALID_ARG;
+  const int64_t rows = axis == 1 ? R : C, k = axis == 1 ? C : R;
+  if (k % block_of(fmt) != 0 || (hadamard && k % 32 != 0)) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  if (R > 0 && C > kMaxElems / R) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  if (out->fmt != fmt || out->rows != rows || out->k != k || out->hadamard != hadamard) return MXFP4_ERR_INVALID_ARG;
+  if (rows == 0 || k == 0) return MXFP4_OK;
+  if (!x || !out->codes || !out->scales || !aligned(x, 2) || !aligned(out->codes, 16)) return MXFP4_ERR_INVALID_ARG;
+  if (fmt == MXFP4_FMT_NV) {
+    if (!out->tensor_scale) return MXFP4_ERR_INVALID_ARG;
+    const size_t need = mxfp4::quantize_mse_workspace_bytes(fmt, hadamard, R, C, axis);
+    if (!workspace || ws_bytes < need || !aligned(workspace, 16)) return MXFP4_ERR_WORKSPACE;
+  }
+  hipError_t e = mxfp4::launch_quantize_mse(x, R, C, ldx, fmt, hadamard, axis, iters, out->codes, out->scales,
+                                            out->tensor_scale, workspace, stream);
+  return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
+}
+
 }  // extern "C"

@@ -49,6 +49,17 @@ hipError_t launch_gemm_nv(const uint8_t* a_codes, const uint8_t* a_scales, const
                           int64_t N, int64_t K, float* C, int64_t ldc, float* workspace, const GemmPlan& plan,
                           hipStream_t stream);
 
+// NVFP4 tensor scale of an input (amax pass + finalize) into tensor_scale;
+// partials: quantize_workspace_bytes(FMT_NV, R, C) bytes.
+void launch_tensor_scale(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int hadamard, int axis,
+                         float* tensor_scale, uint32_t* partials, hipStream_t s);
+
+// Round-to-nearest quantization with MSE-fitted scales (mse.hip).
+size_t quantize_mse_workspace_bytes(int fmt, int hadamard, int64_t R, int64_t C, int axis);
+hipError_t launch_quantize_mse(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int fmt, int hadamard,
+                               int axis, int iters, uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                               void* workspace, hipStream_t stream);
+
 // Signal and quantization-noise sums of a quantized operand (noise.hip):
 // workspace = 3 doubles per workgroup of the pass.
 size_t noise_workspace_bytes(int fmt, int hadamard, int64_t rows, int64_t K);

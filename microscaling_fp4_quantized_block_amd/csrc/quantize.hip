@@ -626,7 +626,7 @@ static void launch_had(bool had, int axis, const uint16_t* x, int64_t R, int64_t
 
 // Tensor amax of an NVFP4 input into s_t (device): partial maxima, then the
 // one-workgroup finalize.
-static void launch_tensor_scale(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int hadamard, int axis,
+void launch_tensor_scale(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int hadamard, int axis,
                                 float* tensor_scale, uint32_t* partials, hipStream_t s) {
   int64_t nparts = 0;
   if (hadamard) {

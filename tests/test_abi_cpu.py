@@ -232,3 +232,40 @@ def test_quantization_noise_workspace_bytes(mx):
     assert f(desc(mx, fmt=1, rows=10, k=48)) == (OK, 24)        # NVFP4, units of 16: one workgroup
     assert f(desc(mx, rows=0, k=0)) == (OK, 24)
     assert mx.lib.mxfp4_quantization_noise_workspace_bytes(None, ctypes.byref(b)) == INVALID
+
+
+def qmse(mx, R=64, C=256, ldx=256, fmt=0, had=0, axis=1, iters=2, out=None, ws=FAKE, wsb=1 << 20, x=FAKE):
+    if out is None:
+        rows, k = (R, C) if axis == 1 else (C, R)
+        out = desc(mx, fmt, had, rows, k)
+    return mx.lib.mxfp4_quantize_mse(x, R, C, ldx, fmt, had, axis, iters, ctypes.byref(out) if out != "null" else None,
+                                     ws, wsb, None)
+
+
+def test_quantize_mse_rejects_bad_arguments(mx):
+    assert qmse(mx, fmt=3) == INVALID
+    assert qmse(mx, had=2) == INVALID
+    assert qmse(mx, axis=2) == INVALID
+    assert qmse(mx, iters=-1) == INVALID
+    assert qmse(mx, iters=65) == INVALID
+    assert qmse(mx, out="null") == INVALID
+    assert qmse(mx, ldx=100) == INVALID
+    assert qmse(mx, C=48, ldx=48) == SHAPE                     # MX block of 32
+    assert qmse(mx, fmt=1, had=1, C=48, ldx=48) == SHAPE       # rotation needs k % 32
+    assert qmse(mx, out=desc(mx, rows=63)) == INVALID          # descriptor disagrees with the call
+    assert qmse(mx, x=None) == INVALID
+    assert qmse(mx, out=desc(mx, codes=FAKE + 4)) == INVALID   # codes 16-byte aligned
+    assert qmse(mx, fmt=1, out=desc(mx, 1, ts=None)) == INVALID
+    assert qmse(mx, fmt=1, ws=None, wsb=0) == WORKSPACE
+    assert qmse(mx, fmt=1, wsb=100) == WORKSPACE
+    assert qmse(mx, R=0, out=desc(mx, rows=0)) == OK             # empty: no-op
+
+
+def test_quantize_mse_workspace_bytes(mx):
+    assert mx.mxfp4_quantize_mse_workspace_bytes("mx", False, 64, 256) == 0
+    # NVFP4: amax partials (4096 bytes here), 16 bytes per 32-element unit (64 x 8), 16 per row
+    assert mx.mxfp4_quantize_mse_workspace_bytes("nv", False, 64, 256) == 4096 + 64 * 8 * 16 + 64 * 16
+    # units of 16 for NVFP4 without rotation on a contraction of 80
+    assert mx.mxfp4_quantize_mse_workspace_bytes("nv", False, 10, 80) == 4096 + 10 * 5 * 16 + 10 * 16
+    # axis 0: rows = C, k = R
+    assert mx.mxfp4_quantize_mse_workspace_bytes("nv", True, 256, 64, 0) == 4096 + 64 * 8 * 16 + 64 * 16
