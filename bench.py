@@ -320,6 +320,20 @@ def sweep(args):
             rows.append((cfg, "gemm", gname, f"{Mg}x{Ng}x{Kg}", t * 1e6, tf, "TFLOP/s",
                          bound + ("-fp16" if fmt == "nv" and bound == "mfma" else ""), bound_t / t))
             del C, ws
+        if cfg in (2, 3, 5):
+            # weights with MSE-fitted scales (two alternations for NVFP4)
+            for name in [n for n in tens if n.startswith("W")]:
+                x = tens[name]
+                R, Cc = x.shape
+                q = mx.empty_qtensor(fmt, R, Cc, had, dev)
+                wsb = mx.mxfp4_quantize_mse_workspace_bytes(fmt, had, R, Cc, 1)
+                ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+                t = timed(lambda: mx.mxfp4_quantize_mse(x, fmt, had, 1, 2, out=q, workspace=ws), True)
+                nbytes = R * Cc * (2.0 + 0.5 + 1.0 / bs) + (4 if fmt == "nv" else 0)
+                gbps = nbytes / t / 1e9
+                rows.append((cfg, "quantize_mse", f"{name} rtn axis1" + (" H" if had else "") + (" 2 rounds" if fmt == "nv" else ""),
+                             f"{R}x{Cc}", t * 1e6, gbps, "GB/s", "hbm", gbps / PEAK_HBM_GBPS))
+                del q, ws
         if cfg in (4, 5):
             # signal / noise sums of the stochastically rounded gradient
             # operands (one pass over x, codes and scales)
