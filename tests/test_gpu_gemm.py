@@ -198,3 +198,21 @@ def test_gemm_format_mismatch_rejected(oracle_mod):
     with pytest.raises(mx.MxFp4Error) as e:
         mx.mxfp4_gemm(qa, qh)
     assert e.value.status == -3
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [("mx", 768, 3072, 50432), ("nv", 512, 768, 8192), ("mx", 16, 14336, 4096)])
+def test_gemm_is_deterministic(fmt, M, N, K):
+    """Split-K partials are added in a fixed order and every tile's MFMA
+    sequence is fixed: two calls on the same operands give the same bits."""
+    mx = need_gpu()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(81)
+    a = (torch.randn((M, K), generator=g, device="cuda")).to(torch.bfloat16)
+    b = (torch.randn((N, K), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    qa = mx.mxfp4_quantize(a, fmt, "rtn", False, 1, 0)
+    qb = mx.mxfp4_quantize(b, fmt, "rtn", False, 1, 0)
+    say("gemm determinism", fmt, M, N, K, "ws", mx.mxfp4_gemm_workspace_bytes(qa, qb))
+    c1 = mx.mxfp4_gemm(qa, qb)
+    c2 = mx.mxfp4_gemm(qa, qb)
+    torch.cuda.synchronize()
+    assert torch.equal(c1.view(torch.int32), c2.view(torch.int32))
