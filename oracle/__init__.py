@@ -71,6 +71,8 @@ def _load():
     lib.mxo_nv_tensor_scale.argtypes = [ctypes.c_float]
     lib.mxo_quantize.restype = i32
     lib.mxo_quantize.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, u64, vp, vp, vp]
+    lib.mxo_quantize_rows_at.restype = i32
+    lib.mxo_quantize_rows_at.argtypes = [vp, i64, i64, i64, i32, i32, u64, i64, vp, vp]
     lib.mxo_dequantize.restype = i32
     lib.mxo_dequantize.argtypes = [i32, i64, i64, vp, vp, vp, vp, i64]
     lib.mxo_gemm.restype = i32
@@ -163,6 +165,21 @@ def quantize(x_bits: np.ndarray, fmt: str = "mx", rounding: str = "rtn",
     if rc != 0:
         raise ValueError("oracle quantize rejected its arguments")
     return codes, scales, (float(ts[0]) if ts is not None else None)
+
+
+def quantize_rows_at(x_bits: np.ndarray, row0: int, rounding: str = "rtn", hadamard: bool = False, seed: int = 0):
+    """MXFP4 along axis 1 for rows row0 .. of a larger tensor (given as those
+    rows only): the same codes and scales the whole tensor's quantization
+    has there.  Returns (codes, scales)."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    R, C = x.shape
+    codes = np.zeros((R, C // 2), dtype=np.uint8)
+    scales = np.zeros((R, C // 32), dtype=np.uint8)
+    rc = _load().mxo_quantize_rows_at(_ptr(x), R, C, C, ROUNDING[rounding], int(bool(hadamard)), int(seed),
+                                      int(row0), _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError("oracle quantize_rows_at rejected its arguments")
+    return codes, scales
 
 
 def dequantize(fmt: str, codes: np.ndarray, scales: np.ndarray, tensor_scale=None) -> np.ndarray:

@@ -255,9 +255,12 @@ float mxo_nv_tensor_scale(float amax_t)
     return st < floor_st ? floor_st : st;
 }
 
-int mxo_quantize(const uint16_t *x, int64_t R, int64_t C, int64_t ldx,
-                 int fmt, int rounding, int hadamard, int axis, uint64_t seed,
-                 uint8_t *codes, uint8_t *scales, float *tensor_scale)
+/* l0: stream index of the operand's element (0, 0); 0 for a whole tensor
+ * (mxo_quantize), row0 * K for rows row0.. of a larger MXFP4 tensor
+ * quantized along axis 1 (mxo_quantize_rows_at). */
+static int quantize_impl(const uint16_t *x, int64_t R, int64_t C, int64_t ldx,
+                         int fmt, int rounding, int hadamard, int axis, uint64_t seed,
+                         uint64_t l0, uint8_t *codes, uint8_t *scales, float *tensor_scale)
 {
     if (!x || !codes || !scales || R < 0 || C < 0 || ldx < C) return -1;
     if (fmt != FMT_MX && fmt != FMT_NV) return -1;
@@ -350,7 +353,7 @@ int mxo_quantize(const uint16_t *x, int64_t R, int64_t C, int64_t ldx,
                         if (rounding == RND_RTN)
                             code = mxo_rtn_code(xs);
                         else
-                            code = mxo_sr_code(xs, mxo_rnd16(seed, (uint64_t)(i * K + k), axis));
+                            code = mxo_sr_code(xs, mxo_rnd16(seed, l0 + (uint64_t)(i * K + k), axis));
                     }
                     uint8_t *byte = &codes[i * (K / 2) + k / 2];
                     if ((k & 1) == 0) *byte = (uint8_t)((*byte & 0xF0) | code);
@@ -361,6 +364,24 @@ int mxo_quantize(const uint16_t *x, int64_t R, int64_t C, int64_t ldx,
         free(v);
     }
     return 0;
+}
+
+int mxo_quantize(const uint16_t *x, int64_t R, int64_t C, int64_t ldx,
+                 int fmt, int rounding, int hadamard, int axis, uint64_t seed,
+                 uint8_t *codes, uint8_t *scales, float *tensor_scale)
+{
+    return quantize_impl(x, R, C, ldx, fmt, rounding, hadamard, axis, seed, 0, codes, scales, tensor_scale);
+}
+
+/* Rows row0 .. row0 + R - 1 of a larger tensor, MXFP4 along axis 1: every
+ * block lies in one row, so only the stochastic-rounding stream index needs
+ * the offset (NVFP4 would need the whole tensor's amax, and is refused). */
+int mxo_quantize_rows_at(const uint16_t *x, int64_t R, int64_t C, int64_t ldx, int rounding, int hadamard,
+                         uint64_t seed, int64_t row0, uint8_t *codes, uint8_t *scales)
+{
+    if (row0 < 0) return -1;
+    return quantize_impl(x, R, C, ldx, FMT_MX, rounding, hadamard, 1, seed, (uint64_t)row0 * (uint64_t)C,
+                         codes, scales, NULL);
 }
 
 /* ------------------------------------------------------------------ */

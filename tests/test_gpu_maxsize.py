@@ -1,0 +1,62 @@
+"""Maximum sizes: a row-quantized tensor of more than 2^32 chunks of 8
+elements (68.7 GB of bf16: the launch is cut into slices below 2^31 chunks,
+and the stochastic-rounding counter crosses 2^32), and a transposed
+quantization with more than 65535 tiles of 256 rows (the grid is cut into
+slabs).  Checked against the oracle on rows sampled at every boundary (the
+first), or in full (the second)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import need_gpu, say, q_to_host, assert_codes_equal
+
+pytestmark = pytest.mark.gpu
+
+
+def _fill_normal(x, seed, rows_per_slab=1 << 16, std=1.0):
+    g = torch.Generator(device=x.device)
+    g.manual_seed(seed)
+    for r0 in range(0, x.shape[0], rows_per_slab):
+        r1 = min(r0 + rows_per_slab, x.shape[0])
+        x[r0:r1] = (torch.randn((r1 - r0, x.shape[1]), generator=g, device=x.device) * std).to(torch.bfloat16)
+
+
+def _bits(t):
+    return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def test_rows_beyond_2_to_the_32_chunks(oracle_mod):
+    mx = need_gpu()
+    R, C = (1 << 22) + 1, 8192            # R * C / 8 = 2^32 + 1024 chunks
+    free, _ = torch.cuda.mem_get_info()
+    if free < 100 * (1 << 30):
+        pytest.skip("needs about 90 GB of device memory")
+    say("max size rows", R, C)
+    x = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
+    _fill_normal(x, 93)
+    q = mx.mxfp4_quantize(x, "mx", "sr", False, 1, 77)
+    torch.cuda.synchronize()
+    # rows at the slice boundaries (2^30 chunks = 2^20 rows) and where the
+    # chunk counter passes 2^31 and 2^32
+    for r in (0, 1, (1 << 20) - 1, 1 << 20, (1 << 21) - 1, 1 << 21, (1 << 22) - 1, 1 << 22):
+        xr = _bits(x[r:r + 1])
+        want = oracle_mod.quantize_rows_at(xr, r, "sr", False, 77)
+        got = (q.codes[r:r + 1].cpu().numpy(), q.scales[r:r + 1].cpu().numpy(), None)
+        assert_codes_equal(got, (want[0], want[1], None), f"max-size row {r}")
+    del x, q
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt,rnd", [("mx", "rtn"), ("nv", "sr")])
+def test_transposed_beyond_65535_row_tiles(oracle_mod, fmt, rnd):
+    mx = need_gpu()
+    R, C = 65538 * 256, 64                 # 65538 tiles of 256 rows along the contraction
+    say("max size transposed", fmt, rnd, R, C)
+    x = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
+    _fill_normal(x, 94, std=0.5)
+    q = mx.mxfp4_quantize(x, fmt, rnd, False, 0, 5)
+    got = q_to_host(q)
+    X = _bits(x)
+    del x, q
+    torch.cuda.empty_cache()
+    assert_codes_equal(got, oracle_mod.quantize(X, fmt, rnd, False, 0, 5), f"max-size transposed {fmt}")

@@ -260,3 +260,16 @@ def test_sr_stream_follows_the_stated_counter_layout(oracle_mod, axis):
             xs = v[i, k] / 2.0 ** e
             expect = oracle_mod.sr_code(xs, oracle_mod.rnd16(seed, i * K + k, axis))
             assert c[i, k] == expect, (i, k)
+
+
+def test_rows_at_equals_the_whole_tensor():
+    """quantize_rows_at (used to check samples of very large tensors) gives
+    exactly the whole tensor's codes and scales on those rows, stochastic
+    rounding stream included."""
+    import oracle
+    x = workloads.small_t_bf16((64, 512), 3.0, seed=91)
+    for rnd, had in (("sr", False), ("sr", True), ("rtn", True)):
+        full = oracle.quantize(x, "mx", rnd, had, 1, 12)
+        for r0, r1 in ((0, 5), (17, 40), (63, 64)):
+            part = oracle.quantize_rows_at(x[r0:r1], r0, rnd, had, 12)
+            assert np.array_equal(full[0][r0:r1], part[0]) and np.array_equal(full[1][r0:r1], part[1])
