@@ -133,8 +133,8 @@ mxfp4_status mxfp4_gemm_workspace_bytes(const mxfp4_tensor *A, const mxfp4_tenso
  * FP4 matrix cores; NVFP4 dequantizes exactly to fp16 in registers (an
  * E2M1 x E4M3 product has at most 6 significant bits) for the fp16 matrix
  * cores and applies both tensor scales in the epilogue.
- * C: device, row-major, ldc >= N.  k must be a multiple of 128
- * (UNSUPPORTED_SHAPE otherwise); fmt, k and hadamard of A and B must agree
+ * C: device, row-major, ldc >= N.  k must be a multiple of 128 and at most
+ * 2^24 (UNSUPPORTED_SHAPE otherwise); fmt, k and hadamard of A and B must agree
  * (FORMAT_MISMATCH).  A->codes and B->codes must be 16-byte aligned and the
  * scales 4-byte aligned (INVALID_ARG otherwise).
  * workspace: device, at least mxfp4_gemm_workspace_bytes (NULL if 0). */
@@ -166,8 +166,8 @@ mxfp4_status mxfp4_quantize_gemm_workspace_bytes(int64_t M, int64_t K, int hadam
  * x: device, bf16 bit patterns [M, K], row-major, leading dimension ldx >= K.
  * B: the pre-quantized weights [N, K] (MXFP4, B->k == K and B->hadamard ==
  *    hadamard, else FORMAT_MISMATCH); B->codes 16-byte and B->scales 4-byte
- *    aligned (INVALID_ARG otherwise).  K must be a multiple of 128
- *    (UNSUPPORTED_SHAPE).
+ *    aligned (INVALID_ARG otherwise).  K must be a multiple of 128 and at
+ *    most 2^24 (UNSUPPORTED_SHAPE).
  * C: device, FP32, row-major, ldc >= N.
  * workspace: device, 16-byte aligned, at least
  *    mxfp4_quantize_gemm_workspace_bytes (NULL if that is 0). */

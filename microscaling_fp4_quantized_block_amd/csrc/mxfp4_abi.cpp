@@ -19,6 +19,10 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 // index math is exact well beyond any tensor that fits in device memory.
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
 
+// Longest GEMM contraction: a 256-row tile of operand codes (256 * K/2 bytes)
+// stays within the 2^31-byte range of a buffer resource.
+constexpr int64_t kMaxGemmK = (int64_t)1 << 24;
+
 }  // namespace
 
 extern "C" {
@@ -95,6 +99,8 @@ static mxfp4_status check_gemm_operands(const mxfp4_tensor* A, const mxfp4_tenso
   if (A->fmt != B->fmt || A->k != B->k || A->hadamard != B->hadamard) return MXFP4_ERR_FORMAT_MISMATCH;
   // the kernels' contraction step is 128 (one 64-byte chunk of codes per row)
   if (A->k % 128 != 0) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  // a tile's operand rows are addressed through 32-bit buffer offsets
+  if (A->k > kMaxGemmK) return MXFP4_ERR_UNSUPPORTED_SHAPE;
   return MXFP4_OK;
 }
 
@@ -139,7 +145,7 @@ static mxfp4_status check_quantize_gemm(int64_t M, int64_t K, int hadamard, cons
   if (!B || M < 0 || K < 0 || B->rows < 0 || B->k < 0 || (hadamard != 0 && hadamard != 1) || !fmt_ok(B->fmt))
     return MXFP4_ERR_INVALID_ARG;
   if (B->fmt != MXFP4_FMT_MX || B->k != K || B->hadamard != hadamard) return MXFP4_ERR_FORMAT_MISMATCH;
-  if (K % 128 != 0) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  if (K % 128 != 0 || K > kMaxGemmK) return MXFP4_ERR_UNSUPPORTED_SHAPE;
   if (M > 0 && K > kMaxElems / M) return MXFP4_ERR_UNSUPPORTED_SHAPE;
   return MXFP4_OK;
 }

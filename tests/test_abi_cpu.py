@@ -124,6 +124,7 @@ def test_gemm_rejects_bad_arguments(mx):
     assert g(a, desc(mx, rows=32, k=512)) == MISMATCH
     assert g(a, desc(mx, had=1, rows=32)) == MISMATCH
     assert g(desc(mx, k=96), desc(mx, rows=32, k=96)) == SHAPE     # MX needs k % 128
+    assert g(desc(mx, k=(1 << 24) + 128), desc(mx, rows=32, k=(1 << 24) + 128)) == SHAPE   # longest contraction
     assert g(a, b, ldc=16) == INVALID
     assert g(a, b, C=None) == INVALID
     assert g(desc(mx, codes=FAKE + 8), b) == INVALID              # operand codes must be 16-byte aligned
@@ -171,6 +172,7 @@ def test_quantize_gemm_rejects_bad_arguments(mx):
     assert qgemm(mx, B=desc(mx, rows=64, k=512)) == MISMATCH            # contraction lengths differ
     assert qgemm(mx, had=1, B=desc(mx, had=0, rows=64)) == MISMATCH     # rotation must match the weights'
     assert qgemm(mx, K=96, ldx=96, B=desc(mx, rows=64, k=96)) == SHAPE  # k % 128
+    assert qgemm(mx, K=(1 << 24) + 128, ldx=(1 << 24) + 128, B=desc(mx, rows=64, k=(1 << 24) + 128)) == SHAPE
     assert qgemm(mx, ldx=100) == INVALID                                 # ldx < K
     assert qgemm(mx, ldc=63) == INVALID                                  # ldc < N
     assert qgemm(mx, x=None) == INVALID

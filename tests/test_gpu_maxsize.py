@@ -2,8 +2,9 @@
 elements (68.7 GB of bf16: the launch is cut into slices below 2^31 chunks,
 and the stochastic-rounding counter crosses 2^32), and a transposed
 quantization with more than 65535 tiles of 256 rows (the grid is cut into
-slabs).  Checked against the oracle on rows sampled at every boundary (the
-first), or in full (the second)."""
+slabs), both checked against the oracle (on rows sampled at every boundary,
+or in full); and GEMMs over the longest contraction the library takes
+(2^24), checked on sampled outputs."""
 import numpy as np
 import pytest
 import torch
@@ -60,3 +61,32 @@ def test_transposed_beyond_65535_row_tiles(oracle_mod, fmt, rnd):
     del x, q
     torch.cuda.empty_cache()
     assert_codes_equal(got, oracle_mod.quantize(X, fmt, rnd, False, 0, 5), f"max-size transposed {fmt}")
+
+
+@pytest.mark.parametrize("fmt,M,N", [("mx", 33, 300), ("mx", 300, 256), ("nv", 40, 260)])
+def test_gemm_longest_contraction(oracle_mod, fmt, M, N):
+    """K = 2^24, the longest contraction the GEMM takes (narrow and wide MXFP4
+    tiles, NVFP4), split along K; sampled outputs against the oracle."""
+    mx = need_gpu()
+    K = 1 << 24
+    say("max size gemm", fmt, M, N, K)
+    a = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    b = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    _fill_normal(a, 95, rows_per_slab=16)
+    _fill_normal(b, 96, rows_per_slab=16, std=0.02)
+    qa = mx.mxfp4_quantize(a, fmt, "rtn", False, 1, 0)
+    qb = mx.mxfp4_quantize(b, fmt, "rtn", False, 1, 0)
+    del a, b
+    assert mx.mxfp4_gemm_workspace_bytes(qa, qb) > 0
+    C = mx.mxfp4_gemm(qa, qb).cpu().numpy()
+    rows = np.array([0, M // 2, M - 1])
+    cols = np.array([0, N // 3, N - 1])
+    ta = float(qa.tensor_scale.cpu()[0]) if fmt == "nv" else None
+    tb = float(qb.tensor_scale.cpu()[0]) if fmt == "nv" else None
+    oa = (qa.codes[torch.from_numpy(rows).cuda()].cpu().numpy(), qa.scales[torch.from_numpy(rows).cuda()].cpu().numpy(), ta)
+    ob = (qb.codes[torch.from_numpy(cols).cuda()].cpu().numpy(), qb.scales[torch.from_numpy(cols).cuda()].cpu().numpy(), tb)
+    del qa, qb
+    torch.cuda.empty_cache()
+    Co, So = oracle_mod.gemm(fmt, oa, ob)
+    err = np.abs(C[np.ix_(rows, cols)].astype(np.float64) - Co)
+    assert np.all(err <= 1e-5 * So), (err, So)
