@@ -142,7 +142,9 @@ def cpu_baseline():
     os.environ.setdefault("OMP_NUM_THREADS", str(len(os.sched_getaffinity(0))))
     cores = int(os.environ["OMP_NUM_THREADS"])       # threads the OpenMP oracle runs with
     oracle._load()
-    qa_rows, qb_rows, g_rows, g_cols = 1024, 4096, 512, 4096
+    # about 10-15 s of oracle work on 16 cores: both quantizations whole, and
+    # 4096 x 8192 of the 4096 x 14336 GEMM outputs
+    qa_rows, qb_rows, g_rows, g_cols = M, N, 4096, 8192
     A = workloads.make_tensor(0, "A", rows=qa_rows)
     B = workloads.make_tensor(0, "B", rows=qb_rows)
     t0 = time.perf_counter()
