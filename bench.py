@@ -52,6 +52,11 @@ def parse():
                          "rooflines and write a markdown table (to stdout with no file)")
     ap.add_argument("--sweep-reps", type=int, default=10)
     ap.add_argument("--sweep-configs", default="1,2,3,4,5,0", help="comma-separated configurations to sweep")
+    ap.add_argument("--quant-profile", action="store_true",
+                    help="run a fixed list of quantizer calls (3 each, the MALL evicted before each) for "
+                         "rocprofv3 kernel-trace and PMC runs")
+    ap.add_argument("--summarize-quant", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "TRACE_DIR", "OUT_MD"),
+                    help="per-kernel HBM traffic and achieved GB/s of the --quant-profile runs")
     return ap.parse_args()
 
 
@@ -121,6 +126,93 @@ def summarize_pmc(fetch_dir, write_dir, out_path):
                 "scaled by a 1 GiB copy; commands in profiles/README.md)\n")
         f.write(json.dumps(d, indent=1) + "\n")
     print(json.dumps(d, indent=1))
+
+
+# The quantizer calls --quant-profile makes: (label, config, tensor, fmt, rounding, hadamard, axis).
+QUANT_PROFILE_CALLS = [
+    ("headline A", 0, "A", "mx", "rtn", False, 1),
+    ("headline B", 0, "B", "mx", "rtn", False, 1),
+    ("config 3 W_down (rotated)", 3, "W_down", "mx", "rtn", True, 1),
+    ("config 2 X (NVFP4)", 2, "X", "nv", "rtn", False, 1),
+    ("config 4 dY1 SR rows", 4, "dY1", "mx", "sr", False, 1),
+    ("config 4 dY1 SR transposed", 4, "dY1", "mx", "sr", False, 0),
+]
+
+
+def quant_profile():
+    """The calls of QUANT_PROFILE_CALLS, 3 times each, each after a 512 MiB
+    write that evicts the MALL (device-drawn inputs with the configurations'
+    shapes; the distributions do not change the traffic)."""
+    import torch
+    import workloads
+    import microscaling_fp4_quantized_block_amd as mx
+    dev = torch.device("cuda", 0)
+    evict = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    for label, cfg, name, fmt, rnd, had, axis in QUANT_PROFILE_CALLS:
+        shape = workloads.CONFIGS[cfg]["tensors"][name][0]
+        x = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+        R, C = shape
+        q = mx.empty_qtensor(fmt, R if axis == 1 else C, C if axis == 1 else R, had, dev)
+        ws = torch.empty(max(mx.mxfp4_quantize_workspace_bytes(fmt, R, C, axis), 4), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            evict.fill_(1.0)
+            mx.mxfp4_quantize(x, fmt, rnd, had, axis, 3, out=q, workspace=ws)
+        torch.cuda.synchronize()
+        print(f"[quant-profile] {label}: {fmt} {rnd} axis {axis} {R}x{C}", flush=True)
+        del x, q, ws
+
+
+def _dispatches(run_dir, counter=None):
+    """Our kernels' dispatches of a rocprofv3 csv run in order: (name, value)
+    with value = the counter (summed over its instances) or the duration."""
+    import csv
+    import glob
+    out = {}
+    pattern = "*counter_collection.csv" if counter else "*kernel_trace.csv"
+    for path in glob.glob(os.path.join(run_dir, "**", pattern), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"]
+                if counter is not None and r["Counter_Name"] != counter:
+                    continue
+                key = int(r.get("Dispatch_Id") or r.get("Correlation_Id") or 0)
+                val = float(r["Counter_Value"]) if counter else (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+                if key in out:
+                    out[key] = (name, out[key][1] + val if counter else val)
+                else:
+                    out[key] = (name, val)
+    return [out[k] for k in sorted(out)]
+
+
+def summarize_quant(fetch_dir, write_dir, trace_dir, out_md):
+    fetch, write, trace = _dispatches(fetch_dir, "FETCH_SIZE"), _dispatches(write_dir, "WRITE_SIZE"), _dispatches(trace_dir)
+    is_copy = lambda k: "elementwise" in k.lower() and "fill" not in k.lower()
+    f_scale = COPY_BYTES / max(v for k, v in fetch if is_copy(k))
+    w_scale = COPY_BYTES / max(v for k, v in write if is_copy(k))
+    ours = lambda lst: [(k, v) for k, v in lst if "mxfp4::" in k]
+    fetch, write, trace = ours(fetch), ours(write), ours(trace)
+    assert len(fetch) == len(write) == len(trace), (len(fetch), len(write), len(trace))
+    # consecutive dispatches per call: 3 repetitions of one launcher's kernels
+    rows, i = [], 0
+    for label, cfg, name, fmt, rnd, had, axis in QUANT_PROFILE_CALLS:
+        per_call = 3 if fmt == "nv" else 1
+        for j in range(per_call):
+            idx = [i + rep * per_call + j for rep in range(3)]
+            kname = trace[idx[0]][0]
+            t = sorted(trace[q][1] for q in idx)[1]
+            fb = sum(fetch[q][1] for q in idx) / 3 * f_scale
+            wb = sum(write[q][1] for q in idx) / 3 * w_scale
+            short = kname.replace("void ", "").replace("mxfp4::", "").split("(")[0]
+            rows.append((label, short, t * 1e6, fb / 1e6, wb / 1e6, (fb + wb) / t / 1e9))
+        i += 3 * per_call
+    with open(out_md, "w") as f:
+        f.write("| call | kernel | us (median of 3) | fetched MB | written MB | actual GB/s | % of 8 TB/s |\n"
+                "|---|---|---|---|---|---|---|\n")
+        for r in rows:
+            f.write("| %s | %s | %.1f | %.1f | %.1f | %.0f | %.1f |\n" % (r + (r[5] / PEAK_HBM_GBPS * 100,)))
+    print(open(out_md).read())
 
 
 def summarize_stats(stats_csv, out_md):
@@ -403,6 +495,9 @@ def main():
     if args.summarize_stats:
         summarize_stats(*args.summarize_stats)
         return
+    if args.summarize_quant:
+        summarize_quant(*args.summarize_quant)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs on a single "
               "MI355X; see the sharding note in DESIGN.md)", file=sys.stderr)
@@ -422,6 +517,9 @@ def main():
         torch.mul(src, 1.0, out=dst)          # one elementwise kernel: reads and writes COPY_BYTES
         torch.cuda.synchronize()
         del src, dst, evict
+    if args.quant_profile:
+        quant_profile()
+        return
     A_bits = workloads.make_tensor(0, "A")
     B_bits = workloads.make_tensor(0, "B")
     A = torch.from_numpy(A_bits.view(np.int16)).view(torch.bfloat16).to(dev)
