@@ -216,22 +216,39 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 }
 
 // ---------------------------------------------------------------------------
-// Stochastic rounding of one scaled element xs to a 4-bit code.
-// a = min(|xs|, 6); for a >= 1 the E2M1 neighbours below a are the binary32
-// value truncated to one mantissa bit, and the position between the two
-// neighbours is the remaining 22 mantissa bits: t = bits[21:6] =
-// floor(frac * 2^16), low code = (bits >> 22) - 252.  For a < 1 the grid step
-// is 1/2: q = floor(a * 2^17) (exact), low code = q >> 16, t = q & 0xFFFF.
-// Round up iff rnd16 < t.  The sign bit is the input's.
+// Stochastic rounding of 8 scaled elements xs[j] to 4-bit codes, element j
+// drawing the 16-bit value r_j = bits 16(j&1)..+15 of rw[j/2].
+//
+// Definition: a = min(|xs|, 6) lies between E2M1 neighbours lo <= a < hi;
+// with t = floor(2^16 (a - lo) / (hi - lo)) the code rounds up iff r_j < t,
+// and carries the input's sign bit (also for a zero result).
+//
+// gfx950's v_cvt_scalef32_sr_pk_fp4_f32 rounds the element in its first slot
+// up iff (a - lo) / (hi - lo) + rnd * 2^-32 >= 1, saturating at 6 and keeping
+// the sign bit (measured on every 16-bit draw at each threshold and one ulp
+// either side in every binade, plus zeros, denormals and saturation).  With
+// rnd = (65535 - r) * 2^16 that is frac + (65535 - r) / 2^16 >= 1, i.e.
+// floor(2^16 frac) >= r + 1: exactly the definition.  The second slot draws
+// from rnd shifted left by one, so two independent 16-bit draws cannot share
+// one call; each element gets its own call with 0 in the second slot (code 0
+// in the byte's high nibble).  Only byte 0 of the result is defined with
+// sel = 0 (the compiler does not carry the old value into the other bytes),
+// so the byte-0 codes are gathered with v_perm_b32.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t sr_code(float xs, uint32_t rnd16) {
-  const uint32_t sign = (__float_as_uint(xs) >> 28) & 8u;
-  const float a = __builtin_fminf(__builtin_fabsf(xs), 6.0f);
-  const uint32_t ab = __float_as_uint(a);
-  // fixed point: low code in bits 16 and up, t in bits 0..15 (for a >= 1,
-  // (ab - 252 * 2^22) >> 6 puts (ab >> 22) - 252 above bits [21:6] of ab)
-  const uint32_t x = (a >= 1.0f) ? ((ab - (252u << 22)) >> 6) : (uint32_t)(a * 131072.0f);
-  return sign | ((x >> 16) + (rnd16 < (x & 0xFFFFu) ? 1u : 0u));
+__device__ __forceinline__ uint32_t sr_encode8(const float xs[8], const uint32_t rw[4]) {
+  uint32_t c[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const uint32_t w = rw[j >> 1];
+    // (65535 - r) << 16 for r in the low or the high half of w
+    const uint32_t rnd = (j & 1) ? (~w & 0xFFFF0000u) : ((w << 16) ^ 0xFFFF0000u);
+    c[j] = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, (f32x2){xs[j], 0.0f}, rnd, 1.0f, 0);
+  }
+  // v_perm_b32 selector bytes: 0..3 pick bytes of the second operand, 4..7 of
+  // the first, 0x0C gives zero
+  const uint32_t even = __builtin_amdgcn_perm(c[2], c[0], 0x0C0C0400u) | __builtin_amdgcn_perm(c[6], c[4], 0x04000C0Cu);
+  const uint32_t odd = __builtin_amdgcn_perm(c[3], c[1], 0x0C0C0400u) | __builtin_amdgcn_perm(c[7], c[5], 0x04000C0Cu);
+  return even | (odd << 4);
 }
 
 }  // namespace mxfp4

@@ -97,7 +97,8 @@ __device__ __forceinline__ void nv_block_scale(float amax, float st, uint32_t& b
 //              saturating); bf16 inputs go in directly as packed pairs.
 //   NVFP4:     x' = RN(y * inv) (+-0 for a zero scale), then RTN (conversion
 //              with unit scale) or SR.
-//   SR:        16 bits per element from the lane's Philox block rw.
+//   SR:        16 bits per element from the lane's Philox block rw, rounded
+//              by the hardware stochastic FP4 conversion (sr_encode8).
 // ---------------------------------------------------------------------------
 template <int FMT, int RND, bool BF16IN>
 __device__ __forceinline__ uint32_t encode8(const float y[8], const uint32_t w[4], uint32_t byte, float mul,
@@ -130,11 +131,7 @@ __device__ __forceinline__ uint32_t encode8(const float y[8], const uint32_t w[4
     packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, xs[4], xs[5], 1.0f, 2);
     packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, xs[6], xs[7], 1.0f, 3);
   } else {
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const uint32_t rnd = (rw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-      packed |= sr_code(xs[j], rnd) << (4 * j);
-    }
+    packed = sr_encode8(xs, rw);
   }
   return packed;
 }
