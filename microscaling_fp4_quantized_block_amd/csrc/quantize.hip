@@ -398,19 +398,20 @@ __global__ void __launch_bounds__(256) quant_cols_tile_kernel(ColArgs a) {
   const int w = tid >> 6, l = tid & 63;
   const int64_t c = c0 + l;
   const int64_t rw0 = r0 + 64 * w;                  // first contraction index of this wave
-  if (rw0 >= R || c >= C) return;
+  const bool active = rw0 < R && c < C;
   // two halves of 32 rows (one MXFP4 block, two NVFP4 blocks); R is a
   // multiple of the block, so a half is whole, half-filled (NVFP4) or empty
-#pragma unroll 1
+  uint32_t out[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+  uint32_t sbyte[2][32 / BS] = {};
+#pragma unroll
   for (int h = 0; h < 2; h++) {
     const int64_t rh = rw0 + 32 * h;
-    if (rh >= R) break;
+    if (!active || rh >= R) break;
     const int nrows = (R - rh) >= 32 ? 32 : (int)(R - rh);
     float y[32];
 #pragma unroll
     for (int j = 0; j < 32; j++) y[j] = __uint_as_float((uint32_t)tile[(64 * w + 32 * h + j) * 64 + l] << 16);
     if (HAD) fwht32_inlane(y);
-    uint32_t out[4];
 #pragma unroll
     for (int b = 0; b < 32 / BS; b++) {
       uint32_t m = 0;
@@ -430,19 +431,54 @@ __global__ void __launch_bounds__(256) quant_cols_tile_kernel(ColArgs a) {
           rw[0] = r.x; rw[1] = r.y; rw[2] = r.z; rw[3] = r.w;
         }
         const uint32_t dummy[4] = {0, 0, 0, 0};
-        out[e0 / 8] = nonfinite ? 0u : encode8<FMT, RND, false>(y + e0, dummy, byte, mul, rw);
+        out[h][e0 / 8] = nonfinite ? 0u : encode8<FMT, RND, false>(y + e0, dummy, byte, mul, rw);
       }
-      if (b * BS < nrows) a.scales[c * (R / BS) + rh / BS + b] = (uint8_t)byte;
+      sbyte[h][b] = byte;
     }
-    // plain stores: each lane writes part of a different output row, and the
-    // workgroup's four waves complete those lines in L2 (streaming stores of
-    // partial lines cost several times more here)
-    uint8_t* dst = a.codes + c * (R / 2) + rh / 2;
-    if (nrows == 32 && (R % 32) == 0) {
-      *(uint4*)dst = make_uint4(out[0], out[1], out[2], out[3]);
+  }
+  // The workgroup's codes form 64 output rows (columns c0..c0+63) of 128
+  // contiguous bytes (contraction rows r0..r0+255), its scales 64 rows of
+  // 256 / BS bytes.  Written straight from the lanes, every store of a wave
+  // would touch 64 different lines; staged through LDS (the tile buffer, once
+  // every wave has read it; code rows padded to 144 bytes and scale rows to
+  // 20 so the lanes' accesses spread over the banks), each wave store of codes
+  // writes eight whole 128-byte row segments and consecutive lanes write
+  // consecutive scale bytes.
+  constexpr int NSB = 256 / BS;                     // scale bytes per output row
+  uint8_t* const stage = (uint8_t*)tile;
+  uint8_t* const stage_s = stage + 64 * 144;
+  __syncthreads();
+  if (active) {
+    *(u32v4*)(stage + l * 144 + 32 * w) = (u32v4){out[0][0], out[0][1], out[0][2], out[0][3]};
+#pragma unroll
+    for (int b = 0; b < 32 / BS; b++) stage_s[l * 20 + (64 * w) / BS + b] = (uint8_t)sbyte[0][b];
+    if (rw0 + 32 < R) {
+      *(u32v4*)(stage + l * 144 + 32 * w + 16) = (u32v4){out[1][0], out[1][1], out[1][2], out[1][3]};
+#pragma unroll
+      for (int b = 0; b < 32 / BS; b++) stage_s[l * 20 + (64 * w + 32) / BS + b] = (uint8_t)sbyte[1][b];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NSB / 4; i++) {
+    const int q = tid + 256 * i;
+    const int row = q / NSB, col = q % NSB;
+    const int64_t cc = c0 + row, rb = r0 / BS + col;  // output row, block index
+    if (cc < C && rb * BS < R) a.scales[cc * (R / BS) + rb] = stage_s[row * 20 + col];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int q = tid + 256 * i;
+    const int row = q >> 3, ch = q & 7;
+    const int64_t cc = c0 + row, rr = r0 + 32 * ch;    // output row, first contraction index
+    if (cc >= C || rr >= R) continue;
+    const u32v4 v = *(const u32v4*)(stage + row * 144 + 16 * ch);
+    uint8_t* dst = a.codes + cc * (R / 2) + rr / 2;
+    if ((R - rr) >= 32 && (R % 32) == 0) {
+      __builtin_nontemporal_store(v, (u32v4*)dst);
     } else {
-      *(uint2*)dst = make_uint2(out[0], out[1]);
-      if (nrows == 32) *(uint2*)(dst + 8) = make_uint2(out[2], out[3]);
+      *(uint2*)dst = make_uint2(v[0], v[1]);
+      if ((R - rr) >= 32) *(uint2*)(dst + 8) = make_uint2(v[2], v[3]);
     }
   }
 }
