@@ -230,62 +230,43 @@ __device__ __forceinline__ void block_barrier() {
 
 // Epilogue of a wave's TM x TN grid of 32x32 fp32 accumulators whose top-left
 // output is (mb, nb).  In an accumulator, lane l holds column l % 32 and rows
-// 8 (v / 4) + 4 (l / 32) + v % 4 (v = 0..15): four consecutive rows of one
-// column per group of four registers.  A 4x4 transpose across each quad of
-// lanes (two DPP exchange steps) turns that into one row and four consecutive
-// columns per lane, written with one 16-byte store: a quarter of the store
-// instructions, each covering whole 128-byte row segments.  Ragged edges and
-// unaligned outputs use 4-byte stores.
-__device__ __forceinline__ float dpp_xor1_f(float v) {
-  return __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)__float_as_uint(v), 0xB1, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float dpp_xor2_f(float v) {
-  return __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)__float_as_uint(v), 0x4E, 0xF, 0xF, true));
-}
-
+// 8 (v / 4) + 4 (l / 32) + v % 4 (v = 0..15), so one register across the wave
+// is two rows of 32 consecutive columns: a 4-byte store per register writes
+// two whole 128-byte row segments, straight from the accumulator.  (A 4x4
+// transpose across lane quads into 16-byte stores, a quarter of the store
+// instructions, measured 4-12 % slower: its DPP exchanges need every value in
+// a VGPR.)  Whole blocks inside C store without checks; ragged edges check
+// each element.
+//
 // Every value is multiplied by mul (the NVFP4 tensor scales) when SCALED.
-// The 16-byte stores are non-temporal: C is not read again here, and on
-// store-bound shapes (short contractions) streaming stores run ~10 % faster
-// (measured; every wave instruction writes whole 128-byte row segments).
-template <int TM, int TN, bool SCALED = false>
-__device__ __forceinline__ void store_tile_f32x4(const GemmArgs& p, float* Cz, int64_t mb, int64_t nb,
-                                                 const v16f (&acc)[TM][TN], float mul = 1.0f) {
-  typedef float f32v4 __attribute__((ext_vector_type(4)));
-  const int l = threadIdx.x & 63, g = l >> 5, c = l & 3;
-  const bool vec_ok = ((p.ldc & 3) == 0) && ((((uintptr_t)Cz) & 15) == 0);
+// The stores of C are non-temporal: C is not read again here, and on
+// store-bound shapes (short contractions) streaming stores run ~10-18 % faster
+// (measured).  Split-K partials (PARTIAL) are re-read by the reduction right
+// after, so they are written with plain stores (~7 % faster on a 3072 x 768 x
+// 50432 wgrad, ~12 % on a 16 x 4096 x 14336 decode).  The choice is a kernel
+// template parameter: two epilogues in one kernel cost the wide kernel ~35 %.
+template <int TM, int TN, bool SCALED, bool PARTIAL>
+__device__ __forceinline__ void store_tile_f32(const GemmArgs& p, float* Cz, int64_t mb, int64_t nb,
+                                               const v16f (&acc)[TM][TN], float mul = 1.0f) {
+  const int l = threadIdx.x & 63, g = l >> 5;
+  const int64_t ldc = p.ldc;
+  const bool full = mb + 32 * TM <= p.M && nb + 32 * TN <= p.N;
+  // this lane's column and its first row (4g) in the block
+  float* const lane0 = Cz + (mb + 4 * g) * ldc + nb + (l & 31);
 #pragma unroll
   for (int tm = 0; tm < TM; tm++) {
 #pragma unroll
-    for (int tn = 0; tn < TN; tn++) {
-      const int64_t ncol0 = nb + tn * 32 + (l & 31);          // this lane's column before the transpose
-      const int64_t nq = nb + tn * 32 + (l & 28);             // first column of the lane's quad
+    for (int a = 0; a < 4; a++) {
 #pragma unroll
-      for (int a = 0; a < 4; a++) {
-        float x[4], z[4], y[4];
+      for (int b = 0; b < 4; b++) {
+        const int r = tm * 32 + 8 * a + b;                      // row in the block, less 4g
+        float* const rp = lane0 + (int64_t)r * ldc;
 #pragma unroll
-        for (int b = 0; b < 4; b++) x[b] = SCALED ? acc[tm][tn][4 * a + b] * mul : acc[tm][tn][4 * a + b];
-        // stage 1: keep x[k] where k and c agree in bit 0, else take the partner lane's x[k ^ 1]
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-          const float o = dpp_xor1_f(x[k ^ 1]);
-          z[k] = ((k ^ c) & 1) ? o : x[k];
-        }
-        // stage 2: the same on bit 1 with the lane two apart
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-          const float o = dpp_xor2_f(z[k ^ 2]);
-          y[k] = ((k ^ c) & 2) ? o : z[k];
-        }
-        // lane c of the quad now holds row 8a + 4g + c, columns nq .. nq+3
-        const int64_t m = mb + tm * 32 + 8 * a + 4 * g + c;
-        if (vec_ok && nq + 3 < p.N) {
-          if (m < p.M) __builtin_nontemporal_store((f32v4){y[0], y[1], y[2], y[3]}, (f32v4*)(Cz + m * p.ldc + nq));
-        } else {
-          // ragged or unaligned: the untransposed values, one column per lane
-#pragma unroll
-          for (int b = 0; b < 4; b++) {
-            const int64_t mm = mb + tm * 32 + 8 * a + 4 * g + b;
-            if (mm < p.M && ncol0 < p.N) Cz[mm * p.ldc + ncol0] = x[b];
+        for (int tn = 0; tn < TN; tn++) {
+          const float v = SCALED ? acc[tm][tn][4 * a + b] * mul : acc[tm][tn][4 * a + b];
+          if (full || (mb + r + 4 * g < p.M && nb + tn * 32 + (l & 31) < p.N)) {
+            if (PARTIAL) rp[tn * 32] = v;
+            else __builtin_nontemporal_store(v, rp + tn * 32);
           }
         }
       }
@@ -539,7 +520,7 @@ __device__ __forceinline__ void mx_fill_store(const MxXBlock& b, AS&& aslot, AG&
 // A halves of the two stage buffers, with its scale bytes in the A halves of
 // the scale-group buffers.  The codes and scale bytes are those the
 // quantizer writes for the same input, so the products are the same.
-template <int TM, int TN, int WM, bool FA = false, bool HAD = false>
+template <int TM, int TN, int WM, bool PARTIAL, bool FA = false, bool HAD = false>
 __device__ __forceinline__ void mx_tile(const GemmArgs& p, uint8_t* smem, int64_t m0, int64_t n0, int kt0, int kt1,
                                         float* Cz) {
   constexpr int WN = 4 / WM;                     // waves along N
@@ -715,7 +696,7 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& p, uint8_t* smem, int64_
     }
     wait_cnt<0, 0>();   // nothing may still write LDS when the workgroup exits
   }
-  store_tile_f32x4<TM, TN>(p, Cz, m0 + wm * (32 * TM), n0 + wn * (32 * TN), acc);
+  store_tile_f32<TM, TN, false, PARTIAL>(p, Cz, m0 + wm * (32 * TM), n0 + wn * (32 * TN), acc);
 }
 
 // Work items.  Workgroups are dispatched in id order to whichever compute
@@ -745,6 +726,8 @@ __device__ __forceinline__ int xcd_gather(int id, int n) {
 }
 
 // Split ranges start on even stages (a scale group spans two stages).
+// PARTIAL: the launch writes split-K partials.
+template <bool PARTIAL>
 __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[MX_LDS];
   const int b = blockIdx.x, z = blockIdx.y;
@@ -758,12 +741,12 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs p) {
   const int F = T - R;
   if (b >= R && b < R + F) {
     tm = mx_walk(p, xcd_gather(b - R, F), tn);
-    mx_tile<4, 4, 2>(p, smem, (int64_t)tm * BM, (int64_t)tn * BN, kt0, kt1, Cz);
+    mx_tile<4, 4, 2, PARTIAL>(p, smem, (int64_t)tm * BM, (int64_t)tn * BN, kt0, kt1, Cz);
   } else {
     const int second = b >= R + F;
     const int i = second ? b - R - F : b;
     tm = mx_walk(p, F + xcd_gather(i, R), tn);
-    mx_tile<4, 2, 2>(p, smem, (int64_t)tm * BM, (int64_t)tn * BN + 128 * second, kt0, kt1, Cz);
+    mx_tile<4, 2, 2, PARTIAL>(p, smem, (int64_t)tm * BM, (int64_t)tn * BN + 128 * second, kt0, kt1, Cz);
   }
 }
 
@@ -771,7 +754,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs p) {
 // weights): 32 TM x 256 tiles, the four waves side by side along N, so no MFMA
 // work is spent on rows past M; these shapes stream the weights from HBM and
 // are split along K for enough workgroups.  Grid: (N tiles, splits).
-template <int TM>
+template <int TM, bool PARTIAL>
 __global__ void __launch_bounds__(256, 1) gemm_mx_narrow_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[MX_LDS];
   const int z = blockIdx.y;
@@ -780,7 +763,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_narrow_kernel(GemmArgs p) {
   int kt1 = 2 * (int)((int64_t)pairs * (z + 1) / p.splits);
   if (kt1 > p.k_tiles) kt1 = p.k_tiles;
   float* Cz = p.C + (int64_t)z * p.split_stride;
-  mx_tile<TM, 2, 1>(p, smem, 0, (int64_t)blockIdx.x * 256, kt0, kt1, Cz);
+  mx_tile<TM, 2, 1, PARTIAL>(p, smem, 0, (int64_t)blockIdx.x * 256, kt0, kt1, Cz);
 }
 
 // Narrow MXFP4 GEMM whose A operand is quantized inside the kernel from the
@@ -791,7 +774,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_narrow_kernel(GemmArgs p) {
 // gemm_mx_narrow_kernel, so the result equals quantize-then-GEMM bit for bit.
 // Each workgroup quantizes the activation rows for its own contraction range
 // (at most 16 / TM stages; the planner checks, and uses it for TM = 1 only).
-template <int TM, bool HAD>
+template <int TM, bool HAD, bool PARTIAL>
 __global__ void __launch_bounds__(256, 1) gemm_mx_fused_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[MX_LDS];
   const int z = blockIdx.y;
@@ -800,7 +783,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_fused_kernel(GemmArgs p) {
   int kt1 = 2 * (int)((int64_t)pairs * (z + 1) / p.splits);
   if (kt1 > p.k_tiles) kt1 = p.k_tiles;
   float* Cz = p.C + (int64_t)z * p.split_stride;
-  mx_tile<TM, 2, 1, true, HAD>(p, smem, 0, (int64_t)blockIdx.x * 256, kt0, kt1, Cz);
+  mx_tile<TM, 2, 1, PARTIAL, true, HAD>(p, smem, 0, (int64_t)blockIdx.x * 256, kt0, kt1, Cz);
 }
 
 // ---------------------------------------------------------------------------
@@ -832,6 +815,7 @@ __device__ __forceinline__ v2h e4m3_pair(int word) {
 // (32 contiguous bytes); at step u it feeds half (u & 1) of block 4g + u/2 to
 // the 32x32x16 fp16 MFMA.  A and B use the same assignment, so every step
 // pairs equal contraction indices.
+template <bool PARTIAL>
 __global__ void __launch_bounds__(256, 1) gemm_nv_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * STAGE_BYTES];
   int tm_, tn_;
@@ -896,7 +880,7 @@ __global__ void __launch_bounds__(256, 1) gemm_nv_kernel(GemmArgs p) {
   // both tensor scales multiply the sum (for split partials too: the factor
   // distributes over the split sum)
   const float mul = p.a_ts[0] * p.b_ts[0];
-  store_tile_f32x4<4, 4, true>(p, Cz, m0 + wm * 128, n0 + wn * 128, acc, mul);
+  store_tile_f32<4, 4, true, PARTIAL>(p, Cz, m0 + wm * 128, n0 + wn * 128, acc, mul);
 }
 
 // ---------------------------------------------------------------------------
@@ -966,6 +950,26 @@ static int compute_units() {
   return cache[dev];
 }
 
+template <bool PARTIAL>
+static void launch_gemm_kernel(bool nv, const GemmArgs& p, const GemmPlan& plan, int fused_had, dim3 grid,
+                               dim3 ngrid, hipStream_t stream) {
+  if (nv) {
+    hipLaunchKernelGGL(gemm_nv_kernel<PARTIAL>, grid, dim3(256), 0, stream, p);
+  } else if (plan.narrow_tm && fused_had >= 0) {
+    // fused plans have 32-row tiles (fused_plan_ok)
+    if (fused_had) hipLaunchKernelGGL((gemm_mx_fused_kernel<1, true, PARTIAL>), ngrid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((gemm_mx_fused_kernel<1, false, PARTIAL>), ngrid, dim3(256), 0, stream, p);
+  } else if (plan.narrow_tm == 1) {
+    hipLaunchKernelGGL((gemm_mx_narrow_kernel<1, PARTIAL>), ngrid, dim3(256), 0, stream, p);
+  } else if (plan.narrow_tm == 2) {
+    hipLaunchKernelGGL((gemm_mx_narrow_kernel<2, PARTIAL>), ngrid, dim3(256), 0, stream, p);
+  } else if (plan.narrow_tm) {
+    hipLaunchKernelGGL((gemm_mx_narrow_kernel<4, PARTIAL>), ngrid, dim3(256), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(gemm_mx_kernel<PARTIAL>, grid, dim3(256), 0, stream, p);
+  }
+}
+
 static hipError_t launch_gemm_common(bool nv, GemmArgs p, float* C, int64_t ldc, float* workspace,
                                      const GemmPlan& plan, hipStream_t stream, int fused_had = -1) {
   p.ntm = (int)((p.M + BM - 1) / BM);
@@ -988,21 +992,9 @@ static hipError_t launch_gemm_common(bool nv, GemmArgs p, float* C, int64_t ldc,
     if (tiles > cus && tiles % cus != 0) p.rem = (int)(tiles % cus);
   }
   dim3 grid((unsigned)(tiles + p.rem), (unsigned)plan.splits);
-  if (nv) {
-    hipLaunchKernelGGL(gemm_nv_kernel, grid, dim3(256), 0, stream, p);
-  } else if (plan.narrow_tm && fused_had >= 0) {
-    dim3 ngrid((unsigned)((p.N + 255) / 256), (unsigned)plan.splits);
-    // fused plans have 32-row tiles (fused_plan_ok)
-    if (fused_had) hipLaunchKernelGGL((gemm_mx_fused_kernel<1, true>), ngrid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((gemm_mx_fused_kernel<1, false>), ngrid, dim3(256), 0, stream, p);
-  } else if (plan.narrow_tm) {
-    dim3 ngrid((unsigned)((p.N + 255) / 256), (unsigned)plan.splits);
-    if (plan.narrow_tm == 1) hipLaunchKernelGGL(gemm_mx_narrow_kernel<1>, ngrid, dim3(256), 0, stream, p);
-    else if (plan.narrow_tm == 2) hipLaunchKernelGGL(gemm_mx_narrow_kernel<2>, ngrid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL(gemm_mx_narrow_kernel<4>, ngrid, dim3(256), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL(gemm_mx_kernel, grid, dim3(256), 0, stream, p);
-  }
+  dim3 ngrid((unsigned)((p.N + 255) / 256), (unsigned)plan.splits);
+  if (plan.splits > 1) launch_gemm_kernel<true>(nv, p, plan, fused_had, grid, ngrid, stream);
+  else launch_gemm_kernel<false>(nv, p, plan, fused_had, grid, ngrid, stream);
   if (plan.splits > 1) {
     int64_t work = p.M * p.N;
     int64_t g = (work + 255) / 256;
