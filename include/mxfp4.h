@@ -133,13 +133,26 @@ mxfp4_status mxfp4_gemm_workspace_bytes(const mxfp4_tensor *A, const mxfp4_tenso
  * FP4 matrix cores; NVFP4 dequantizes exactly to fp16 in registers (an
  * E2M1 x E4M3 product has at most 6 significant bits) for the fp16 matrix
  * cores and applies both tensor scales in the epilogue.
- * C: device, row-major, ldc >= N.  k must be a multiple of 128 and at most
+ * C: device, row-major, ldc >= N, 4-byte aligned.  k must be a multiple of 128 and at most
  * 2^24 (UNSUPPORTED_SHAPE otherwise); fmt, k and hadamard of A and B must agree
  * (FORMAT_MISMATCH).  A->codes and B->codes must be 16-byte aligned and the
  * scales 4-byte aligned (INVALID_ARG otherwise).
  * workspace: device, at least mxfp4_gemm_workspace_bytes (NULL if 0). */
 mxfp4_status mxfp4_gemm(const mxfp4_tensor *A, const mxfp4_tensor *B, float *C, int64_t ldc,
                         void *workspace, size_t ws_bytes, hipStream_t stream);
+
+/* mxfp4_gemm with a bf16 C: each element is the FP32 value mxfp4_gemm writes
+ * for the same operands, rounded to the nearest bf16 (ties to even; NaN stays
+ * NaN, overflow rounds to infinity).  Half the output bytes, for layers whose
+ * consumer takes bf16 (the output epilogue named next to the activation
+ * prologue in "Bridging the Gap Between Promise and Performance for
+ * Microscaling FP4 Quantization", abstract: the quantization costs are fused
+ * into the GEMM kernels).  C: device, bf16 bit patterns, row-major, ldc >= N,
+ * 2-byte aligned (INVALID_ARG otherwise).  Operands, workspace (the same
+ * mxfp4_gemm_workspace_bytes: split-K partial sums stay FP32) and errors as
+ * for mxfp4_gemm. */
+mxfp4_status mxfp4_gemm_bf16(const mxfp4_tensor *A, const mxfp4_tensor *B, uint16_t *C, int64_t ldc,
+                             void *workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace needed by mxfp4_quantize_gemm for activations [M, K] against B:
  * the split-K partial sums when the quantization is fused into the GEMM,

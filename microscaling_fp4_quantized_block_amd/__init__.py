@@ -42,7 +42,7 @@ def _load_library() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"libmxfp4.so not found at {LIB_PATH}; build it with "
-            "`python -m microscaling_fp4_quantized_block_amd.build` (there is no CPU fallback)")
+            "`python microscaling_fp4_quantized_block_amd/build.py` (there is no CPU fallback)")
     lib = ctypes.CDLL(LIB_PATH)
     i32, i64, u64, vp, sz = ctypes.c_int, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_size_t
     P = ctypes.POINTER
@@ -60,6 +60,8 @@ def _load_library() -> ctypes.CDLL:
     lib.mxfp4_gemm_workspace_bytes.argtypes = [P(MxTensorStruct), P(MxTensorStruct), P(sz)]
     lib.mxfp4_gemm.restype = i32
     lib.mxfp4_gemm.argtypes = [P(MxTensorStruct), P(MxTensorStruct), vp, i64, vp, sz, vp]
+    lib.mxfp4_gemm_bf16.restype = i32
+    lib.mxfp4_gemm_bf16.argtypes = [P(MxTensorStruct), P(MxTensorStruct), vp, i64, vp, sz, vp]
     lib.mxfp4_quantize_gemm_workspace_bytes.restype = i32
     lib.mxfp4_quantize_gemm_workspace_bytes.argtypes = [i64, i64, i32, P(MxTensorStruct), P(sz)]
     lib.mxfp4_quantize_gemm.restype = i32
@@ -195,6 +197,23 @@ def mxfp4_gemm(qa: QTensor, qb: QTensor, out: Optional[torch.Tensor] = None,
     return out
 
 
+def mxfp4_gemm_bf16(qa: QTensor, qb: QTensor, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C[M, N] = A B^T as mxfp4_gemm computes it, rounded to bfloat16 (nearest
+    even)."""
+    if out is None:
+        out = torch.empty((qa.rows, qb.rows), dtype=torch.bfloat16, device=qa.codes.device)
+    if out.dtype != torch.bfloat16 or out.dim() != 2 or (out.numel() and out.stride(1) != 1):
+        raise ValueError("out must be a 2-D bfloat16 tensor with unit stride along its last dimension")
+    ws_bytes = mxfp4_gemm_workspace_bytes(qa, qb)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=qa.codes.device)
+    sa, sb = qa.as_struct(), qb.as_struct()
+    _check(lib.mxfp4_gemm_bf16(ctypes.byref(sa), ctypes.byref(sb), _ptr(out), out.stride(0), _ptr(workspace),
+                               workspace.numel() if workspace is not None else 0, _stream(qa.codes.device)))
+    return out
+
+
 def mxfp4_quantize_gemm_workspace_bytes(M: int, K: int, hadamard: bool, qb: QTensor) -> int:
     b = ctypes.c_size_t()
     sb = qb.as_struct()
@@ -290,7 +309,7 @@ gemm = mxfp4_gemm
 quantize_gemm = mxfp4_quantize_gemm
 
 __all__ = ["QTensor", "MxFp4Error", "mxfp4_tensor_bytes", "mxfp4_quantize_workspace_bytes", "mxfp4_quantize",
-           "mxfp4_dequantize", "mxfp4_gemm_workspace_bytes", "mxfp4_gemm", "mxfp4_status_string",
+           "mxfp4_dequantize", "mxfp4_gemm_workspace_bytes", "mxfp4_gemm", "mxfp4_gemm_bf16", "mxfp4_status_string",
            "mxfp4_quantize_gemm_workspace_bytes", "mxfp4_quantize_gemm",
            "mxfp4_quantization_noise_workspace_bytes", "mxfp4_quantization_noise", "gradient_noise_ratio",
            "mxfp4_quantize_mse_workspace_bytes", "mxfp4_quantize_mse",

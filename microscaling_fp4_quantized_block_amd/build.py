@@ -1,6 +1,7 @@
 """Build libmxfp4.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: python -m microscaling_fp4_quantized_block_amd.build
+Usage: python microscaling_fp4_quantized_block_amd/build.py
+(run as a file: importing the package loads the library this builds)
 """
 from __future__ import annotations
 

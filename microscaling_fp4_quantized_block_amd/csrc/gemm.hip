@@ -239,20 +239,67 @@ __device__ __forceinline__ void block_barrier() {
 // each element.
 //
 // Every value is multiplied by mul (the NVFP4 tensor scales) when SCALED.
-// The stores of C are non-temporal: C is not read again here, and on
-// store-bound shapes (short contractions) streaming stores run ~10-18 % faster
-// (measured).  Split-K partials (PARTIAL) are re-read by the reduction right
-// after, so they are written with plain stores (~7 % faster on a 3072 x 768 x
-// 50432 wgrad, ~12 % on a 16 x 4096 x 14336 decode).  The choice is a kernel
-// template parameter: two epilogues in one kernel cost the wide kernel ~35 %.
-template <int TM, int TN, bool SCALED, bool PARTIAL>
-__device__ __forceinline__ void store_tile_f32(const GemmArgs& p, float* Cz, int64_t mb, int64_t nb,
-                                               const v16f (&acc)[TM][TN], float mul = 1.0f) {
+// OUT selects what is written:
+//   OUT_F32   fp32 C with non-temporal stores: C is not read again here, and
+//             on store-bound shapes (short contractions) streaming stores run
+//             ~10-18 % faster (measured);
+//   OUT_PART  fp32 split-K partials with plain stores: the reduction re-reads
+//             them right after (~7 % faster on a 3072 x 768 x 50432 wgrad,
+//             ~12 % on a 16 x 4096 x 14336 decode);
+//   OUT_BF16  C rounded to bf16 (round to nearest even, hardware convert).
+// The choice is a kernel template parameter: two epilogues in one kernel cost
+// the wide kernel ~35 %.
+constexpr int OUT_F32 = 0, OUT_PART = 1, OUT_BF16 = 2;
+
+//
+// bf16 whole blocks: the two column blocks tn, tn + 1 of a row are paired so
+// that each lane stores 4 bytes and a wave store covers 128 contiguous bytes
+// per row: lanes l and l ^ 1 swap one value (one DPP move), then an even lane
+// holds columns l, l + 1 of block tn and an odd lane columns l - 1, l of block
+// tn + 1.  (2-byte stores of half lines ran ~9 % slower than FP32 C on a
+// store-bound 50432 x 3072 x 768.)
+__device__ __forceinline__ float dpp_swap_pairs(float v) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)__float_as_uint(v), 0xB1, 0xF, 0xF, true));
+}
+
+template <int TM, int TN, bool SCALED, int OUT>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, float* Cz, int64_t mb, int64_t nb,
+                                           const v16f (&acc)[TM][TN], float mul = 1.0f) {
+  typedef typename std::conditional<OUT == OUT_BF16, __bf16, float>::type T;
   const int l = threadIdx.x & 63, g = l >> 5;
   const int64_t ldc = p.ldc;
   const bool full = mb + 32 * TM <= p.M && nb + 32 * TN <= p.N;
+  if constexpr (OUT == OUT_BF16 && TN % 2 == 0) {
+    if (full && (ldc & 1) == 0 && (((uintptr_t)Cz) & 3) == 0) {
+      const bool odd = l & 1;
+      // this lane's 4-byte pair: block tn (even lanes) or tn + 1 (odd lanes),
+      // first column (l & 30)
+      __bf16* const pair0 = (__bf16*)Cz + (mb + 4 * g) * ldc + nb + (l & 30) + (odd ? 32 : 0);
+#pragma unroll
+      for (int tm = 0; tm < TM; tm++) {
+#pragma unroll
+        for (int a = 0; a < 4; a++) {
+#pragma unroll
+          for (int b = 0; b < 4; b++) {
+            const int r = tm * 32 + 8 * a + b;
+            __bf16* const rp = pair0 + (int64_t)r * ldc;
+#pragma unroll
+            for (int tn = 0; tn < TN; tn += 2) {
+              float x = acc[tm][tn][4 * a + b], y = acc[tm][tn + 1][4 * a + b];
+              if (SCALED) { x *= mul; y *= mul; }
+              const float got = dpp_swap_pairs(odd ? x : y);
+              const float lo = odd ? got : x, hi = odd ? y : got;
+              typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+              *(bf16x2_t*)(rp + tn * 32) = (bf16x2_t){(__bf16)lo, (__bf16)hi};
+            }
+          }
+        }
+      }
+      return;
+    }
+  }
   // this lane's column and its first row (4g) in the block
-  float* const lane0 = Cz + (mb + 4 * g) * ldc + nb + (l & 31);
+  T* const lane0 = (T*)Cz + (mb + 4 * g) * ldc + nb + (l & 31);
 #pragma unroll
   for (int tm = 0; tm < TM; tm++) {
 #pragma unroll
@@ -260,13 +307,14 @@ __device__ __forceinline__ void store_tile_f32(const GemmArgs& p, float* Cz, int
 #pragma unroll
       for (int b = 0; b < 4; b++) {
         const int r = tm * 32 + 8 * a + b;                      // row in the block, less 4g
-        float* const rp = lane0 + (int64_t)r * ldc;
+        T* const rp = lane0 + (int64_t)r * ldc;
 #pragma unroll
         for (int tn = 0; tn < TN; tn++) {
           const float v = SCALED ? acc[tm][tn][4 * a + b] * mul : acc[tm][tn][4 * a + b];
           if (full || (mb + r + 4 * g < p.M && nb + tn * 32 + (l & 31) < p.N)) {
-            if (PARTIAL) rp[tn * 32] = v;
-            else __builtin_nontemporal_store(v, rp + tn * 32);
+            if (OUT == OUT_PART) rp[tn * 32] = v;
+            else if (OUT == OUT_BF16) rp[tn * 32] = (T)v;
+            else __builtin_nontemporal_store(v, (float*)rp + tn * 32);
           }
         }
       }
@@ -520,7 +568,7 @@ __device__ __forceinline__ void mx_fill_store(const MxXBlock& b, AS&& aslot, AG&
 // A halves of the two stage buffers, with its scale bytes in the A halves of
 // the scale-group buffers.  The codes and scale bytes are those the
 // quantizer writes for the same input, so the products are the same.
-template <int TM, int TN, int WM, bool PARTIAL, bool FA = false, bool HAD = false>
+template <int TM, int TN, int WM, int OUT, bool FA = false, bool HAD = false>
 __device__ __forceinline__ void mx_tile(const GemmArgs& p, uint8_t* smem, int64_t m0, int64_t n0, int kt0, int kt1,
                                         float* Cz) {
   constexpr int WN = 4 / WM;                     // waves along N
@@ -696,7 +744,7 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& p, uint8_t* smem, int64_
     }
     wait_cnt<0, 0>();   // nothing may still write LDS when the workgroup exits
   }
-  store_tile_f32<TM, TN, false, PARTIAL>(p, Cz, m0 + wm * (32 * TM), n0 + wn * (32 * TN), acc);
+  store_tile<TM, TN, false, OUT>(p, Cz, m0 + wm * (32 * TM), n0 + wn * (32 * TN), acc);
 }
 
 // Work items.  Workgroups are dispatched in id order to whichever compute
@@ -726,8 +774,8 @@ __device__ __forceinline__ int xcd_gather(int id, int n) {
 }
 
 // Split ranges start on even stages (a scale group spans two stages).
-// PARTIAL: the launch writes split-K partials.
-template <bool PARTIAL>
+// OUT: what the launch writes (fp32 C, split-K partials or bf16 C).
+template <int OUT>
 __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[MX_LDS];
   const int b = blockIdx.x, z = blockIdx.y;
@@ -741,12 +789,12 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs p) {
   const int F = T - R;
   if (b >= R && b < R + F) {
     tm = mx_walk(p, xcd_gather(b - R, F), tn);
-    mx_tile<4, 4, 2, PARTIAL>(p, smem, (int64_t)tm * BM, (int64_t)tn * BN, kt0, kt1, Cz);
+    mx_tile<4, 4, 2, OUT>(p, smem, (int64_t)tm * BM, (int64_t)tn * BN, kt0, kt1, Cz);
   } else {
     const int second = b >= R + F;
     const int i = second ? b - R - F : b;
     tm = mx_walk(p, F + xcd_gather(i, R), tn);
-    mx_tile<4, 2, 2, PARTIAL>(p, smem, (int64_t)tm * BM, (int64_t)tn * BN + 128 * second, kt0, kt1, Cz);
+    mx_tile<4, 2, 2, OUT>(p, smem, (int64_t)tm * BM, (int64_t)tn * BN + 128 * second, kt0, kt1, Cz);
   }
 }
 
@@ -754,7 +802,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs p) {
 // weights): 32 TM x 256 tiles, the four waves side by side along N, so no MFMA
 // work is spent on rows past M; these shapes stream the weights from HBM and
 // are split along K for enough workgroups.  Grid: (N tiles, splits).
-template <int TM, bool PARTIAL>
+template <int TM, int OUT>
 __global__ void __launch_bounds__(256, 1) gemm_mx_narrow_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[MX_LDS];
   const int z = blockIdx.y;
@@ -763,7 +811,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_narrow_kernel(GemmArgs p) {
   int kt1 = 2 * (int)((int64_t)pairs * (z + 1) / p.splits);
   if (kt1 > p.k_tiles) kt1 = p.k_tiles;
   float* Cz = p.C + (int64_t)z * p.split_stride;
-  mx_tile<TM, 2, 1, PARTIAL>(p, smem, 0, (int64_t)blockIdx.x * 256, kt0, kt1, Cz);
+  mx_tile<TM, 2, 1, OUT>(p, smem, 0, (int64_t)blockIdx.x * 256, kt0, kt1, Cz);
 }
 
 // Narrow MXFP4 GEMM whose A operand is quantized inside the kernel from the
@@ -774,7 +822,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_narrow_kernel(GemmArgs p) {
 // gemm_mx_narrow_kernel, so the result equals quantize-then-GEMM bit for bit.
 // Each workgroup quantizes the activation rows for its own contraction range
 // (at most 16 / TM stages; the planner checks, and uses it for TM = 1 only).
-template <int TM, bool HAD, bool PARTIAL>
+template <int TM, bool HAD, int OUT>
 __global__ void __launch_bounds__(256, 1) gemm_mx_fused_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[MX_LDS];
   const int z = blockIdx.y;
@@ -783,7 +831,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_fused_kernel(GemmArgs p) {
   int kt1 = 2 * (int)((int64_t)pairs * (z + 1) / p.splits);
   if (kt1 > p.k_tiles) kt1 = p.k_tiles;
   float* Cz = p.C + (int64_t)z * p.split_stride;
-  mx_tile<TM, 2, 1, PARTIAL, true, HAD>(p, smem, 0, (int64_t)blockIdx.x * 256, kt0, kt1, Cz);
+  mx_tile<TM, 2, 1, OUT, true, HAD>(p, smem, 0, (int64_t)blockIdx.x * 256, kt0, kt1, Cz);
 }
 
 // ---------------------------------------------------------------------------
@@ -815,7 +863,7 @@ __device__ __forceinline__ v2h e4m3_pair(int word) {
 // (32 contiguous bytes); at step u it feeds half (u & 1) of block 4g + u/2 to
 // the 32x32x16 fp16 MFMA.  A and B use the same assignment, so every step
 // pairs equal contraction indices.
-template <bool PARTIAL>
+template <int OUT>
 __global__ void __launch_bounds__(256, 1) gemm_nv_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * STAGE_BYTES];
   int tm_, tn_;
@@ -880,21 +928,23 @@ __global__ void __launch_bounds__(256, 1) gemm_nv_kernel(GemmArgs p) {
   // both tensor scales multiply the sum (for split partials too: the factor
   // distributes over the split sum)
   const float mul = p.a_ts[0] * p.b_ts[0];
-  store_tile_f32<4, 4, true, PARTIAL>(p, Cz, m0 + wm * 128, n0 + wn * 128, acc, mul);
+  store_tile<4, 4, true, OUT>(p, Cz, m0 + wm * 128, n0 + wn * 128, acc, mul);
 }
 
 // ---------------------------------------------------------------------------
 // Split-K reduction: C = sum over splits, in split order.
 // ---------------------------------------------------------------------------
+// T = float (fp32 C) or __bf16 (the fp32 sum rounded to nearest even).
+template <typename T>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ ws, int splits, int64_t M,
-                                                            int64_t N, float* __restrict__ C, int64_t ldc) {
+                                                            int64_t N, T* __restrict__ C, int64_t ldc) {
   const int64_t total = M * N;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
     float s = ws[t];
     for (int z = 1; z < splits; z++) s += ws[(int64_t)z * total + t];
     const int64_t m = t / N, n = t - m * N;
-    C[m * ldc + n] = s;
+    C[m * ldc + n] = (T)s;
   }
 }
 
@@ -950,27 +1000,29 @@ static int compute_units() {
   return cache[dev];
 }
 
-template <bool PARTIAL>
+template <int OUT>
 static void launch_gemm_kernel(bool nv, const GemmArgs& p, const GemmPlan& plan, int fused_had, dim3 grid,
                                dim3 ngrid, hipStream_t stream) {
   if (nv) {
-    hipLaunchKernelGGL(gemm_nv_kernel<PARTIAL>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(gemm_nv_kernel<OUT>, grid, dim3(256), 0, stream, p);
   } else if (plan.narrow_tm && fused_had >= 0) {
     // fused plans have 32-row tiles (fused_plan_ok)
-    if (fused_had) hipLaunchKernelGGL((gemm_mx_fused_kernel<1, true, PARTIAL>), ngrid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((gemm_mx_fused_kernel<1, false, PARTIAL>), ngrid, dim3(256), 0, stream, p);
+    if (fused_had) hipLaunchKernelGGL((gemm_mx_fused_kernel<1, true, OUT>), ngrid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((gemm_mx_fused_kernel<1, false, OUT>), ngrid, dim3(256), 0, stream, p);
   } else if (plan.narrow_tm == 1) {
-    hipLaunchKernelGGL((gemm_mx_narrow_kernel<1, PARTIAL>), ngrid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_mx_narrow_kernel<1, OUT>), ngrid, dim3(256), 0, stream, p);
   } else if (plan.narrow_tm == 2) {
-    hipLaunchKernelGGL((gemm_mx_narrow_kernel<2, PARTIAL>), ngrid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_mx_narrow_kernel<2, OUT>), ngrid, dim3(256), 0, stream, p);
   } else if (plan.narrow_tm) {
-    hipLaunchKernelGGL((gemm_mx_narrow_kernel<4, PARTIAL>), ngrid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((gemm_mx_narrow_kernel<4, OUT>), ngrid, dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(gemm_mx_kernel<PARTIAL>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(gemm_mx_kernel<OUT>, grid, dim3(256), 0, stream, p);
   }
 }
 
-static hipError_t launch_gemm_common(bool nv, GemmArgs p, float* C, int64_t ldc, float* workspace,
+// C: fp32, or bf16 when c_bf16 (then written by the epilogue, or by the
+// split-K reduction from fp32 partials).
+static hipError_t launch_gemm_common(bool nv, GemmArgs p, void* C, int64_t ldc, int c_bf16, float* workspace,
                                      const GemmPlan& plan, hipStream_t stream, int fused_had = -1) {
   p.ntm = (int)((p.M + BM - 1) / BM);
   p.ntn = (int)((p.N + BN - 1) / BN);
@@ -981,7 +1033,7 @@ static hipError_t launch_gemm_common(bool nv, GemmArgs p, float* C, int64_t ldc,
     p.ldc = p.N;
     p.split_stride = p.M * p.N;
   } else {
-    p.C = C;
+    p.C = (float*)C;
     p.ldc = ldc;
     p.split_stride = 0;
   }
@@ -993,26 +1045,31 @@ static hipError_t launch_gemm_common(bool nv, GemmArgs p, float* C, int64_t ldc,
   }
   dim3 grid((unsigned)(tiles + p.rem), (unsigned)plan.splits);
   dim3 ngrid((unsigned)((p.N + 255) / 256), (unsigned)plan.splits);
-  if (plan.splits > 1) launch_gemm_kernel<true>(nv, p, plan, fused_had, grid, ngrid, stream);
-  else launch_gemm_kernel<false>(nv, p, plan, fused_had, grid, ngrid, stream);
+  if (plan.splits > 1) launch_gemm_kernel<OUT_PART>(nv, p, plan, fused_had, grid, ngrid, stream);
+  else if (c_bf16) launch_gemm_kernel<OUT_BF16>(nv, p, plan, fused_had, grid, ngrid, stream);
+  else launch_gemm_kernel<OUT_F32>(nv, p, plan, fused_had, grid, ngrid, stream);
   if (plan.splits > 1) {
     int64_t work = p.M * p.N;
     int64_t g = (work + 255) / 256;
     if (g > 4096) g = 4096;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)g), dim3(256), 0, stream, workspace, plan.splits,
-                       p.M, p.N, C, ldc);
+    if (c_bf16)
+      hipLaunchKernelGGL(splitk_reduce_kernel<__bf16>, dim3((unsigned)g), dim3(256), 0, stream, workspace,
+                         plan.splits, p.M, p.N, (__bf16*)C, ldc);
+    else
+      hipLaunchKernelGGL(splitk_reduce_kernel<float>, dim3((unsigned)g), dim3(256), 0, stream, workspace,
+                         plan.splits, p.M, p.N, (float*)C, ldc);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
-                          const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, float* C, int64_t ldc,
-                          float* workspace, const GemmPlan& plan, hipStream_t stream) {
+                          const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* C, int64_t ldc,
+                          int c_bf16, float* workspace, const GemmPlan& plan, hipStream_t stream) {
   GemmArgs p{};
   p.a = a_codes; p.as = a_scales; p.b = b_codes; p.bs = b_scales;
   p.a_ts = nullptr; p.b_ts = nullptr;
   p.M = M; p.N = N; p.K = K;
-  return launch_gemm_common(false, p, C, ldc, workspace, plan, stream);
+  return launch_gemm_common(false, p, C, ldc, c_bf16, workspace, plan, stream);
 }
 
 bool fused_plan_ok(const GemmPlan& plan) {
@@ -1036,18 +1093,18 @@ hipError_t launch_gemm_mx_fused(const uint16_t* x, int64_t ldx, int hadamard, co
   p.x = x;
   p.ldx = ldx;
   p.x_vec = (((uintptr_t)x & 15) == 0 && (ldx % 8) == 0) ? 1 : 0;
-  return launch_gemm_common(false, p, C, ldc, workspace, plan, stream, hadamard ? 1 : 0);
+  return launch_gemm_common(false, p, C, ldc, 0, workspace, plan, stream, hadamard ? 1 : 0);
 }
 
 hipError_t launch_gemm_nv(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
                           const uint8_t* b_codes, const uint8_t* b_scales, const float* b_ts, int64_t M,
-                          int64_t N, int64_t K, float* C, int64_t ldc, float* workspace, const GemmPlan& plan,
-                          hipStream_t stream) {
+                          int64_t N, int64_t K, void* C, int64_t ldc, int c_bf16, float* workspace,
+                          const GemmPlan& plan, hipStream_t stream) {
   GemmArgs p{};
   p.a = a_codes; p.as = a_scales; p.b = b_codes; p.bs = b_scales;
   p.a_ts = a_ts; p.b_ts = b_ts;
   p.M = M; p.N = N; p.K = K;
-  return launch_gemm_common(true, p, C, ldc, workspace, plan, stream);
+  return launch_gemm_common(true, p, C, ldc, c_bf16, workspace, plan, stream);
 }
 
 }  // namespace mxfp4

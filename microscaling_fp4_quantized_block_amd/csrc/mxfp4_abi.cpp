@@ -113,14 +113,16 @@ mxfp4_status mxfp4_gemm_workspace_bytes(const mxfp4_tensor* A, const mxfp4_tenso
   return MXFP4_OK;
 }
 
-mxfp4_status mxfp4_gemm(const mxfp4_tensor* A, const mxfp4_tensor* B, float* C, int64_t ldc, void* workspace,
-                        size_t ws_bytes, hipStream_t stream) {
+// C: fp32, or bf16 bit patterns when c_bf16.
+static mxfp4_status gemm_impl(const mxfp4_tensor* A, const mxfp4_tensor* B, void* C, int64_t ldc, int c_bf16,
+                              void* workspace, size_t ws_bytes, hipStream_t stream) {
   mxfp4_status s = check_gemm_operands(A, B);
   if (s != MXFP4_OK) return s;
   const int64_t M = A->rows, N = B->rows, K = A->k;
   if (ldc < N || ldc < 1) return MXFP4_ERR_INVALID_ARG;
   if (M == 0 || N == 0) return MXFP4_OK;
   if (!C || !A->codes || !A->scales || !B->codes || !B->scales) return MXFP4_ERR_INVALID_ARG;
+  if (!aligned(C, c_bf16 ? 2 : 4)) return MXFP4_ERR_INVALID_ARG;
   if (A->fmt == MXFP4_FMT_NV && (!A->tensor_scale || !B->tensor_scale)) return MXFP4_ERR_INVALID_ARG;
   if (!aligned(A->codes, 16) || !aligned(B->codes, 16) || !aligned(A->scales, 4) || !aligned(B->scales, 4))
     return MXFP4_ERR_INVALID_ARG;
@@ -131,12 +133,22 @@ mxfp4_status mxfp4_gemm(const mxfp4_tensor* A, const mxfp4_tensor* B, float* C, 
   }
   hipError_t e;
   if (A->fmt == MXFP4_FMT_MX)
-    e = mxfp4::launch_gemm_mx(A->codes, A->scales, B->codes, B->scales, M, N, K, C, ldc, (float*)workspace, pl,
-                              stream);
+    e = mxfp4::launch_gemm_mx(A->codes, A->scales, B->codes, B->scales, M, N, K, C, ldc, c_bf16,
+                              (float*)workspace, pl, stream);
   else
     e = mxfp4::launch_gemm_nv(A->codes, A->scales, A->tensor_scale, B->codes, B->scales, B->tensor_scale, M, N, K,
-                              C, ldc, (float*)workspace, pl, stream);
+                              C, ldc, c_bf16, (float*)workspace, pl, stream);
   return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
+}
+
+mxfp4_status mxfp4_gemm(const mxfp4_tensor* A, const mxfp4_tensor* B, float* C, int64_t ldc, void* workspace,
+                        size_t ws_bytes, hipStream_t stream) {
+  return gemm_impl(A, B, C, ldc, 0, workspace, ws_bytes, stream);
+}
+
+mxfp4_status mxfp4_gemm_bf16(const mxfp4_tensor* A, const mxfp4_tensor* B, uint16_t* C, int64_t ldc,
+                             void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return gemm_impl(A, B, C, ldc, 1, workspace, ws_bytes, stream);
 }
 
 // Online activation quantization + GEMM: fused into the narrow GEMM when the
@@ -195,7 +207,7 @@ mxfp4_status mxfp4_quantize_gemm(const uint16_t* x, int64_t M, int64_t K, int64_
     e = mxfp4::launch_quantize(x, M, K, ldx, MXFP4_FMT_MX, MXFP4_RTN, hadamard, 1, 0, a_codes, a_scales, nullptr,
                                nullptr, stream);
     if (e == hipSuccess)
-      e = mxfp4::launch_gemm_mx(a_codes, a_scales, B->codes, B->scales, M, N, K, C, ldc, gemm_ws, pl, stream);
+      e = mxfp4::launch_gemm_mx(a_codes, a_scales, B->codes, B->scales, M, N, K, C, ldc, 0, gemm_ws, pl, stream);
   }
   return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
 }

@@ -32,9 +32,10 @@ struct GemmPlan {
 };
 GemmPlan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K);
 
+// C: fp32, or bf16 (round to nearest even from the fp32 result) when c_bf16.
 hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
-                          const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, float* C, int64_t ldc,
-                          float* workspace, const GemmPlan& plan, hipStream_t stream);
+                          const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* C, int64_t ldc,
+                          int c_bf16, float* workspace, const GemmPlan& plan, hipStream_t stream);
 
 // Fused activation quantization + MXFP4 GEMM (narrow plans with 32-row tiles,
 // M <= 32, whose splits hold at most 16 stages): A = Q_MX,RTN(x [M, K] bf16,
@@ -46,8 +47,8 @@ hipError_t launch_gemm_mx_fused(const uint16_t* x, int64_t ldx, int hadamard, co
 
 hipError_t launch_gemm_nv(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
                           const uint8_t* b_codes, const uint8_t* b_scales, const float* b_ts, int64_t M,
-                          int64_t N, int64_t K, float* C, int64_t ldc, float* workspace, const GemmPlan& plan,
-                          hipStream_t stream);
+                          int64_t N, int64_t K, void* C, int64_t ldc, int c_bf16, float* workspace,
+                          const GemmPlan& plan, hipStream_t stream);
 
 // NVFP4 tensor scale of an input (amax pass + finalize) into tensor_scale;
 // partials: quantize_workspace_bytes(FMT_NV, R, C) bytes.

@@ -407,7 +407,6 @@ __global__ void __launch_bounds__(256) quant_cols_tile_kernel(ColArgs a) {
   for (int h = 0; h < 2; h++) {
     const int64_t rh = rw0 + 32 * h;
     if (!active || rh >= R) break;
-    const int nrows = (R - rh) >= 32 ? 32 : (int)(R - rh);
     float y[32];
 #pragma unroll
     for (int j = 0; j < 32; j++) y[j] = __uint_as_float((uint32_t)tile[(64 * w + 32 * h + j) * 64 + l] << 16);

@@ -132,6 +132,30 @@ def test_gemm_rejects_bad_arguments(mx):
     assert g(desc(mx, rows=0), b) == OK                            # empty output: no-op
 
 
+def test_gemm_bf16_rejects_bad_arguments(mx):
+    """The bf16-output GEMM checks what mxfp4_gemm checks, and a bf16 C needs
+    only 2-byte alignment."""
+    a, b = desc(mx, rows=64, k=256), desc(mx, rows=32, k=256)
+    g = lambda A, B, C=FAKE, ldc=32, ws=None, wsb=0: mx.lib.mxfp4_gemm_bf16(
+        ctypes.byref(A) if A is not None else None, ctypes.byref(B), C, ldc, ws, wsb, None)
+    assert g(None, b) == INVALID
+    assert g(a, desc(mx, fmt=1, rows=32)) == MISMATCH
+    assert g(desc(mx, k=96), desc(mx, rows=32, k=96)) == SHAPE
+    assert g(a, b, ldc=16) == INVALID
+    assert g(a, b, C=None) == INVALID
+    assert g(a, b, C=FAKE + 1) == INVALID                          # bf16 C must be 2-byte aligned
+    assert g(desc(mx, codes=FAKE + 8), b) == INVALID
+    assert g(desc(mx, rows=0), b) == OK
+    # a split plan still needs its FP32 partial-sum workspace
+    A, B = desc(mx, rows=64, k=8192), desc(mx, rows=96, k=8192)
+    assert mx.lib.mxfp4_gemm_bf16(ctypes.byref(A), ctypes.byref(B), FAKE + 2, 96, None, 0, None) == WORKSPACE
+
+
+def test_gemm_fp32_output_alignment(mx):
+    a, b = desc(mx, rows=64, k=256), desc(mx, rows=32, k=256)
+    assert mx.lib.mxfp4_gemm(ctypes.byref(a), ctypes.byref(b), FAKE + 2, 32, None, 0, None) == INVALID
+
+
 def test_gemm_workspace_query_matches_split_plan(mx):
     b = ctypes.c_size_t()
     # 64 x 96 outputs over a long contraction: split along K, fp32 partials
