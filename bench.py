@@ -413,6 +413,16 @@ def sweep(args):
             tf = flops / t / 1e12
             rows.append((cfg, "gemm", gname, f"{Mg}x{Ng}x{Kg}", t * 1e6, tf, "TFLOP/s",
                          bound + ("-fp16" if fmt == "nv" and bound == "mfma" else ""), bound_t / t))
+            if cfg in (0, 3):
+                # the same GEMM writing bf16 (inference consumers): 2 bytes per output
+                Cb = torch.empty((Mg, Ng), dtype=torch.bfloat16, device=dev)
+                tb = timed(lambda: mx.mxfp4_gemm_bf16(qa, qb, out=Cb, workspace=ws), False)
+                nbytes_b = nbytes - 2.0 * Mg * Ng
+                bound_tb = max(flops / (peak * 1e12), nbytes_b / (PEAK_HBM_GBPS * 1e9))
+                bound_b = "mfma" if flops / (peak * 1e12) >= nbytes_b / (PEAK_HBM_GBPS * 1e9) else "hbm"
+                rows.append((cfg, "gemm_bf16", gname, f"{Mg}x{Ng}x{Kg}", tb * 1e6, flops / tb / 1e12, "TFLOP/s",
+                             bound_b, bound_tb / tb))
+                del Cb
             del C, ws
         if cfg in (2, 3, 5):
             # weights with MSE-fitted scales (two alternations for NVFP4)
