@@ -244,6 +244,31 @@ mxfp4_status mxfp4_quantization_noise(const uint16_t *x, int64_t ldx, int axis, 
                                       double *stats, void *workspace, size_t ws_bytes,
                                       hipStream_t stream);
 
+/* Workspace needed by mxfp4_quantize_noise (the quantizer's, padded to 16
+ * bytes, then three doubles per workgroup of the largest launch plan the call
+ * can take).  Errors as for mxfp4_quantize. */
+mxfp4_status mxfp4_quantize_noise_workspace_bytes(int fmt, int hadamard, int64_t R, int64_t C, int axis,
+                                                  size_t *bytes);
+
+/* mxfp4_quantize and the sums of mxfp4_quantization_noise of its output in
+ * one pass: the sqrt(3) diagnostic of "FP4 All the Way", abstract, computed
+ * while the (typically stochastically rounded) gradient is quantized, so the
+ * input is read once.  out receives exactly what mxfp4_quantize writes for
+ * the same arguments; stats[0..2] = sum y^2, sum (Q(y) - y)^2 and the number
+ * of elements in blocks with a NaN scale byte, in binary64 as
+ * mxfp4_quantization_noise defines them (the terms are the same; the sums
+ * are added in another fixed order, so the last bits may differ from that
+ * call's; the same inputs give the same bits).  Transposed inputs that are
+ * not 16-byte aligned (or C % 8 != 0) are quantized, then summed by the
+ * separate pass.
+ * Arguments as for mxfp4_quantize, plus stats: device, 3 doubles, 8-byte
+ * aligned; x must be 2-byte aligned.  workspace: device, 16-byte aligned, at
+ * least mxfp4_quantize_noise_workspace_bytes (never 0). */
+mxfp4_status mxfp4_quantize_noise(const uint16_t *x, int64_t R, int64_t C, int64_t ldx,
+                                  int fmt, int rounding, int hadamard, int axis, uint64_t seed,
+                                  mxfp4_tensor *out, double *stats, void *workspace, size_t ws_bytes,
+                                  hipStream_t stream);
+
 /* A static, human-readable description of a status code. */
 const char *mxfp4_status_string(int status);
 

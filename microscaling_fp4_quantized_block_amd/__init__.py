@@ -70,6 +70,11 @@ def _load_library() -> ctypes.CDLL:
     lib.mxfp4_quantize_mse_workspace_bytes.argtypes = [i32, i32, i64, i64, i32, P(sz)]
     lib.mxfp4_quantize_mse.restype = i32
     lib.mxfp4_quantize_mse.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, P(MxTensorStruct), vp, sz, vp]
+    lib.mxfp4_quantize_noise_workspace_bytes.restype = i32
+    lib.mxfp4_quantize_noise_workspace_bytes.argtypes = [i32, i32, i64, i64, i32, P(sz)]
+    lib.mxfp4_quantize_noise.restype = i32
+    lib.mxfp4_quantize_noise.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, u64, P(MxTensorStruct), vp, vp, sz,
+                                         vp]
     lib.mxfp4_quantization_noise_workspace_bytes.restype = i32
     lib.mxfp4_quantization_noise_workspace_bytes.argtypes = [P(MxTensorStruct), P(sz)]
     lib.mxfp4_quantization_noise.restype = i32
@@ -294,6 +299,36 @@ def mxfp4_quantization_noise(x: torch.Tensor, q: QTensor, axis: int = 1, out: Op
     return out
 
 
+def mxfp4_quantize_noise_workspace_bytes(fmt: str, hadamard: bool, R: int, C: int, axis: int = 1) -> int:
+    b = ctypes.c_size_t()
+    _check(lib.mxfp4_quantize_noise_workspace_bytes(FMT[fmt], int(bool(hadamard)), R, C, axis, ctypes.byref(b)))
+    return b.value
+
+
+def mxfp4_quantize_noise(x: torch.Tensor, fmt: str = "mx", rounding: str = "sr", hadamard: bool = False,
+                         axis: int = 1, seed: int = 0, out: Optional[QTensor] = None,
+                         stats: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """(q, stats): mxfp4_quantize(x, ...) and, from the same pass, the float64
+    [3] sums of mxfp4_quantization_noise (sum y^2, sum (Q(y) - y)^2, elements
+    left out)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bfloat16 CUDA/HIP tensor with unit stride along its last dimension")
+    R, C = x.shape
+    rows, k = (R, C) if axis == 1 else (C, R)
+    if out is None:
+        out = empty_qtensor(fmt, rows, k, hadamard, x.device)
+    if stats is None:
+        stats = torch.empty(3, dtype=torch.float64, device=x.device)
+    ws_bytes = mxfp4_quantize_noise_workspace_bytes(fmt, hadamard, R, C, axis)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    st = out.as_struct()
+    _check(lib.mxfp4_quantize_noise(_ptr(x), R, C, x.stride(0), FMT[fmt], ROUNDING[rounding], int(bool(hadamard)),
+                                    int(axis), int(seed) & (2 ** 64 - 1), ctypes.byref(st), _ptr(stats),
+                                    _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return out, stats
+
+
 def gradient_noise_ratio(x: torch.Tensor, q: QTensor, axis: int = 1):
     """(ratio, below): ratio = ||y|| / ||Q(y) - y|| for the quantized operand,
     and whether it falls below sqrt(3), the threshold under which quantized
@@ -312,5 +347,6 @@ __all__ = ["QTensor", "MxFp4Error", "mxfp4_tensor_bytes", "mxfp4_quantize_worksp
            "mxfp4_dequantize", "mxfp4_gemm_workspace_bytes", "mxfp4_gemm", "mxfp4_gemm_bf16", "mxfp4_status_string",
            "mxfp4_quantize_gemm_workspace_bytes", "mxfp4_quantize_gemm",
            "mxfp4_quantization_noise_workspace_bytes", "mxfp4_quantization_noise", "gradient_noise_ratio",
+           "mxfp4_quantize_noise_workspace_bytes", "mxfp4_quantize_noise",
            "mxfp4_quantize_mse_workspace_bytes", "mxfp4_quantize_mse",
            "quantize", "dequantize", "gemm", "quantize_gemm", "empty_qtensor", "lib", "LIB_PATH"]

@@ -251,4 +251,49 @@ __device__ __forceinline__ uint32_t sr_encode8(const float xs[8], const uint32_t
   return even | (odd << 4);
 }
 
+// ---------------------------------------------------------------------------
+// Signal and quantization-noise sums (binary64): for 8 elements y and their
+// codes (one 32-bit word), Q(y) = E2M1(code) * sc exactly,
+//   s0 += y^2, s1 += (Q(y) - y)^2,
+// squares accumulated with fused multiply-adds (y * y is exact, so the
+// same as a multiply and an add).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void noise_accum8(const float y[8], uint32_t codes, double sc, double& s0, double& s1) {
+  float g[8];
+  const f32x2 g0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+  const f32x2 g1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+  const f32x2 g2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+  const f32x2 g3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+  g[0] = g0[0]; g[1] = g0[1]; g[2] = g1[0]; g[3] = g1[1];
+  g[4] = g2[0]; g[5] = g2[1]; g[6] = g3[0]; g[7] = g3[1];
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const double yv = (double)y[j];
+    const double d = (double)g[j] * sc - yv;
+    s0 = __builtin_fma(yv, yv, s0);
+    s1 = __builtin_fma(d, d, s1);
+  }
+}
+
+// Sum of three per-thread values over a 256-thread workgroup (butterflies
+// within each wave, then the four waves in a fixed order) into out[0..2] by
+// thread 0.  Every thread of the workgroup must call it.
+__device__ __forceinline__ void block_sum3(double& a, double& b, double& c, double* out) {
+  __shared__ double red[3][4];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    a += __shfl_xor(a, off, 64);
+    b += __shfl_xor(b, off, 64);
+    c += __shfl_xor(c, off, 64);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { red[0][w] = a; red[1][w] = b; red[2][w] = c; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    out[0] = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+    out[1] = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+    out[2] = (red[2][0] + red[2][1]) + (red[2][2] + red[2][3]);
+  }
+}
+
 }  // namespace mxfp4

@@ -81,6 +81,59 @@ mxfp4_status mxfp4_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx
   return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
 }
 
+// Workspace of mxfp4_quantize_noise: the quantizer's (NVFP4 amax partials),
+// padded to 16 bytes, then the partial sums.
+static size_t quantize_noise_ws(int fmt, int hadamard, int64_t R, int64_t C, int axis, size_t* amax_bytes) {
+  const size_t q = (mxfp4::quantize_workspace_bytes(fmt, R, C) + 15) & ~(size_t)15;
+  *amax_bytes = q;
+  return q + (size_t)mxfp4::quantize_noise_parts(fmt, hadamard, R, C, axis) * 3 * sizeof(double);
+}
+
+mxfp4_status mxfp4_quantize_noise_workspace_bytes(int fmt, int hadamard, int64_t R, int64_t C, int axis,
+                                                  size_t* bytes) {
+  if (!fmt_ok(fmt) || (hadamard != 0 && hadamard != 1) || R < 0 || C < 0 || (axis != 0 && axis != 1) || !bytes)
+    return MXFP4_ERR_INVALID_ARG;
+  const int64_t k = axis == 1 ? C : R;
+  if (k % block_of(fmt) != 0 || (hadamard && k % 32 != 0)) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  if (R > 0 && C > kMaxElems / R) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  size_t a;
+  *bytes = quantize_noise_ws(fmt, hadamard, R, C, axis, &a);
+  return MXFP4_OK;
+}
+
+mxfp4_status mxfp4_quantize_noise(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int fmt, int rounding,
+                                  int hadamard, int axis, uint64_t seed, mxfp4_tensor* out, double* stats,
+                                  void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!fmt_ok(fmt) || (rounding != MXFP4_RTN && rounding != MXFP4_SR) || (hadamard != 0 && hadamard != 1) ||
+      (axis != 0 && axis != 1) || !out || !stats)
+    return MXFP4_ERR_INVALID_ARG;
+  if (R < 0 || C < 0 || ldx < C || ldx < 1) return MXFP4_ERR_INVALID_ARG;
+  const int64_t rows = axis == 1 ? R : C, k = axis == 1 ? C : R;
+  if (k % block_of(fmt) != 0 || (hadamard && k % 32 != 0)) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  if (R > 0 && C > kMaxElems / R) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  if (out->fmt != fmt || out->rows != rows || out->k != k || out->hadamard != hadamard)
+    return MXFP4_ERR_INVALID_ARG;
+  if (!aligned(stats, 8)) return MXFP4_ERR_INVALID_ARG;
+  if (rows > 0 && k > 0) {
+    if (!x || !out->codes || !out->scales || !aligned(x, 2) || !aligned(out->codes, 16)) return MXFP4_ERR_INVALID_ARG;
+    if (fmt == MXFP4_FMT_NV && !out->tensor_scale) return MXFP4_ERR_INVALID_ARG;
+  }
+  size_t amax_bytes;
+  const size_t need = quantize_noise_ws(fmt, hadamard, R, C, axis, &amax_bytes);
+  if (!workspace || ws_bytes < need || !aligned(workspace, 16)) return MXFP4_ERR_WORKSPACE;
+  hipError_t e;
+  if (rows == 0 || k == 0) {
+    // nothing to quantize: the finalize over no partials writes zero sums
+    mxfp4::launch_noise_finalize(nullptr, 0, stats, stream);
+    e = hipGetLastError();
+  } else {
+    e = mxfp4::launch_quantize_noise(x, R, C, ldx, fmt, rounding, hadamard, axis, seed, out->codes, out->scales,
+                                     out->tensor_scale, (uint32_t*)workspace, stats,
+                                     (double*)((uint8_t*)workspace + amax_bytes), stream);
+  }
+  return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
+}
+
 mxfp4_status mxfp4_dequantize(const mxfp4_tensor* q, float* y, int64_t ldy, hipStream_t stream) {
   if (!q || !fmt_ok(q->fmt) || q->rows < 0 || q->k < 0) return MXFP4_ERR_INVALID_ARG;
   if (q->k % block_of(q->fmt) != 0) return MXFP4_ERR_UNSUPPORTED_SHAPE;

@@ -64,6 +64,15 @@ hipError_t launch_quantize_mse(const uint16_t* x, int64_t R, int64_t C, int64_t 
 // Signal and quantization-noise sums of a quantized operand (noise.hip):
 // workspace = 3 doubles per workgroup of the pass.
 size_t noise_workspace_bytes(int fmt, int hadamard, int64_t rows, int64_t K);
+// Fixed-order sum of nparts partial triples into stats[0..2].
+void launch_noise_finalize(const double* partials, int64_t nparts, double* stats, hipStream_t s);
+// Quantize with the signal / noise sums: quantize_noise_parts is the largest
+// number of partial triples (doubles x 3) any launch plan of the call writes.
+int64_t quantize_noise_parts(int fmt, int hadamard, int64_t R, int64_t C, int axis);
+hipError_t launch_quantize_noise(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int fmt, int rounding,
+                                 int hadamard, int axis, uint64_t seed, uint8_t* codes, uint8_t* scales,
+                                 float* tensor_scale, uint32_t* amax_partials, double* stats, double* parts,
+                                 hipStream_t stream);
 hipError_t launch_noise(const uint16_t* x, int64_t ldx, int axis, int fmt, int hadamard, int64_t rows, int64_t K,
                         const uint8_t* codes, const uint8_t* scales, const float* ts, double* stats,
                         double* partials, hipStream_t stream);

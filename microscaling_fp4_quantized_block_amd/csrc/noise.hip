@@ -37,24 +37,6 @@ struct NoiseArgs {
   double* partials;         // 3 per workgroup
 };
 
-__device__ __forceinline__ void block_sum3(double& a, double& b, double& c, double* out) {
-  __shared__ double red[3][4];
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    a += __shfl_xor(a, off, 64);
-    b += __shfl_xor(b, off, 64);
-    c += __shfl_xor(c, off, 64);
-  }
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) { red[0][w] = a; red[1][w] = b; red[2][w] = c; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    out[0] = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
-    out[1] = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
-    out[2] = (red[2][0] + red[2][1]) + (red[2][2] + red[2][3]);
-  }
-}
-
 template <int FMT, bool HAD, int AXIS, int U>
 __global__ void __launch_bounds__(256) noise_kernel(NoiseArgs a) {
   constexpr int BS = (FMT == FMT_MX) ? 32 : 16;
@@ -141,17 +123,46 @@ __global__ void __launch_bounds__(256) noise_kernel(NoiseArgs a) {
   block_sum3(s0, s1, n, a.partials + 3 * (int64_t)blockIdx.x);
 }
 
-// Fixed-order sum of the partials: thread t adds partials t, t + 256, ...,
-// then a fixed tree.
-__global__ void __launch_bounds__(256) noise_finalize_kernel(const double* __restrict__ partials, int nparts,
-                                                             double* __restrict__ stats) {
+// Fixed-order sum of the partials: 1024 threads, thread t adds partials t,
+// t + 1024, ... (four loads in flight), then butterflies within each wave and
+// the 16 wave sums in a fixed order.
+__global__ void __launch_bounds__(1024) noise_finalize_kernel(const double* __restrict__ partials, int64_t nparts,
+                                                              double* __restrict__ stats) {
+  __shared__ double red[3][16];
   double a = 0.0, b = 0.0, c = 0.0;
-  for (int p = threadIdx.x; p < nparts; p += 256) {
+  int64_t p = threadIdx.x;
+  for (; p + 3 * 1024 < nparts; p += 4 * 1024) {
+    double v[4][3];
+#pragma unroll
+    for (int q = 0; q < 4; q++)
+#pragma unroll
+      for (int j = 0; j < 3; j++) v[q][j] = partials[3 * (p + q * 1024) + j];
+#pragma unroll
+    for (int q = 0; q < 4; q++) { a += v[q][0]; b += v[q][1]; c += v[q][2]; }
+  }
+  for (; p < nparts; p += 1024) {
     a += partials[3 * p];
     b += partials[3 * p + 1];
     c += partials[3 * p + 2];
   }
-  block_sum3(a, b, c, stats);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    a += __shfl_xor(a, off, 64);
+    b += __shfl_xor(b, off, 64);
+    c += __shfl_xor(c, off, 64);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { red[0][w] = a; red[1][w] = b; red[2][w] = c; }
+  __syncthreads();
+  if (threadIdx.x < 3) {
+    double t = 0.0;
+    for (int k = 0; k < 16; k++) t += red[threadIdx.x][k];
+    stats[threadIdx.x] = t;
+  }
+}
+
+void launch_noise_finalize(const double* partials, int64_t nparts, double* stats, hipStream_t s) {
+  hipLaunchKernelGGL(noise_finalize_kernel, dim3(1), dim3(1024), 0, s, partials, nparts, stats);
 }
 
 // One unit per thread up to 2^16 workgroups (16.7 M units), so that many
@@ -216,7 +227,7 @@ hipError_t launch_noise(const uint16_t* x, int64_t ldx, int axis, int fmt, int h
     if (hadamard) launch_noise_axis<FMT_NV, true>(a, axis, u, g, stream);
     else launch_noise_axis<FMT_NV, false>(a, axis, u, g, stream);
   }
-  hipLaunchKernelGGL(noise_finalize_kernel, dim3(1), dim3(256), 0, stream, partials, (int)g, stats);
+  launch_noise_finalize(partials, g, stats, stream);
   return hipGetLastError();
 }
 

@@ -270,12 +270,15 @@ struct RowArgs {
   uint8_t* scales;
   uint64_t seed;
   const float* st;        // NVFP4 tensor scale (device), written by the finalize kernel
+  double* parts;          // STATS: 3 binary64 sums per workgroup of the launch
 };
 
 // LOAD bit 0: element loads (the input is not 16-byte aligned), else 16-byte
 // loads.  LOAD bit 1: rows are padded (ldx > C), so a chunk's row comes from a
 // division; else the slice is contiguous.
-template <int FMT, int RND, bool HAD, int LOAD>
+// STATS: also the signal and noise sums of the operand (noise_accum8; blocks
+// with a NaN scale byte counted as left out), one triple per workgroup.
+template <int FMT, int RND, bool HAD, int LOAD, bool STATS = false>
 __global__ void __launch_bounds__(256) quant_rows_kernel(RowArgs a) {
   constexpr int LPB = (FMT == FMT_MX) ? 4 : 2;   // lanes per scale block
   constexpr int U = kRowChunksPerWG / 256;
@@ -283,6 +286,7 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(RowArgs a) {
   const uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32);
   const uint32_t p = threadIdx.x & 3u;           // position in the quad
   const uint32_t base = blockIdx.x * (uint32_t)kRowChunksPerWG + threadIdx.x;
+  double s0 = 0.0, s1 = 0.0, left = 0.0;
   uint32_t w[U][4];
 #pragma unroll
   for (int u = 0; u < U; u++) {
@@ -340,7 +344,13 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(RowArgs a) {
     // outputs are not re-read by this kernel: stream them past the caches
     __builtin_nontemporal_store(packed, (uint32_t*)(a.codes + (uint64_t)t * 4));
     if ((p & (LPB - 1)) == 0) __builtin_nontemporal_store((uint8_t)byte, a.scales + t / LPB);
+    if constexpr (STATS) {
+      if (nonfinite) left += 8.0;
+      else noise_accum8(y, packed, FMT == FMT_MX ? (double)e8m0_value(byte) : (double)e4m3_value(byte) * (double)st,
+                        s0, s1);
+    }
   }
+  if constexpr (STATS) block_sum3(s0, s1, left, a.parts + 3 * (int64_t)blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -360,9 +370,10 @@ struct ColArgs {
   uint8_t* scales;
   uint64_t seed;
   const float* st;
+  double* parts;          // STATS (tile kernel): 3 binary64 sums per workgroup of the launch
 };
 
-template <int FMT, int RND, bool HAD>
+template <int FMT, int RND, bool HAD, bool STATS = false>
 __global__ void __launch_bounds__(256) quant_cols_tile_kernel(ColArgs a) {
   constexpr int BS = (FMT == FMT_MX) ? 32 : 16;
   __shared__ __attribute__((aligned(16))) uint16_t tile[256 * 64];   // 32 KB
@@ -399,6 +410,7 @@ __global__ void __launch_bounds__(256) quant_cols_tile_kernel(ColArgs a) {
   const int64_t c = c0 + l;
   const int64_t rw0 = r0 + 64 * w;                  // first contraction index of this wave
   const bool active = rw0 < R && c < C;
+  double s0 = 0.0, s1 = 0.0, left = 0.0;
   // two halves of 32 rows (one MXFP4 block, two NVFP4 blocks); R is a
   // multiple of the block, so a half is whole, half-filled (NVFP4) or empty
   uint32_t out[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
@@ -431,6 +443,12 @@ __global__ void __launch_bounds__(256) quant_cols_tile_kernel(ColArgs a) {
         }
         const uint32_t dummy[4] = {0, 0, 0, 0};
         out[h][e0 / 8] = nonfinite ? 0u : encode8<FMT, RND, false>(y + e0, dummy, byte, mul, rw);
+        // (rows past R are zeros with zero codes: they add nothing)
+        if constexpr (STATS) {
+          if (nonfinite) left += 8.0;
+          else noise_accum8(y + e0, out[h][e0 / 8],
+                            FMT == FMT_MX ? (double)e8m0_value(byte) : (double)e4m3_value(byte) * (double)st, s0, s1);
+        }
       }
       sbyte[h][b] = byte;
     }
@@ -480,6 +498,7 @@ __global__ void __launch_bounds__(256) quant_cols_tile_kernel(ColArgs a) {
       if ((R - rr) >= 32) *(uint2*)(dst + 8) = make_uint2(v[2], v[3]);
     }
   }
+  if constexpr (STATS) block_sum3(s0, s1, left, a.parts + 3 * ((int64_t)blockIdx.y * gridDim.x + blockIdx.x));
 }
 
 // Small transposing kernel for ragged or unaligned inputs: a lane holds
@@ -563,57 +582,78 @@ static int grid_for(int64_t work_items, int per_block, int64_t cap) {
   return (int)(g < 1 ? 1 : g);
 }
 
-template <int FMT, int RND, bool HAD>
-static void launch_rows(const RowArgs& a, int load, hipStream_t s) {
+// Each launcher returns the number of workgroups it launched (the STATS
+// partial triples it wrote); with launch = false it only counts them.
+template <int FMT, int RND, bool HAD, bool STATS>
+static int64_t launch_rows(const RowArgs& a, int load, bool launch, hipStream_t s) {
   const int grid = (int)(((uint64_t)a.total + kRowChunksPerWG - 1) / kRowChunksPerWG);
+  if (!launch) return grid;
   switch (load) {
-    case 0: hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, 0>), dim3(grid), dim3(256), 0, s, a); break;
-    case 1: hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, 1>), dim3(grid), dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, 2>), dim3(grid), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, 3>), dim3(grid), dim3(256), 0, s, a); break;
+    case 0: hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, 0, STATS>), dim3(grid), dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, 1, STATS>), dim3(grid), dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, 2, STATS>), dim3(grid), dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, 3, STATS>), dim3(grid), dim3(256), 0, s, a); break;
   }
+  return grid;
 }
 
-template <int FMT, int RND, bool HAD>
-static void launch_cols(ColArgs a, bool tiled, bool vec, hipStream_t s) {
+// STATS only with the tiled kernel (the caller sends the other inputs
+// through quantize, then the separate noise pass).
+template <int FMT, int RND, bool HAD, bool STATS>
+static int64_t launch_cols(ColArgs a, bool tiled, bool vec, bool launch, hipStream_t s) {
   // grid.y is limited to 65535: larger inputs go in slabs of rows
   const int64_t rows_per = tiled ? 256 : 128;
   const int64_t slab = 65535 * rows_per;
+  int64_t n = 0;
   for (int64_t r = 0; r < a.R; r += slab) {
     a.r_off = r;
     const int64_t nr = (a.R - r) < slab ? (a.R - r) : slab;
     const int64_t cols_per = tiled ? 64 : 128;
     dim3 grid((unsigned)((a.C + cols_per - 1) / cols_per), (unsigned)((nr + rows_per - 1) / rows_per));
-    if (tiled) hipLaunchKernelGGL((quant_cols_tile_kernel<FMT, RND, HAD>), grid, dim3(256), 0, s, a);
-    else if (vec) hipLaunchKernelGGL((quant_cols_kernel<FMT, RND, HAD, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((quant_cols_kernel<FMT, RND, HAD, false>), grid, dim3(256), 0, s, a);
+    if (launch) {
+      if (tiled) hipLaunchKernelGGL((quant_cols_tile_kernel<FMT, RND, HAD, STATS>), grid, dim3(256), 0, s, a);
+      else if (vec) hipLaunchKernelGGL((quant_cols_kernel<FMT, RND, HAD, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((quant_cols_kernel<FMT, RND, HAD, false>), grid, dim3(256), 0, s, a);
+    }
+    const int64_t wgs = (int64_t)grid.x * grid.y;
+    n += wgs;
+    if (STATS) a.parts += 3 * wgs;
   }
+  return n;
 }
 
 // Chunk ranges of one launch stay below 2^31 so the kernels index in 32 bits.
 constexpr uint64_t kSliceChunks = (uint64_t)1 << 30;
 
-template <int FMT, int RND, bool HAD>
-static void launch_rows_sliced(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, bool aligned16, uint64_t seed,
-                               uint8_t* codes, uint8_t* scales, const float* st, hipStream_t s) {
+template <int FMT, int RND, bool HAD, bool STATS>
+static int64_t launch_rows_sliced(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, bool aligned16,
+                                  uint64_t seed, uint8_t* codes, uint8_t* scales, const float* st, double* parts,
+                                  bool launch, hipStream_t s) {
   constexpr int LPB = (FMT == FMT_MX) ? 4 : 2;
   const uint64_t cpr = (uint64_t)C / 8;
   RowArgs a{};
   a.ldx = ldx;
   a.seed = seed;
   a.st = st;
+  a.parts = parts;
+  int64_t n = 0;
+  auto go = [&](int load) {
+    const int64_t g = launch_rows<FMT, RND, HAD, STATS>(a, load, launch, s);
+    n += g;
+    if (STATS) a.parts += 3 * g;
+  };
   const int elem = aligned16 ? 0 : 1;
-  auto packed_range = [&](const uint16_t* xr, uint64_t t0, uint64_t n) {
-    // a contiguous range of n chunks starting at global chunk t0
-    for (uint64_t off = 0; off < n; off += kSliceChunks) {
-      const uint64_t m = (n - off) < kSliceChunks ? (n - off) : kSliceChunks;
+  auto packed_range = [&](const uint16_t* xr, uint64_t t0, uint64_t m_all) {
+    // a contiguous range of m_all chunks starting at global chunk t0
+    for (uint64_t off = 0; off < m_all; off += kSliceChunks) {
+      const uint64_t m = (m_all - off) < kSliceChunks ? (m_all - off) : kSliceChunks;
       a.x = xr + off * 8;
       a.cpr = make_fastdiv(1);
       a.total = (uint32_t)m;
       a.tbase = t0 + off;
       a.codes = codes + (t0 + off) * 4;
       a.scales = scales + (t0 + off) / LPB;
-      launch_rows<FMT, RND, HAD>(a, elem, s);
+      go(elem);
     }
   };
   if (ldx == C || R == 1) {
@@ -628,32 +668,31 @@ static void launch_rows_sliced(const uint16_t* x, int64_t R, int64_t C, int64_t 
       a.tbase = (uint64_t)r * cpr;
       a.codes = codes + a.tbase * 4;
       a.scales = scales + a.tbase / LPB;
-      launch_rows<FMT, RND, HAD>(a, 2 | elem, s);
+      go(2 | elem);
     }
   } else {
     for (int64_t r = 0; r < R; r++) packed_range(x + r * ldx, (uint64_t)r * cpr, cpr);
   }
+  return n;
 }
 
-template <int FMT, int RND, bool HAD>
-static void launch_one(int axis, const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint64_t seed,
-                       uint8_t* codes, uint8_t* scales, const float* st, hipStream_t s) {
+template <int FMT, int RND, bool HAD, bool STATS>
+static int64_t launch_one(int axis, const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint64_t seed,
+                          uint8_t* codes, uint8_t* scales, const float* st, double* parts, hipStream_t s) {
   const bool aligned16 = (((uintptr_t)x & 15u) == 0) && (ldx % 8 == 0);
-  if (axis == 1) {
-    launch_rows_sliced<FMT, RND, HAD>(x, R, C, ldx, aligned16, seed, codes, scales, st, s);
-  } else {
-    ColArgs ca{x, R, C, ldx, 0, codes, scales, seed, st};
-    const bool tiled = aligned16 && (C % 8 == 0);
-    const bool vec = (((uintptr_t)x & 3u) == 0) && (ldx % 2 == 0);
-    launch_cols<FMT, RND, HAD>(ca, tiled, vec, s);
-  }
+  if (axis == 1)
+    return launch_rows_sliced<FMT, RND, HAD, STATS>(x, R, C, ldx, aligned16, seed, codes, scales, st, parts, true, s);
+  ColArgs ca{x, R, C, ldx, 0, codes, scales, seed, st, parts};
+  const bool tiled = aligned16 && (C % 8 == 0);
+  const bool vec = (((uintptr_t)x & 3u) == 0) && (ldx % 2 == 0);
+  return launch_cols<FMT, RND, HAD, STATS>(ca, tiled, vec, true, s);
 }
 
-template <int FMT, int RND>
-static void launch_had(bool had, int axis, const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint64_t seed,
-                       uint8_t* codes, uint8_t* scales, const float* st, hipStream_t s) {
-  if (had) launch_one<FMT, RND, true>(axis, x, R, C, ldx, seed, codes, scales, st, s);
-  else launch_one<FMT, RND, false>(axis, x, R, C, ldx, seed, codes, scales, st, s);
+template <int FMT, int RND, bool STATS = false>
+static int64_t launch_had(bool had, int axis, const uint16_t* x, int64_t R, int64_t C, int64_t ldx, uint64_t seed,
+                          uint8_t* codes, uint8_t* scales, const float* st, hipStream_t s, double* parts = nullptr) {
+  if (had) return launch_one<FMT, RND, true, STATS>(axis, x, R, C, ldx, seed, codes, scales, st, parts, s);
+  return launch_one<FMT, RND, false, STATS>(axis, x, R, C, ldx, seed, codes, scales, st, parts, s);
 }
 
 // Tensor amax of an NVFP4 input into s_t (device): partial maxima, then the
@@ -726,6 +765,57 @@ hipError_t launch_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx,
     if (rounding == RND_RTN) launch_had<FMT_NV, RND_RTN>(hadamard, axis, x, R, C, ldx, seed, codes, scales, tensor_scale, stream);
     else launch_had<FMT_NV, RND_SR>(hadamard, axis, x, R, C, ldx, seed, codes, scales, tensor_scale, stream);
   }
+  return hipGetLastError();
+}
+
+// Quantize with the signal / noise sums (mxfp4_quantize_noise).  The row and
+// the tiled transposing kernels add the sums as they encode; inputs that take
+// the small transposing kernel are quantized, then summed by the separate
+// noise pass (the same sums).
+int64_t quantize_noise_parts(int fmt, int hadamard, int64_t R, int64_t C, int axis) {
+  if (R == 0 || C == 0) return 1;
+  int64_t n;
+  if (axis == 1) {
+    // the launch plan depends on whether the rows are packed: count both
+    const int64_t a = launch_rows_sliced<FMT_MX, RND_RTN, false, true>(nullptr, R, C, C, true, 0, nullptr, nullptr,
+                                                                      nullptr, nullptr, false, nullptr);
+    const int64_t b = launch_rows_sliced<FMT_MX, RND_RTN, false, true>(nullptr, R, C, C + 8, true, 0, nullptr,
+                                                                      nullptr, nullptr, nullptr, false, nullptr);
+    n = a > b ? a : b;
+  } else {
+    ColArgs ca{nullptr, R, C, C, 0, nullptr, nullptr, 0, nullptr, nullptr};
+    const int64_t a = launch_cols<FMT_MX, RND_RTN, false, true>(ca, true, true, false, nullptr);
+    const int64_t b = (int64_t)(noise_workspace_bytes(fmt, hadamard, C, R) / (3 * sizeof(double)));
+    n = a > b ? a : b;
+  }
+  return n < 1 ? 1 : n;
+}
+
+hipError_t launch_quantize_noise(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int fmt, int rounding,
+                                 int hadamard, int axis, uint64_t seed, uint8_t* codes, uint8_t* scales,
+                                 float* tensor_scale, uint32_t* amax_partials, double* stats, double* parts,
+                                 hipStream_t stream) {
+  const bool aligned16 = (((uintptr_t)x & 15u) == 0) && (ldx % 8 == 0);
+  if (axis == 0 && !(aligned16 && C % 8 == 0)) {
+    hipError_t e = launch_quantize(x, R, C, ldx, fmt, rounding, hadamard, axis, seed, codes, scales, tensor_scale,
+                                   amax_partials, stream);
+    if (e != hipSuccess) return e;
+    return launch_noise(x, ldx, axis, fmt, hadamard, C, R, codes, scales, tensor_scale, stats, parts, stream);
+  }
+  if (fmt == FMT_NV) launch_tensor_scale(x, R, C, ldx, hadamard, axis, tensor_scale, amax_partials, stream);
+  int64_t n;
+  if (fmt == FMT_MX) {
+    if (rounding == RND_RTN)
+      n = launch_had<FMT_MX, RND_RTN, true>(hadamard, axis, x, R, C, ldx, seed, codes, scales, tensor_scale, stream, parts);
+    else
+      n = launch_had<FMT_MX, RND_SR, true>(hadamard, axis, x, R, C, ldx, seed, codes, scales, tensor_scale, stream, parts);
+  } else {
+    if (rounding == RND_RTN)
+      n = launch_had<FMT_NV, RND_RTN, true>(hadamard, axis, x, R, C, ldx, seed, codes, scales, tensor_scale, stream, parts);
+    else
+      n = launch_had<FMT_NV, RND_SR, true>(hadamard, axis, x, R, C, ldx, seed, codes, scales, tensor_scale, stream, parts);
+  }
+  launch_noise_finalize(parts, n, stats, stream);
   return hipGetLastError();
 }
 

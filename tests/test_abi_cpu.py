@@ -105,6 +105,56 @@ def test_quantize_rejects_bad_arguments(mx):
     assert quantize(mx, R=64, C=0, ldx=1, out=desc(mx, rows=64, k=0)) == OK
 
 
+def qnoise(mx, R=64, C=256, ldx=256, fmt=0, rnd=1, had=0, axis=1, out=None, stats=FAKE, ws=FAKE, ws_bytes=1 << 20,
+           x=FAKE):
+    if out is None:
+        rows, k = (R, C) if axis == 1 else (C, R)
+        out = desc(mx, fmt, had, rows, k)
+    return mx.lib.mxfp4_quantize_noise(x, R, C, ldx, fmt, rnd, had, axis, 0,
+                                       ctypes.byref(out) if out != "null" else None, stats, ws, ws_bytes, None)
+
+
+def qnoise_ws(mx, fmt, had, R, C, axis):
+    b = ctypes.c_size_t()
+    s = mx.lib.mxfp4_quantize_noise_workspace_bytes(fmt, had, R, C, axis, ctypes.byref(b))
+    return s, b.value
+
+
+def test_quantize_noise_rejects_bad_arguments(mx):
+    assert qnoise(mx, fmt=3) == INVALID
+    assert qnoise(mx, rnd=2) == INVALID
+    assert qnoise(mx, axis=2) == INVALID
+    assert qnoise(mx, out="null") == INVALID
+    assert qnoise(mx, stats=None) == INVALID
+    assert qnoise(mx, stats=FAKE + 4) == INVALID                   # stats: 8-byte aligned doubles
+    assert qnoise(mx, ldx=100) == INVALID
+    assert qnoise(mx, C=48, ldx=48) == SHAPE
+    assert qnoise(mx, out=desc(mx, rows=63)) == INVALID
+    assert qnoise(mx, x=None) == INVALID
+    assert qnoise(mx, x=FAKE + 1) == INVALID                       # bf16 input: 2-byte aligned
+    assert qnoise(mx, out=desc(mx, codes=FAKE + 4)) == INVALID
+    assert qnoise(mx, fmt=1, out=desc(mx, 1, ts=None)) == INVALID
+    assert qnoise(mx, ws=None) == WORKSPACE
+    assert qnoise(mx, ws=FAKE + 8) == WORKSPACE                    # 16-byte aligned workspace
+    assert qnoise(mx, ws_bytes=95) == WORKSPACE                     # 4 workgroups x 24 bytes needed
+
+
+def test_quantize_noise_workspace_bytes(mx):
+    assert qnoise_ws(mx, 3, 0, 64, 256, 1)[0] == INVALID
+    assert qnoise_ws(mx, 0, 0, 64, 48, 1)[0] == SHAPE
+    # MXFP4 rows: one triple of doubles per workgroup of 512 16-byte chunks
+    assert qnoise_ws(mx, 0, 0, 50432, 3072, 1) == (OK, 24 * (50432 * 3072 // 8 // 512))
+    # transposed: the larger of the tiled kernel's 64 x 256 tiles and the
+    # separate noise pass's workgroups (256 units of 32)
+    assert qnoise_ws(mx, 0, 0, 50432, 3072, 0) == (OK, 24 * (3072 * 50432 // 32 // 256))
+    # NVFP4: the quantizer's amax partials (16-byte padded) come first
+    s, b = qnoise_ws(mx, 1, 0, 4096, 4096, 1)
+    q = mx.mxfp4_quantize_workspace_bytes("nv", 4096, 4096)
+    assert s == OK and b == ((q + 15) // 16 * 16) + 24 * (4096 * 4096 // 8 // 512)
+    # empty input: room for one triple
+    assert qnoise_ws(mx, 0, 0, 0, 256, 1) == (OK, 24)
+
+
 def test_dequantize_rejects_bad_arguments(mx):
     d = desc(mx)
     assert mx.lib.mxfp4_dequantize(None, FAKE, 256, None) == INVALID
