@@ -453,7 +453,17 @@ def sweep(args):
                 gbps = nbytes / t / 1e9
                 rows.append((cfg, "noise", f"{name} {rnd} axis{axis}", f"{R}x{Cc}", t * 1e6, gbps, "GB/s", "hbm",
                              gbps / PEAK_HBM_GBPS))
-                del st, ws
+                # the same sums computed while quantizing (one pass; bytes:
+                # the quantizer's, input once + codes and scales written)
+                qf = mx.empty_qtensor(fmt, q.rows, q.k, had, dev)
+                fws = torch.empty(mx.mxfp4_quantize_noise_workspace_bytes(fmt, had, R, Cc, axis), dtype=torch.uint8,
+                                  device=dev)
+                tf = timed(lambda: mx.mxfp4_quantize_noise(x, fmt, rnd, had, axis, 5, out=qf, stats=st,
+                                                           workspace=fws), True)
+                gbps_f = R * Cc * (2.0 + 0.5 + 1.0 / bs) / tf / 1e9
+                rows.append((cfg, "quantize+noise", f"{name} {rnd} axis{axis} (fused)", f"{R}x{Cc}", tf * 1e6, gbps_f,
+                             "GB/s", "hbm", gbps_f / PEAK_HBM_GBPS))
+                del st, ws, qf, fws
         if cfg == 3:
             # decode with the activation quantization fused into the GEMM,
             # against the two launches it replaces (quantize, then GEMM)
