@@ -13,14 +13,20 @@
 // The work is bound by HBM bandwidth (2 bytes in, ~0.53 bytes out per
 // element), so the kernels are built around 16-byte coalesced loads, integer
 // absmax on raw bit patterns, quad-level DPP reductions and the hardware
-// FP4 conversion for round-to-nearest (v_cvt_scalef32_pk_fp4_*, which
-// rounds x / 2^e to nearest-even with saturation).
+// FP4 conversions: v_cvt_scalef32_pk_fp4_* for round-to-nearest (x / 2^e to
+// nearest-even with saturation) and v_cvt_scalef32_sr_pk_fp4_f32 for
+// stochastic rounding (sr_encode8 in fp4_device.h), fed by Philox4x32-10.
 //
-// axis = 1 (rows): each lane owns 8 consecutive elements of one row, so a
-//   32-block spans a quad of 4 lanes (16-block: 2 lanes).
-// axis = 0 (transposed): each lane owns two adjacent columns and 32
-//   consecutive rows, so both column blocks sit in one lane's registers and the
-//   output (contraction along rows) is written as whole 16-byte block rows.
+// axis = 1 (rows, quant_rows_kernel): each lane owns 8 consecutive elements
+//   of one row, so a 32-block spans a quad of 4 lanes (16-block: 2 lanes).
+// axis = 0 (transposed, quant_cols_tile_kernel): a workgroup stages a
+//   256-row x 64-column tile in LDS, each lane then owns one column (so a
+//   contraction block sits in one lane's registers), and the codes and scale
+//   bytes go back through LDS so that the stores write whole row segments;
+//   inputs that are not 16-byte aligned take quant_cols_kernel (a lane owns
+//   two adjacent columns and 32 consecutive rows).
+// STATS instantiations of the row and tiled kernels also add the signal and
+// quantization-noise sums of the operand (mxfp4_quantize_noise).
 #include "fp4_device.h"
 #include "mxfp4_internal.h"
 
