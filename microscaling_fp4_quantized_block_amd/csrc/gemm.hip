@@ -234,7 +234,7 @@ __device__ __forceinline__ void block_barrier() {
 // is two rows of 32 consecutive columns: a 4-byte store per register writes
 // two whole 128-byte row segments, straight from the accumulator.  (A 4x4
 // transpose across lane quads into 16-byte stores, a quarter of the store
-// instructions, measured 3-12 % slower: its DPP exchanges need every value in
+// instructions, measured 4-12 % slower: its DPP exchanges need every value in
 // a VGPR.)  Whole blocks inside C store without checks; ragged edges check
 // each element.
 //
