@@ -519,8 +519,9 @@ def main():
         summarize_quant(*args.summarize_quant)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs on a single "
-              "MI355X; see the sharding note in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library runs the hot path "
+              "on a single MI355X; a multi-GPU layer would shard the GEMM's N or M dimension across devices)",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     import workloads

@@ -1,0 +1,71 @@
+"""Host logic of bench.py (no GPU): the one-GPU refusal, the traffic figure
+gated on the GEMM source it was measured on, and the rocprofv3 summaries."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and "--gpus 2" in r.stderr
+    assert r.stdout == ""
+
+
+def _traffic_file(tmp_path, digest, nbytes=123456.0):
+    p = tmp_path / "traffic.txt"
+    p.write_text("header line\n" + json.dumps({"bytes_per_launch": nbytes, "gemm_source_sha256_16": digest}))
+    return str(p)
+
+
+def test_traffic_only_for_the_measured_gemm_source(tmp_path):
+    assert bench.gemm_traffic(_traffic_file(tmp_path, bench.source_digest())) == 123456.0
+    assert bench.gemm_traffic(_traffic_file(tmp_path, "0" * 16)) is None
+    assert bench.gemm_traffic(str(tmp_path / "missing.txt")) is None
+    bad = tmp_path / "bad.txt"
+    bad.write_text("header\nnot json")
+    assert bench.gemm_traffic(str(bad)) is None
+
+
+def test_committed_traffic_matches_the_gemm_source():
+    """The committed PMC summary was taken on the current GEMM source, so the
+    benchmark reports its traffic figure."""
+    path = os.path.join(ROOT, "profiles", "gemm_mx_headline_traffic.txt")
+    assert bench.gemm_traffic(path) is not None
+
+
+def test_summarize_stats_table(tmp_path):
+    csv_path = tmp_path / "stats.csv"
+    csv_path.write_text('"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs"\n'
+                        '"gemm_kernel",12,3000000,250000,80.5,240000,260000\n'
+                        '"quant_kernel",26,700000,26923,19.5,13000,48000\n')
+    out = tmp_path / "out.md"
+    bench.summarize_stats(str(csv_path), str(out))
+    lines = out.read_text().splitlines()
+    assert lines[0].startswith("| kernel | calls | average us")
+    assert lines[2] == "| gemm_kernel | 12 | 250.0 | 240.0 | 260.0 | 80.5 |"
+    assert lines[3] == "| quant_kernel | 26 | 26.9 | 13.0 | 48.0 | 19.5 |"
+
+
+def test_sweep_plan_covers_every_configuration():
+    import workloads
+    plan = bench.sweep_plan()
+    assert sorted(plan) == [0, 1, 2, 3, 4, 5]
+    for cfg, (calls, gemms) in plan.items():
+        names = set(workloads.CONFIGS[cfg]["tensors"])
+        for name, rnd, axis in calls:
+            assert name in names and rnd in ("rtn", "sr") and axis in (0, 1)
+        for gname, ca, cb in gemms:
+            assert ca in calls and cb in calls
+    # the training configurations time the three GEMMs of every linear layer
+    for cfg in (4, 5):
+        kinds = {g[0].split()[-1] for g in plan[cfg][1]}
+        assert kinds == {"fwd", "dgrad", "wgrad"}
