@@ -4,7 +4,8 @@ and the stochastic-rounding counter crosses 2^32), and a transposed
 quantization with more than 65535 tiles of 256 rows (the grid is cut into
 slabs), both checked against the oracle (on rows sampled at every boundary,
 or in full); and GEMMs over the longest contraction the library takes
-(2^24), checked on sampled outputs."""
+(2^24), checked on sampled outputs.  The fused quantize + noise sums at the
+same slicing and slab boundaries, against the unfused calls."""
 import numpy as np
 import pytest
 import torch
@@ -90,3 +91,52 @@ def test_gemm_longest_contraction(oracle_mod, fmt, M, N):
     Co, So = oracle_mod.gemm(fmt, oa, ob)
     err = np.abs(C[np.ix_(rows, cols)].astype(np.float64) - Co)
     assert np.all(err <= 1e-5 * So), (err, So)
+
+
+def _same_stats(a, b, what):
+    a, b = a.cpu().numpy(), b.cpu().numpy()
+    for j in (0, 1):
+        assert abs(a[j] - b[j]) <= 1e-12 * max(abs(b[j]), 1e-300), (what, j, a[j], b[j])
+    assert a[2] == b[2], (what, a[2], b[2])
+
+
+@pytest.mark.parametrize("strided", [False, True])
+def test_quantize_noise_sliced_launches(strided):
+    """mxfp4_quantize_noise past 2^30 chunks of 8 elements, where the row
+    quantizer is launched in slices (packed rows: contiguous chunk ranges;
+    padded rows: ranges of whole rows) and each slice writes its own run of
+    partial sums: the tensor equals mxfp4_quantize's bit for bit and the sums
+    equal those of the separate noise pass (both are checked against the
+    oracle at smaller sizes)."""
+    mx = need_gpu()
+    R, C = (1 << 20) + 1, 8192             # 2^30 + 1024 chunks
+    free, _ = torch.cuda.mem_get_info()
+    if free < 60 * (1 << 30):
+        pytest.skip("needs about 50 GB of device memory")
+    say("max size quantize+noise", "strided" if strided else "packed", R, C)
+    base = torch.empty((R, C + (64 if strided else 0)), dtype=torch.bfloat16, device="cuda")
+    x = base[:, :C]
+    _fill_normal(base, 95, rows_per_slab=1 << 15, std=0.01)
+    q, st = mx.mxfp4_quantize_noise(x, "mx", "sr", False, 1, 41)
+    q2 = mx.mxfp4_quantize(x, "mx", "sr", False, 1, 41)
+    assert torch.equal(q.codes, q2.codes) and torch.equal(q.scales, q2.scales)
+    st2 = mx.mxfp4_quantization_noise(x, q2, 1)
+    _same_stats(st, st2, "sliced quantize+noise")
+    del base, x, q, q2
+    torch.cuda.empty_cache()
+
+
+def test_quantize_noise_transposed_slabs():
+    """The tiled transposing quantizer with sums past 65535 row tiles (two
+    grid slabs, each with its own run of partial sums)."""
+    mx = need_gpu()
+    R, C = 65538 * 256, 64
+    say("max size transposed quantize+noise", R, C)
+    x = torch.empty((R, C), dtype=torch.bfloat16, device="cuda")
+    _fill_normal(x, 96, std=0.5)
+    q, st = mx.mxfp4_quantize_noise(x, "nv", "sr", False, 0, 9)
+    q2 = mx.mxfp4_quantize(x, "nv", "sr", False, 0, 9)
+    assert torch.equal(q.codes, q2.codes) and torch.equal(q.scales, q2.scales)
+    assert torch.equal(q.tensor_scale, q2.tensor_scale)
+    st2 = mx.mxfp4_quantization_noise(x, q2, 0)
+    _same_stats(st, st2, "transposed slabs quantize+noise")
