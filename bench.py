@@ -47,6 +47,9 @@ def parse():
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into the traffic file")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "OUT_MD"),
                     help="turn a rocprofv3 --stats kernel_stats.csv into a short markdown summary")
+    ap.add_argument("--summarize-sq", nargs="+", metavar="DIR",
+                    help="rocprofv3 --pmc run directories (SQ/GRBM counters) followed by the output .md: "
+                         "MFMA-pipe utilisation and wave-cycle shares of the MXFP4 GEMM")
     ap.add_argument("--sweep", metavar="OUT_MD", nargs="?", const="-",
                     help="time every quantizer call and GEMM of all workload configurations against their "
                          "rooflines and write a markdown table (to stdout with no file)")
@@ -224,6 +227,53 @@ def summarize_stats(stats_csv, out_md):
             f.write("| %s | %s | %.1f | %.1f | %.1f | %.1f |\n" % (
                 r["Name"][:90], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
                 float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    print(open(out_md).read())
+
+
+SIMDS, XCDS = 256 * 4, 8   # MI355X: 256 compute units of 4 SIMDs in 8 XCDs
+
+
+def summarize_sq(dirs, out_md, kernel="gemm_mx_kernel"):
+    """Per-dispatch averages of SQ/GRBM counters for one kernel over rocprofv3
+    --pmc runs, and what they give: the clock (GRBM_GUI_ACTIVE counts each XCD's
+    busy cycles, summed over the 8 XCDs), the MFMA pipe's busy share of all
+    SIMD-cycles, busy cycles per MFMA instruction, and the shares of
+    resident-wave cycles spent issuing and waiting."""
+    import csv
+    import glob
+    vals, dur = {}, {}
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if kernel not in r["Kernel_Name"]:
+                        continue
+                    key = (d, r["Dispatch_Id"])
+                    per = vals.setdefault(r["Counter_Name"], {})
+                    per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+                    dur[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    mean = {c: sum(v.values()) / len(v) for c, v in vals.items()}
+    t = sum(dur.values()) / len(dur)
+    lines = [f"SQ/GRBM counters of {kernel} (rocprofv3 --pmc, per-dispatch averages over {len(dur)} dispatches "
+             f"in {len(dirs)} runs; commands in profiles/README.md)", "",
+             "| counter | per dispatch |", "|---|---|"]
+    lines += [f"| {c} | {mean[c]:.4g} |" for c in sorted(mean)]
+    lines += ["", f"| derived | value |", "|---|---|", f"| dispatch duration under counters | {t * 1e6:.1f} us |"]
+    gui = mean.get("GRBM_GUI_ACTIVE")
+    if gui:
+        cyc = gui / XCDS
+        lines.append(f"| busy cycles per XCD | {cyc:.4g} ({cyc / t / 1e9:.2f} GHz) |")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            lines.append(f"| MFMA pipe busy, share of SIMD-cycles | {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (SIMDS * cyc) * 100:.1f} % |")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and mean.get("SQ_INSTS_MFMA"):
+        lines.append(f"| MFMA busy cycles per MFMA instruction | {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / mean['SQ_INSTS_MFMA']:.1f} |")
+    wc = mean.get("SQ_WAVE_CYCLES")
+    if wc:
+        for c in ("SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_WAIT_INST_LDS"):
+            if c in mean:
+                lines.append(f"| {c} / SQ_WAVE_CYCLES | {mean[c] / wc * 100:.1f} % |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
     print(open(out_md).read())
 
 
@@ -517,6 +567,11 @@ def main():
         return
     if args.summarize_quant:
         summarize_quant(*args.summarize_quant)
+        return
+    if args.summarize_sq:
+        if len(args.summarize_sq) < 2:
+            sys.exit("--summarize-sq takes one or more run directories, then the output file")
+        summarize_sq(args.summarize_sq[:-1], args.summarize_sq[-1])
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library runs the hot path "

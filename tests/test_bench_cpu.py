@@ -55,6 +55,39 @@ def test_summarize_stats_table(tmp_path):
     assert lines[3] == "| quant_kernel | 26 | 26.9 | 13.0 | 48.0 | 19.5 |"
 
 
+def test_summarize_sq_derived_figures(tmp_path):
+    """Two counter runs of one kernel (other kernels ignored): averages per
+    dispatch, the clock from GRBM_GUI_ACTIVE summed over 8 XCDs, the MFMA
+    pipe's share of 1024 SIMDs' cycles and cycles per MFMA instruction."""
+    head = "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp\n"
+    run_a = tmp_path / "a" / "host"
+    run_b = tmp_path / "b" / "host"
+    run_a.mkdir(parents=True)
+    run_b.mkdir(parents=True)
+    # 100 us dispatches; 2e5 cycles per XCD -> 2.0 GHz
+    (run_a / "s_counter_collection.csv").write_text(
+        head
+        + "1,mxfp4::gemm_mx_kernel<0>,GRBM_GUI_ACTIVE,1600000,0,100000\n"
+        + "1,mxfp4::gemm_mx_kernel<0>,SQ_VALU_MFMA_BUSY_CYCLES,51200000,0,100000\n"
+        + "1,mxfp4::gemm_mx_kernel<0>,SQ_INSTS_MFMA,1600000,0,100000\n"
+        + "1,mxfp4::gemm_mx_kernel<0>,SQ_WAVE_CYCLES,1000,0,100000\n"
+        + "1,mxfp4::gemm_mx_kernel<0>,SQ_WAIT_INST_ANY,250,0,100000\n"
+        + "2,mxfp4::quant_rows_kernel,SQ_WAVE_CYCLES,5,0,100000\n")
+    (run_b / "s_counter_collection.csv").write_text(
+        head + "1,mxfp4::gemm_mx_kernel<0>,GRBM_GUI_ACTIVE,1600000,0,100000\n"
+        + "1,mxfp4::gemm_mx_kernel<0>,SQ_LDS_BANK_CONFLICT,0,0,100000\n")
+    out = tmp_path / "sq.md"
+    bench.summarize_sq([str(tmp_path / "a"), str(tmp_path / "b")], str(out))
+    text = out.read_text()
+    assert "over 2 dispatches in 2 runs" in text
+    assert "| dispatch duration under counters | 100.0 us |" in text
+    assert "| busy cycles per XCD | 2e+05 (2.00 GHz) |" in text
+    assert "| MFMA pipe busy, share of SIMD-cycles | 25.0 % |" in text      # 51.2e6 / (1024 * 2e5)
+    assert "| MFMA busy cycles per MFMA instruction | 32.0 |" in text
+    assert "| SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES | 25.0 % |" in text
+    assert "| SQ_LDS_BANK_CONFLICT | 0 |" in text
+
+
 def test_sweep_plan_covers_every_configuration():
     import workloads
     plan = bench.sweep_plan()
