@@ -36,8 +36,10 @@ MX_BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0   # bf16 in, packed codes + E8M0 scal
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps first: from idle, the GEMM runs 15-30 %% slower for the first "
+                         "~10 ms (about 30 steps) and settles within ~70 ms")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "gemm_mx_headline_traffic.txt"),
                     help="HBM bytes per GEMM launch from rocprofv3 counters (written by --summarize-pmc)")
@@ -608,11 +610,14 @@ def main():
     ws_bytes = mx.mxfp4_gemm_workspace_bytes(qa, qb)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
-    def step(ev=None):
-        if ev is not None:
+    # ev: events recorded on the launch stream (torch's current stream, which
+    # the binding passes to the library) around the GEMM, and with `parts`
+    # also around each quantizer call
+    def step(ev=None, parts=False):
+        if parts:
             ev[0].record()
         mx.mxfp4_quantize(A, "mx", "rtn", False, 1, 0, out=qa)
-        if ev is not None:
+        if parts:
             ev[1].record()
         mx.mxfp4_quantize(B, "mx", "rtn", False, 1, 0, out=qb)
         if ev is not None:
@@ -624,7 +629,8 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    new_events = lambda: [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = new_events()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -632,9 +638,16 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    qa_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    qb_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     g_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+    # the quantizer components: the same steps again after the timed region,
+    # with events between the calls (each event pair adds a few microseconds
+    # to a step, so the timed steps carry only the GEMM's)
+    part_events = new_events()
+    for i in range(args.steps):
+        step(part_events[i], parts=True)
+    torch.cuda.synchronize()
+    qa_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in part_events]))
+    qb_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in part_events]))
 
     flops = 2.0 * M * N * K
     gemm_tflops = flops / (g_ms * 1e-3) / 1e12
