@@ -398,6 +398,16 @@ def sweep(args):
         return g
 
     def replay_time(g):
+        # from idle the clock needs ~10 ms of load to settle: replay the graph
+        # back to back for about 30 ms before timing it
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        for _ in range(min(5000, int(30.0 / max(e0.elapsed_time(e1), 1e-3)) + 1)):
+            g.replay()
+        torch.cuda.synchronize()
         ts = []
         for i in range(args.sweep_reps + 2):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
