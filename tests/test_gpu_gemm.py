@@ -190,6 +190,35 @@ def test_gemm_config4_wgrad_split_k(oracle_mod):
     _sampled_check(mx, oracle_mod, qa, qb, oa, ob, "mx", "config4 wgrad fc2", nsample=16)
 
 
+@pytest.mark.parametrize("fmt,M,N,K", [("mx", 300, 300, 16384), ("mx", 40, 260, 16384), ("mx", 300, 300, 4096),
+                                       ("nv", 200, 260, 8192)])
+def test_splitk_reduction_load_widths_agree(oracle_mod, fmt, M, N, K):
+    """The split-K reduction adds the partials in split order whether it reads
+    them four outputs at a time (contiguous, 16-byte aligned C, more than four
+    splits: 16 here, wide and narrow tiles, NVFP4) or one at a time (C at an odd
+    row stride and a 4-byte offset; 4 splits): the same bits, fp32 and bf16 C,
+    and the oracle within tolerance on sampled rows."""
+    mx = need_gpu()
+    A = workloads.small_normal_bf16((M, K), 1.0, seed=41)
+    B = workloads.small_normal_bf16((N, K), 0.02, seed=42)
+    qa, qb, oa, ob = _quant_pair(mx, oracle_mod, A, B, fmt)
+    assert mx.mxfp4_gemm_workspace_bytes(qa, qb) > 0
+    say("split-K reduction widths", fmt, M, N, K)
+    c_vec = mx.mxfp4_gemm(qa, qb)
+    big = torch.full((M, N + 3), 5.0, device="cuda")
+    mx.mxfp4_gemm(qa, qb, out=big[:, 1:N + 1])
+    h_vec, h_big = c_vec.cpu().numpy(), big.cpu().numpy()
+    assert np.array_equal(h_vec.view(np.uint32), h_big[:, 1:N + 1].view(np.uint32))
+    assert (h_big[:, 0] == 5.0).all() and (h_big[:, N + 1:] == 5.0).all()
+    b_vec = mx.mxfp4_gemm_bf16(qa, qb)
+    bbig = torch.full((M, N + 3), 5.0, dtype=torch.bfloat16, device="cuda")
+    mx.mxfp4_gemm_bf16(qa, qb, out=bbig[:, 1:N + 1])
+    assert torch.equal(b_vec.view(torch.int16), bbig[:, 1:N + 1].contiguous().view(torch.int16))
+    rows = np.array([0, M // 2, M - 1])
+    Co, So = oracle_mod.gemm(fmt, oa, ob, rows=rows)
+    assert_gemm_within(h_vec[rows], Co, So, f"split-K {fmt} {M}x{N}x{K}")
+
+
 def test_gemm_format_mismatch_rejected(oracle_mod):
     mx = need_gpu()
     A = workloads.small_normal_bf16((64, 256), 1.0, seed=36)
