@@ -137,7 +137,10 @@ mxfp4_status mxfp4_gemm_workspace_bytes(const mxfp4_tensor *A, const mxfp4_tenso
  * 2^24 (UNSUPPORTED_SHAPE otherwise); fmt, k and hadamard of A and B must agree
  * (FORMAT_MISMATCH).  A->codes and B->codes must be 16-byte aligned and the
  * scales 4-byte aligned (INVALID_ARG otherwise).
- * workspace: device, at least mxfp4_gemm_workspace_bytes (NULL if 0). */
+ * workspace: device, 4-byte aligned (WORKSPACE otherwise), at least
+ *    mxfp4_gemm_workspace_bytes (NULL if 0); with 16-byte alignment, a
+ *    16-byte aligned C and N and ldc multiples of 4, the split-K reduction
+ *    reads four outputs at a time (same results either way). */
 mxfp4_status mxfp4_gemm(const mxfp4_tensor *A, const mxfp4_tensor *B, float *C, int64_t ldc,
                         void *workspace, size_t ws_bytes, hipStream_t stream);
 
