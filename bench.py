@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--summarize-sq", nargs="+", metavar="DIR",
                     help="rocprofv3 --pmc run directories (SQ/GRBM counters) followed by the output .md: "
                          "MFMA-pipe utilisation and wave-cycle shares of the MXFP4 GEMM")
+    ap.add_argument("--settle-trace", metavar="OUT_MD",
+                    help="GEMM time per headline step over 1500 steps started from an idle GPU (window means)")
     ap.add_argument("--sweep", metavar="OUT_MD", nargs="?", const="-",
                     help="time every quantizer call and GEMM of all workload configurations against their "
                          "rooflines and write a markdown table (to stdout with no file)")
@@ -274,6 +276,43 @@ def summarize_sq(dirs, out_md, kernel="gemm_mx_kernel"):
         for c in ("SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_WAIT_INST_LDS"):
             if c in mean:
                 lines.append(f"| {c} / SQ_WAVE_CYCLES | {mean[c] / wc * 100:.1f} % |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(open(out_md).read())
+
+
+def settle_trace(out_md, steps=1500):
+    """Headline steps from an idle GPU (2 s without work first), HIP events
+    around each GEMM; the mean, min and max GEMM time per window of steps show
+    how long the clock takes to settle."""
+    import torch
+    import microscaling_fp4_quantized_block_amd as mx
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    A = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+    B = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    qa, qb = mx.empty_qtensor("mx", M, K, False, dev), mx.empty_qtensor("mx", N, K, False, dev)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    time.sleep(2.0)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        mx.mxfp4_quantize(A, "mx", "rtn", False, 1, 0, out=qa)
+        mx.mxfp4_quantize(B, "mx", "rtn", False, 1, 0, out=qb)
+        evs[i][0].record()
+        mx.mxfp4_gemm(qa, qb, out=C)
+        evs[i][1].record()
+        if i % 100 == 99:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    bounds = list(range(0, 60, 5)) + list(range(60, steps + 1, 60))
+    lines = [f"Headline GEMM ({M}x{N}x{K}) time per step, {steps} steps of `bench.py`'s step started after 2 s "
+             "without GPU work (HIP events around each GEMM). Command: `python bench.py --settle-trace OUT_MD`.",
+             "", "| steps | mean us | min us | max us |", "|---|---|---|---|"]
+    for w0, w1 in zip(bounds[:-1], bounds[1:]):
+        lines.append(f"| {w0}-{w1 - 1} | {t[w0:w1].mean():.1f} | {t[w0:w1].min():.1f} | {t[w0:w1].max():.1f} |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(open(out_md).read())
@@ -579,6 +618,9 @@ def main():
         return
     if args.summarize_quant:
         summarize_quant(*args.summarize_quant)
+        return
+    if args.settle_trace:
+        settle_trace(args.settle_trace)
         return
     if args.summarize_sq:
         if len(args.summarize_sq) < 2:
