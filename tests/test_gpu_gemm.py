@@ -110,31 +110,33 @@ def test_gemm_headline_sampled(oracle_mod):
     _sampled_check(mx, oracle_mod, qa, qb, oa, ob, "mx", "headline", nsample=24)
 
 
-def test_gemm_balanced_half_tiles(oracle_mod):
+@pytest.mark.parametrize("fmt", ["mx", "nv"])
+def test_gemm_balanced_half_tiles(oracle_mod, fmt):
     """More 256 x 256 tiles than compute units, not a multiple of them: the
     remainder tiles run as 256 x 128 halves at the start and at the end of
-    the launch.  M = 4352 (17 tile rows), N = 3904 (the last tile column has
+    the launch (MXFP4; the NVFP4 kernel runs the same shape as whole tiles).  M = 4352 (17 tile rows), N = 3904 (the last tile column has
     64 valid columns, so its second half lies wholly past N); the 16
     remainder tiles are the bottom tile row, checked in full."""
     mx = need_gpu()
     M, N, K = 4352, 3904, 512
     A = workloads.small_t_bf16((M, K), 3.0, seed=36, outlier_frac=0.01)
     B = workloads.small_normal_bf16((N, K), 0.02, seed=37)
-    qa, qb, oa, ob = _quant_pair(mx, oracle_mod, A, B, "mx")
-    say("gemm balanced", M, N, K)
+    qa, qb, oa, ob = _quant_pair(mx, oracle_mod, A, B, fmt)
+    say("gemm balanced", fmt, M, N, K)
     C = mx.mxfp4_gemm(qa, qb)
     torch.cuda.synchronize()
     rows = np.concatenate([np.arange(4096, M), np.arange(0, 4096, 97)])
     Cr = C[torch.from_numpy(rows).cuda()].cpu().numpy()
-    Co, So = oracle_mod.gemm("mx", oa, ob, rows=rows)
+    Co, So = oracle_mod.gemm(fmt, oa, ob, rows=rows)
     assert_gemm_within(Cr, Co, So, "balanced rows")
     cols = np.array([0, 1, 127, 128, 255, 256, 3839, 3840, 3871, 3872, N - 1])
     Cc = C[:, torch.from_numpy(cols).cuda()].cpu().numpy()
-    Co, So = oracle_mod.gemm("mx", oa, ob, cols=cols)
+    Co, So = oracle_mod.gemm(fmt, oa, ob, cols=cols)
     assert_gemm_within(Cc, Co, So, "balanced cols")
 
 
-def test_gemm_balanced_halves_partial_column(oracle_mod):
+@pytest.mark.parametrize("fmt", ["mx", "nv"])
+def test_gemm_balanced_halves_partial_column(oracle_mod, fmt):
     """Tile count = 1.5 x 256: 128 remainder tiles run as 256 x 128 halves at
     the start and at the end of the launch.  M = 3072, N = 8128 (the last tile
     column has 192 valid columns, so its second half is partly past N),
@@ -143,17 +145,17 @@ def test_gemm_balanced_halves_partial_column(oracle_mod):
     M, N, K = 3072, 8128, 256
     A = workloads.small_t_bf16((M, K), 3.0, seed=38, outlier_frac=0.01)
     B = workloads.small_normal_bf16((N, K), 0.02, seed=39)
-    qa, qb, oa, ob = _quant_pair(mx, oracle_mod, A, B, "mx")
-    say("gemm halves, partial column", M, N, K)
+    qa, qb, oa, ob = _quant_pair(mx, oracle_mod, A, B, fmt)
+    say("gemm halves, partial column", fmt, M, N, K)
     C = mx.mxfp4_gemm(qa, qb)
     torch.cuda.synchronize()
     rows = np.concatenate([np.arange(1024, 3072, 7), np.arange(0, 1024, 61), [M - 1]])
     Cr = C[torch.from_numpy(rows).cuda()].cpu().numpy()
-    Co, So = oracle_mod.gemm("mx", oa, ob, rows=rows)
+    Co, So = oracle_mod.gemm(fmt, oa, ob, rows=rows)
     assert_gemm_within(Cr, Co, So, "halves rows")
     cols = np.array([0, 63, 64, 127, 128, 191, 192, 255, 4096, 4160, 4288, 4351, 7936, 8000, 8127])
     Cc = C[:, torch.from_numpy(cols).cuda()].cpu().numpy()
-    Co, So = oracle_mod.gemm("mx", oa, ob, cols=cols)
+    Co, So = oracle_mod.gemm(fmt, oa, ob, cols=cols)
     assert_gemm_within(Cc, Co, So, "halves cols")
 
 
