@@ -79,6 +79,10 @@ def _load():
     lib.mxo_gemm.argtypes = [i32, i64, vp, vp, vp, vp, vp, vp, vp, i64, vp, i64, vp, vp]
     lib.mxo_quantize_mse.restype = i32
     lib.mxo_quantize_mse.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, vp, vp, vp]
+    lib.mxo_mse_check.restype = i32
+    lib.mxo_mse_check.argtypes = [vp, i64, i64, i64, i32, i32, i32, ctypes.c_float, vp, vp, ctypes.c_double, vp]
+    lib.mxo_mse_tensor_step.restype = i32
+    lib.mxo_mse_tensor_step.argtypes = [vp, i64, i64, i64, i32, i32, vp, vp, ctypes.c_float, vp]
     lib.mxo_noise_stats.restype = i32
     lib.mxo_noise_stats.argtypes = [vp, i64, i64, i64, i32, i32, i32, vp, vp, vp, vp]
     _lib = lib
@@ -247,9 +251,9 @@ def noise_stats(x_bits: np.ndarray, q, fmt: str = "mx", hadamard: bool = False, 
 
 def quantize_mse(x_bits: np.ndarray, fmt: str = "nv", hadamard: bool = False, axis: int = 1, iters: int = 2):
     """Round-to-nearest quantization with MSE-fitted scales (the digest of the
-    MR-GPTQ paper, step 1): per-block scale search within a window below the
-    absmax scale, alternating with the least-squares tensor scale (NVFP4)
-    `iters` times.  Same return value as quantize()."""
+    MR-GPTQ paper, step 1): each block keeps the scale at or below its absmax
+    scale with the smallest squared error, alternating with the least-squares
+    tensor scale (NVFP4) `iters` times.  Same return value as quantize()."""
     x = np.ascontiguousarray(x_bits, dtype=np.uint16)
     R, C = x.shape
     rows, K = (R, C) if axis == 1 else (C, R)
@@ -262,3 +266,40 @@ def quantize_mse(x_bits: np.ndarray, fmt: str = "nv", hadamard: bool = False, ax
     if rc != 0:
         raise ValueError("oracle quantize_mse rejected its arguments")
     return codes, scales, (float(ts[0]) if ts is not None else None)
+
+
+def mse_check(x_bits: np.ndarray, q, fmt: str, hadamard: bool = False, axis: int = 1, st=None,
+              rel_tol: float = 0.0) -> dict:
+    """Check that q = (codes, scales, tensor_scale) is a block step of the MSE
+    quantizer for x under tensor scale st (default: q's own; ignored for MX):
+    every block's byte is a candidate, its codes are the round-to-nearest
+    encoding for that byte, and its squared error is within (1 + rel_tol) of
+    the smallest over all candidates.  Returns the counts of the C checker."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    R, C = x.shape
+    codes = np.ascontiguousarray(q[0], dtype=np.uint8)
+    scales = np.ascontiguousarray(q[1], dtype=np.uint8)
+    if st is None:
+        st = q[2] if q[2] is not None else 1.0
+    out = np.zeros(5, dtype=np.int64)
+    rc = _load().mxo_mse_check(_ptr(x), R, C, C, FMT[fmt], int(bool(hadamard)), int(axis), float(st), _ptr(codes),
+                               _ptr(scales), float(rel_tol), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle mse_check rejected its arguments")
+    return {"blocks": int(out[0]), "bad_encoding": int(out[1]), "bad_error": int(out[2]),
+            "differ_from_oracle": int(out[3]), "first_bad": int(out[4])}
+
+
+def mse_tensor_step(x_bits: np.ndarray, q, hadamard: bool = False, axis: int = 1, st_prev: float = 1.0) -> float:
+    """The least-squares NVFP4 tensor scale for the bytes and codes of q (a
+    quantization of x), as a binary32 value; st_prev if sum(y p) <= 0."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    R, C = x.shape
+    codes = np.ascontiguousarray(q[0], dtype=np.uint8)
+    scales = np.ascontiguousarray(q[1], dtype=np.uint8)
+    out = np.zeros(1, dtype=np.float32)
+    rc = _load().mxo_mse_tensor_step(_ptr(x), R, C, C, int(bool(hadamard)), int(axis), _ptr(codes), _ptr(scales),
+                                     float(st_prev), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle mse_tensor_step rejected its arguments")
+    return float(out[0])

@@ -542,102 +542,196 @@ int mxo_noise_stats(const uint16_t *x, int64_t R, int64_t C, int64_t ldx,
 }
 
 /* ------------------------------------------------------------------ */
-/* MSE-optimal scales [DIG step 1: the quantization grid is fitted for  */
+/* MSE-fitted scales [DIG step 1: the quantization grid is fitted for   */
 /* mean squared error by optimizing, in turn, the scales of each block  */
 /* and the scale of the tensor].  READINGS (the page gives the idea,    */
 /* not the procedure):                                                  */
 /*  - round-to-nearest only (a forward / weight quantizer);             */
-/*  - block step: among a window of candidate scales the block keeps    */
-/*    the one with the smallest squared error sum (y - Q(y))^2 over its */
-/*    own elements, Q(y) the exactly dequantized value; MX candidates:  */
-/*    the absmax exponent e0, e0 - 1, e0 - 2 (>= -127); NV candidates:  */
-/*    the absmax E4M3 byte b0 and the 8 bytes below it (>= 1), scales   */
-/*    down to about half; a tie keeps the larger scale; elements are    */
-/*    encoded exactly as in the absmax quantizer for the chosen scale;  */
-/*  - a block's error is summed in binary64 in a fixed order: runs of 8 */
-/*    consecutive elements summed in turn, then (S0 + S1) + (S2 + S3)   */
-/*    for 32 elements, S0 + S1 for 16;                                  */
+/*  - block step: among every scale value at or below the block's       */
+/*    absmax scale (MX: 2^e for e = e0, e0 - 1, ..., -127; NV: the E4M3  */
+/*    bytes b0, b0 - 1, ..., 1 times the tensor scale), the block keeps  */
+/*    the one whose round-to-nearest encoding -- exactly the absmax     */
+/*    quantizer's encoding for that scale -- has the smallest squared   */
+/*    error sum (y - Q(y))^2 over the block, Q(y) the exactly           */
+/*    dequantized value; a tie keeps the larger scale.  Larger scales   */
+/*    are not candidates: below the block maximum their grids hold no   */
+/*    point the absmax grid lacks (MX: {0,1,2,3,4,6} 2^(e0+1) is a      */
+/*    subset of the e0 grid), so they only coarsen it;                  */
+/*  - the error of a candidate is exact up to a final rounding: each    */
+/*    difference y - Q(y) is exact in binary64 (at most ~36 significant */
+/*    bits), its square exact in binary128, and the block's squares are */
+/*    added in binary128, elements in turn;                             */
+/*  - the search walks the scales downwards and stops once the clipping */
+/*    of the block maximum alone, (amax - 6 s)^2 for a grid top 6 s      */
+/*    below amax, exceeds the best error found: that term only grows as */
+/*    s falls, so no smaller scale can win (an exact cut, not a window);*/
 /*  - tensor step (NV): with block bytes b and codes g fixed, the least */
-/*    squares tensor scale sum(y p) / sum(p^2), p = E4M3(b) E2M1(g),    */
-/*    both sums in binary64 in a fixed order (each unit of 32           */
-/*    contraction elements -- 16 for NV without rotation when K is not  */
-/*    a multiple of 32 -- in turn; each operand row over its units in   */
-/*    turn; rows in 256 contiguous ranges [t rows/256, (t+1) rows/256)  */
-/*    in turn; the 256 range sums in turn), blocks with a NaN scale left*/
-/*    out; the binary64 quotient rounded to binary32 and kept >= 2^-117;*/
-/*    unchanged when sum(y p) <= 0;                                     */
+/*    squares tensor scale sum(y p) / sum(p^2), p = E4M3(b) E2M1(g);    */
+/*    each product is exact in binary64 and added in binary128, elements*/
+/*    of a row in turn, then the rows in turn; blocks with a NaN scale  */
+/*    are left out; the quotient is rounded once to binary32 and kept   */
+/*    >= 2^-117; the scale is unchanged when sum(y p) <= 0;             */
 /*  - schedule: block step with the absmax tensor scale, then `iters`   */
 /*    times (tensor step, block step).  MX has no tensor step.          */
 /* ------------------------------------------------------------------ */
-static double mse_tree(const double *d2, int n)
+typedef __float128 q128;
+
+/* Codes of one block for MX exponent e (scale 2^e), or for NV byte b under
+ * tensor scale st, encoded as the absmax quantizer encodes them; returns the
+ * block's squared error in binary128. */
+static q128 mx_candidate(const float *y, int bs, int e, int *codes)
 {
-    double s[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int r = 0; r < n / 8; r++)
-        for (int j = 0; j < 8; j++) s[r] += d2[8 * r + j];
-    return n == 16 ? s[0] + s[1] : (s[0] + s[1]) + (s[2] + s[3]);
+    const double step = ldexp(1.0, -e), sc = ldexp(1.0, e);
+    q128 E = 0;
+    for (int j = 0; j < bs; j++) {
+        codes[j] = mxo_rtn_code((double)y[j] * step);
+        double d = (double)y[j] - mxo_e2m1_value(codes[j]) * sc;      /* exact */
+        E += (q128)d * (q128)d;
+    }
+    return E;
 }
 
-/* One block: scale byte and codes of the MSE choice. */
-static void mse_block(int fmt, const float *y, float st, int *byte_out, int *codes)
+static q128 nv_candidate(const float *y, int bs, int b, float st, int *codes)
 {
-    const int bs = (fmt == FMT_MX) ? 32 : 16;
-    float amax = 0.0f;
-    int finite = 1;
+    const float sb = (float)mxo_e4m3_value(b);
+    const float d32 = sb * st;
+    const float inv = 1.0f / d32;
+    q128 E = 0;
     for (int j = 0; j < bs; j++) {
-        if (!isfinite(y[j])) finite = 0;
-        else if (fabsf(y[j]) > amax) amax = fabsf(y[j]);
+        float q = y[j] * inv;                                          /* one binary32 multiply */
+        codes[j] = mxo_rtn_code((double)q);
+        double d = (double)y[j] - mxo_e2m1_value(codes[j]) * (double)sb * (double)st;   /* exact */
+        E += (q128)d * (q128)d;
     }
-    if (!finite) {
-        *byte_out = (fmt == FMT_MX) ? 0xFF : 0x7F;
-        for (int j = 0; j < bs; j++) codes[j] = 0;
-        return;
+    return E;
+}
+
+/* Absmax of a block; 0 if it holds a non-finite value. */
+static int block_amax(const float *y, int bs, float *amax)
+{
+    *amax = 0.0f;
+    for (int j = 0; j < bs; j++) {
+        if (!isfinite(y[j])) return 0;
+        if (fabsf(y[j]) > *amax) *amax = fabsf(y[j]);
     }
-    double d2[32];
-    int cand[32];
-    double best = INFINITY;
-    if (fmt == FMT_MX) {
-        int e0 = mxo_mx_scale_exponent(amax);
-        for (int e = e0; e >= e0 - 2 && e >= -127; e--) {
-            double step = ldexp(1.0, -e), sc = ldexp(1.0, e);
-            for (int j = 0; j < bs; j++) {
-                cand[j] = mxo_rtn_code((double)y[j] * step);
-                double d = (double)y[j] - mxo_e2m1_value(cand[j]) * sc;
-                d2[j] = d * d;
-            }
-            double E = mse_tree(d2, bs);
-            if (E < best) {
-                best = E;
-                *byte_out = e + 127;
-                for (int j = 0; j < bs; j++) codes[j] = cand[j];
-            }
-        }
-        return;
-    }
+    return 1;
+}
+
+/* The absmax scale of a finite block: MX exponent e0, NV byte b0. */
+static int absmax_scale(int fmt, float amax, float st)
+{
+    if (fmt == FMT_MX) return mxo_mx_scale_exponent(amax);
     float den = 6.0f * st;
     float r = amax / den;
-    int b0 = mxo_e4m3_round_up(r);
-    if (b0 == 0) {
+    return mxo_e4m3_round_up(r);
+}
+
+/* The block step for one finite block: scale byte, codes and the smallest
+ * squared error (binary128). */
+static void mse_block(int fmt, const float *y, float st, int *byte_out, int *codes, q128 *err_out)
+{
+    const int bs = (fmt == FMT_MX) ? 32 : 16;
+    float amax;
+    int cand[32];
+    block_amax(y, bs, &amax);
+    const int top = absmax_scale(fmt, amax, st);
+    if (fmt == FMT_NV && top == 0) {
+        /* the block's absmax maps to scale 0: every code is a signed zero */
         *byte_out = 0;
-        for (int j = 0; j < bs; j++) codes[j] = mxo_rtn_code(copysign(0.0, (double)y[j]));
+        q128 E = 0;
+        for (int j = 0; j < bs; j++) {
+            codes[j] = mxo_rtn_code(copysign(0.0, (double)y[j]));
+            E += (q128)y[j] * (q128)y[j];
+        }
+        *err_out = E;
         return;
     }
-    for (int b = b0; b >= b0 - 8 && b >= 1; b--) {
-        float sb = (float)mxo_e4m3_value(b);
-        float d = sb * st;
-        float inv = 1.0f / d;
-        for (int j = 0; j < bs; j++) {
-            float q = y[j] * inv;
-            cand[j] = mxo_rtn_code((double)q);
-            double dd = (double)y[j] - mxo_e2m1_value(cand[j]) * (double)sb * (double)st;
-            d2[j] = dd * dd;
+    const int lowest = (fmt == FMT_MX) ? -127 : 1;
+    q128 best = 0;
+    int have = 0;
+    for (int s = top; s >= lowest; s--) {
+        const double grid_top = (fmt == FMT_MX) ? 6.0 * ldexp(1.0, s)
+                                                : 6.0 * mxo_e4m3_value(s) * (double)st;
+        if (have && grid_top < (double)amax) {
+            const q128 clip = ((q128)amax - (q128)grid_top) * ((q128)amax - (q128)grid_top);
+            if (clip > best) break;
         }
-        double E = mse_tree(d2, bs);
-        if (E < best) {
+        q128 E = (fmt == FMT_MX) ? mx_candidate(y, bs, s, cand) : nv_candidate(y, bs, s, st, cand);
+        if (!have || E < best) {
+            have = 1;
             best = E;
-            *byte_out = b;
+            *byte_out = (fmt == FMT_MX) ? s + 127 : s;
             for (int j = 0; j < bs; j++) codes[j] = cand[j];
         }
     }
+    *err_out = best;
+}
+
+/* The operand's contraction rows, rotated once: rows x K floats. */
+static float *load_operand(const uint16_t *x, int64_t ldx, int hadamard, int axis, int64_t rows, int64_t K)
+{
+    float *Y = (float *)malloc(sizeof(float) * (size_t)rows * (size_t)K);
+    if (!Y) return NULL;
+    #pragma omp parallel for
+    for (int64_t i = 0; i < rows; i++) load_contraction_row(x, ldx, axis, i, K, hadamard, Y + i * K);
+    return Y;
+}
+
+/* Least-squares tensor scale for fixed bytes and codes (NV); st_prev when
+ * sum(y p) <= 0. */
+static float ls_tensor_scale(const float *Y, int64_t rows, int64_t K, const uint8_t *codes,
+                             const uint8_t *scales, float st_prev)
+{
+    const int bs = 16;
+    q128 *rn = (q128 *)malloc(sizeof(q128) * (size_t)rows);
+    q128 *rd = (q128 *)malloc(sizeof(q128) * (size_t)rows);
+    #pragma omp parallel for
+    for (int64_t i = 0; i < rows; i++) {
+        q128 sn = 0, sd = 0;
+        for (int64_t k = 0; k < K; k++) {
+            int sbyte = scales[i * (K / bs) + k / bs];
+            if ((sbyte & 0x7F) == 0x7F) continue;
+            int code = (codes[i * (K / 2) + k / 2] >> (4 * (k & 1))) & 0xF;
+            double p = mxo_e2m1_value(code) * mxo_e4m3_value(sbyte);     /* exact */
+            sn += (q128)((double)Y[i * K + k] * p);                      /* exact product */
+            sd += (q128)(p * p);
+        }
+        rn[i] = sn;
+        rd[i] = sd;
+    }
+    q128 num = 0, den = 0;
+    for (int64_t i = 0; i < rows; i++) {
+        num += rn[i];
+        den += rd[i];
+    }
+    free(rn);
+    free(rd);
+    if (!(num > 0) || !(den > 0)) return st_prev;
+    float s = (float)(num / den);
+    const float floor_st = ldexpf(1.0f, -117);
+    return s < floor_st ? floor_st : s;
+}
+
+static void put_code(uint8_t *codes, int64_t K, int64_t i, int64_t k, int c)
+{
+    uint8_t *cb = &codes[i * (K / 2) + k / 2];
+    if ((k & 1) == 0) *cb = (uint8_t)((*cb & 0xF0) | c);
+    else *cb = (uint8_t)((*cb & 0x0F) | (c << 4));
+}
+
+static int get_code(const uint8_t *codes, int64_t K, int64_t i, int64_t k)
+{
+    return (codes[i * (K / 2) + k / 2] >> (4 * (k & 1))) & 0xF;
+}
+
+static float tensor_absmax_scale(const float *Y, int64_t n)
+{
+    float amax_t = 0.0f;
+    for (int64_t t = 0; t < n; t++) {
+        float a = fabsf(Y[t]);
+        if (isfinite(a) && a > amax_t) amax_t = a;
+    }
+    return mxo_nv_tensor_scale(amax_t);
 }
 
 int mxo_quantize_mse(const uint16_t *x, int64_t R, int64_t C, int64_t ldx,
@@ -655,81 +749,133 @@ int mxo_quantize_mse(const uint16_t *x, int64_t R, int64_t C, int64_t ldx,
         if (fmt == FMT_NV) *tensor_scale = 1.0f;
         return 0;
     }
-    /* the operand, rotated once */
-    float *Y = (float *)malloc(sizeof(float) * (size_t)rows * (size_t)K);
+    float *Y = load_operand(x, ldx, hadamard, axis, rows, K);
     if (!Y) return -1;
-    #pragma omp parallel for
-    for (int64_t i = 0; i < rows; i++) load_contraction_row(x, ldx, axis, i, K, hadamard, Y + i * K);
-    float st = 1.0f;
-    if (fmt == FMT_NV) {
-        float amax_t = 0.0f;
-        for (int64_t t = 0; t < rows * K; t++) {
-            float a = fabsf(Y[t]);
-            if (isfinite(a) && a > amax_t) amax_t = a;
-        }
-        st = mxo_nv_tensor_scale(amax_t);
-    }
-    const int unit = (fmt == FMT_NV && !hadamard && K % 32 != 0) ? 16 : 32;
-    double *row_num = (double *)malloc(sizeof(double) * (size_t)rows);
-    double *row_den = (double *)malloc(sizeof(double) * (size_t)rows);
+    float st = (fmt == FMT_NV) ? tensor_absmax_scale(Y, rows * K) : 1.0f;
     for (int round = 0; round <= iters; round++) {
-        if (round > 0 && fmt == FMT_NV) {
-            /* tensor step from the previous block step's bytes and codes */
-            #pragma omp parallel for
-            for (int64_t i = 0; i < rows; i++) {
-                double rn = 0.0, rd = 0.0;
-                for (int64_t k0 = 0; k0 < K; k0 += unit) {
-                    double un = 0.0, ud = 0.0;
-                    for (int64_t k = k0; k < k0 + unit; k++) {
-                        int sbyte = scales[i * (K / bs) + k / bs];
-                        if ((sbyte & 0x7F) == 0x7F) continue;
-                        int code = (codes[i * (K / 2) + k / 2] >> (4 * (k & 1))) & 0xF;
-                        double p = mxo_e2m1_value(code) * mxo_e4m3_value(sbyte);
-                        un += (double)Y[i * K + k] * p;
-                        ud += p * p;
-                    }
-                    rn += un;
-                    rd += ud;
-                }
-                row_num[i] = rn;
-                row_den[i] = rd;
-            }
-            double num = 0.0, den = 0.0;
-            for (int64_t t = 0; t < 256; t++) {
-                double sn = 0.0, sd = 0.0;
-                for (int64_t i = t * rows / 256; i < (t + 1) * rows / 256; i++) {
-                    sn += row_num[i];
-                    sd += row_den[i];
-                }
-                num += sn;
-                den += sd;
-            }
-            if (num > 0.0 && den > 0.0) {
-                float s = (float)(num / den);
-                const float floor_st = ldexpf(1.0f, -117);
-                st = s < floor_st ? floor_st : s;
-            }
-        }
+        if (round > 0 && fmt == FMT_NV) st = ls_tensor_scale(Y, rows, K, codes, scales, st);
+        if (round > 0 && fmt == FMT_MX) break;
         /* block step */
         #pragma omp parallel for
         for (int64_t i = 0; i < rows; i++) {
             int cs[32];
             for (int64_t b = 0; b < K / bs; b++) {
+                const float *y = Y + i * K + b * bs;
+                float amax;
                 int byte = 0;
-                mse_block(fmt, Y + i * K + b * bs, st, &byte, cs);
-                scales[i * (K / bs) + b] = (uint8_t)byte;
-                for (int j = 0; j < bs; j++) {
-                    int64_t k = b * bs + j;
-                    uint8_t *cb = &codes[i * (K / 2) + k / 2];
-                    if ((k & 1) == 0) *cb = (uint8_t)((*cb & 0xF0) | cs[j]);
-                    else *cb = (uint8_t)((*cb & 0x0F) | (cs[j] << 4));
+                if (!block_amax(y, bs, &amax)) {
+                    byte = (fmt == FMT_MX) ? 0xFF : 0x7F;
+                    for (int j = 0; j < bs; j++) cs[j] = 0;
+                } else {
+                    q128 E;
+                    mse_block(fmt, y, st, &byte, cs, &E);
                 }
+                scales[i * (K / bs) + b] = (uint8_t)byte;
+                for (int j = 0; j < bs; j++) put_code(codes, K, i, b * bs + j, cs[j]);
             }
         }
     }
     if (fmt == FMT_NV) *tensor_scale = st;
-    free(row_num);
-    free(row_den);
+    free(Y);
+    return 0;
+}
+
+/* Check a quantized tensor that claims to be the block step of the MSE
+ * quantizer for x under tensor scale st (st ignored for MX).  A block passes
+ * when (1) a non-finite block has the NaN byte and zero codes; otherwise
+ * (2) its byte is a candidate (a scale at or below its absmax scale; NV:
+ * byte 0 only when the absmax scale is byte 0), (3) its codes are the
+ * round-to-nearest encoding for its byte, and (4) its squared error is at
+ * most (1 + rel_tol) times the smallest over all candidates (several bytes
+ * are correct when errors tie to within the rounding of a binary64 sum).
+ * out[0] blocks, out[1] blocks failing (1)-(3), out[2] blocks failing (4),
+ * out[3] blocks whose byte differs from the oracle's own choice (near ties),
+ * out[4] the first failing block (row-major over [rows, K / bs]) or -1. */
+int mxo_mse_check(const uint16_t *x, int64_t R, int64_t C, int64_t ldx, int fmt, int hadamard, int axis,
+                  float st, const uint8_t *codes, const uint8_t *scales, double rel_tol, int64_t *out)
+{
+    if (!x || !codes || !scales || !out || R < 0 || C < 0 || ldx < C) return -1;
+    if ((fmt != FMT_MX && fmt != FMT_NV) || (axis != 0 && axis != 1)) return -1;
+    const int bs = (fmt == FMT_MX) ? 32 : 16;
+    const int64_t rows = (axis == 1) ? R : C;
+    const int64_t K = (axis == 1) ? C : R;
+    if (K % bs != 0 || (hadamard && K % 32 != 0)) return -1;
+    for (int t = 0; t < 4; t++) out[t] = 0;
+    out[4] = -1;
+    if (rows == 0 || K == 0) return 0;
+    float *Y = load_operand(x, ldx, hadamard, axis, rows, K);
+    if (!Y) return -1;
+    const int64_t nb = K / bs;
+    int64_t bad_enc = 0, bad_err = 0, differ = 0, first = -1;
+    #pragma omp parallel for reduction(+:bad_enc, bad_err, differ)
+    for (int64_t i = 0; i < rows; i++) {
+        for (int64_t b = 0; b < nb; b++) {
+            const float *y = Y + i * K + b * bs;
+            const int byte = scales[i * nb + b];
+            int got[32], cand[32], best_codes[32];
+            for (int j = 0; j < bs; j++) got[j] = get_code(codes, K, i, b * bs + j);
+            int enc_ok = 1, err_ok = 1;
+            float amax;
+            if (!block_amax(y, bs, &amax)) {
+                enc_ok = byte == ((fmt == FMT_MX) ? 0xFF : 0x7F);
+                for (int j = 0; j < bs; j++) enc_ok = enc_ok && got[j] == 0;
+            } else {
+                int best_byte = 0;
+                q128 Emin;
+                mse_block(fmt, y, st, &best_byte, best_codes, &Emin);
+                const int top = absmax_scale(fmt, amax, st);
+                q128 E = 0;
+                if (fmt == FMT_MX) {
+                    const int e = byte - 127;
+                    if (byte == 0xFF || e > top || e < -127) enc_ok = 0;
+                    else E = mx_candidate(y, bs, e, cand);
+                } else if (top == 0) {
+                    enc_ok = byte == 0;
+                    for (int j = 0; j < bs; j++) cand[j] = mxo_rtn_code(copysign(0.0, (double)y[j]));
+                    E = Emin;
+                } else {
+                    if (byte < 1 || byte > top) enc_ok = 0;
+                    else E = nv_candidate(y, bs, byte, st, cand);
+                }
+                if (enc_ok)
+                    for (int j = 0; j < bs; j++) enc_ok = enc_ok && got[j] == cand[j];
+                if (enc_ok) err_ok = E <= Emin * (q128)(1.0 + rel_tol);
+                if (enc_ok && byte != best_byte) differ++;
+            }
+            if (!enc_ok) bad_enc++;
+            else if (!err_ok) bad_err++;
+            if (!enc_ok || !err_ok) {
+                #pragma omp critical
+                if (first < 0 || i * nb + b < first) first = i * nb + b;
+            }
+        }
+    }
+    out[1] = bad_enc;
+    out[2] = bad_err;
+    out[3] = differ;
+    out[0] = rows * nb;
+    out[4] = first;
+    free(Y);
+    return 0;
+}
+
+/* The tensor step of the MSE quantizer (NV) for given bytes and codes of x's
+ * quantization: the least-squares tensor scale, or st_prev when
+ * sum(y p) <= 0.  Returns 0, or -1 on an invalid argument. */
+int mxo_mse_tensor_step(const uint16_t *x, int64_t R, int64_t C, int64_t ldx, int hadamard, int axis,
+                        const uint8_t *codes, const uint8_t *scales, float st_prev, float *st_out)
+{
+    if (!x || !codes || !scales || !st_out || R < 0 || C < 0 || ldx < C || (axis != 0 && axis != 1)) return -1;
+    const int64_t rows = (axis == 1) ? R : C;
+    const int64_t K = (axis == 1) ? C : R;
+    if (K % 16 != 0 || (hadamard && K % 32 != 0)) return -1;
+    if (rows == 0 || K == 0) {
+        *st_out = st_prev;
+        return 0;
+    }
+    float *Y = load_operand(x, ldx, hadamard, axis, rows, K);
+    if (!Y) return -1;
+    *st_out = ls_tensor_scale(Y, rows, K, codes, scales, st_prev);
     free(Y);
     return 0;
 }

@@ -70,3 +70,21 @@ def test_sign_of_zero_follows_butterfly(oracle_mod):
     x[0] = x[1] = 1.0
     y = oracle_mod.fwht32(x)
     assert y[1] == 0.0 and not np.signbit(y[1])
+
+
+def test_stride_order_on_a_hand_worked_vector(oracle_mod):
+    """The butterfly's evaluation order decides binary32 bits: for x = (2^24,
+    1, 1, 0, ...) strides 1, 2, 4, 8, 16 and the reverse order give different
+    results in slots 1 and 2 (mod 4), worked by hand in the fixture."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "fwht_stride_order.json")))
+    x = np.zeros(32, dtype=np.float32)
+    x[0], x[1], x[2] = 2.0 ** 24, 1.0, 1.0
+    y = oracle_mod.fwht32(x)
+    c = np.float64(np.float32(oracle_mod.hadamard_scale()))
+    # v * c is exact in binary64 (24 + 24 bits), so this is one binary32 rounding
+    want = np.array([np.float32(np.float64(g["unscaled_by_i_mod_4"][i % 4]) * c) for i in range(32)])
+    other = np.array([np.float32(np.float64(g["other_order_unscaled_by_i_mod_4"][i % 4]) * c) for i in range(32)])
+    assert not np.array_equal(want.view(np.uint32), other.view(np.uint32))
+    np.testing.assert_array_equal(y.view(np.uint32), want.view(np.uint32))
