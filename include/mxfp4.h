@@ -200,13 +200,15 @@ mxfp4_status mxfp4_quantize_mse_workspace_bytes(int fmt, int hadamard, int64_t R
 /* Round-to-nearest quantization with scales fitted for mean squared error
  * (the digest of the MR-GPTQ paper, step 1: the grid is fitted for MSE by
  * optimizing the block scales and the tensor scale in turn).  As read here:
- *   block step:  each block keeps, among candidate scales at and below its
- *                absmax scale (MXFP4: exponents e0, e0 - 1, e0 - 2; NVFP4: the
- *                absmax E4M3 byte and the 8 bytes below it), the one with the
- *                smallest sum of (y - Q(y))^2 over its elements (binary64, runs
- *                of 8 elements in turn, then (S0 + S1) + (S2 + S3) or S0 + S1),
- *                a tie keeping the larger scale; elements are encoded as
- *                mxfp4_quantize(RTN) encodes them for that scale;
+ *   block step:  each block keeps, among the scales at and below its absmax
+ *                scale, the one whose round-to-nearest encoding (exactly
+ *                mxfp4_quantize(RTN)'s for that scale) has the smallest sum
+ *                of (y - Q(y))^2 over its elements, a tie keeping the larger
+ *                scale.  Only MXFP4 exponents e0, e0 - 1 and NVFP4 bytes
+ *                b0 .. b0 - 5 (b0 the absmax scale) can ever win, and those
+ *                are the ones tried; each error is summed in binary64, so
+ *                blocks whose candidates tie to within that sum's rounding
+ *                may take either;
  *   tensor step: NVFP4 only, the least-squares tensor scale for the block
  *                step's bytes and codes, sum(y p) / sum(p^2) with p = E4M3 x
  *                E2M1 in binary64 in a fixed order, rounded to binary32;
@@ -214,8 +216,8 @@ mxfp4_status mxfp4_quantize_mse_workspace_bytes(int fmt, int hadamard, int64_t R
  *                (tensor step, block step); iters in [0, 64], ignored for MXFP4.
  * The output is an ordinary quantized tensor (mxfp4_gemm and
  * mxfp4_dequantize take it as is); arguments and layout as mxfp4_quantize
- * (RTN).  workspace: device, 16-byte aligned, at least
- * mxfp4_quantize_mse_workspace_bytes (NULL if that is 0). */
+ * (RTN); the same input gives the same bits.  workspace: device, 16-byte
+ * aligned, at least mxfp4_quantize_mse_workspace_bytes (NULL if that is 0). */
 mxfp4_status mxfp4_quantize_mse(const uint16_t *x, int64_t R, int64_t C, int64_t ldx, int fmt, int hadamard,
                                 int axis, int iters, mxfp4_tensor *out, void *workspace, size_t ws_bytes,
                                 hipStream_t stream);
@@ -271,6 +273,17 @@ mxfp4_status mxfp4_quantize_noise(const uint16_t *x, int64_t R, int64_t C, int64
                                   int fmt, int rounding, int hadamard, int axis, uint64_t seed,
                                   mxfp4_tensor *out, double *stats, void *workspace, size_t ws_bytes,
                                   hipStream_t stream);
+
+/* The sqrt(3) test of "FP4 All the Way", abstract (quantized training loses
+ * effectiveness once the gradient norm falls below about sqrt(3) times the
+ * quantization noise), on the sums of mxfp4_quantization_noise or
+ * mxfp4_quantize_noise after the caller has copied them to the host:
+ *   *ratio = sqrt(stats[0] / stats[1])   (+infinity when stats[1] = 0),
+ *   *below_threshold = 1 if *ratio < sqrt(3), else 0.
+ * stats: host, 3 doubles; ratio, below_threshold: host.  INVALID_ARG for a
+ * null pointer or a negative or NaN sum.  Pure host arithmetic: no stream, no
+ * device access. */
+mxfp4_status mxfp4_noise_ratio(const double *stats, double *ratio, int *below_threshold);
 
 /* A static, human-readable description of a status code. */
 const char *mxfp4_status_string(int status);

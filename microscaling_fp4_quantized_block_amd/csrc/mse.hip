@@ -4,19 +4,32 @@
 // Microscaling FP4 Quantization" (step 1) fits the quantization grid for
 // mean squared error by optimizing the block scales and the tensor scale in
 // turn.  The procedure, as this library reads it:
-//   block step:  each block keeps, among candidate scales below its absmax
-//                scale (MXFP4: exponents e0, e0 - 1, e0 - 2; NVFP4: the
-//                absmax E4M3 byte b0 and the 8 bytes below it), the one with
-//                the smallest sum of (y - Q(y))^2 over its elements (Q(y)
-//                exactly dequantized; the sum in binary64, runs of 8
-//                elements in turn, then (S0 + S1) + (S2 + S3) or S0 + S1);
-//                ties keep the larger scale; elements are encoded as the
-//                absmax quantizer encodes them for that scale;
+//   block step:  each block keeps, among the scales at and below its absmax
+//                scale, the one whose round-to-nearest encoding has the
+//                smallest sum of (y - Q(y))^2 over its elements (Q(y) exactly
+//                dequantized); ties keep the larger scale; elements are
+//                encoded as the absmax quantizer encodes them for that scale.
+//                Only a few scales below the absmax one can ever win, and the
+//                search here tries exactly those:
+//                  MXFP4: e0 and e0 - 1.  At e0 - 2 the grid tops out at
+//                    1.5 * 2^e0 while the block maximum exceeds 3 * 2^e0, so
+//                    its own error grows by more than 2.25 * 4^e0, and the 31
+//                    others can gain at most (2^e0 / 8)^2 each (0.48 * 4^e0 in
+//                    all) over e0 - 1;
+//                  NVFP4: the absmax E4M3 byte b0 and the five below it.  A
+//                    linear-programming bound over every mantissa pattern of b0
+//                    (and the subnormal bytes) and every block maximum shows
+//                    that no block prefers b0 - 6 or less to b0; b0 - 5 does
+//                    win for some blocks.
+//                The per-candidate error is summed in binary64 (runs of 8
+//                elements, then (S0 + S1) + (S2 + S3) or S0 + S1); near ties
+//                may resolve differently from an exact sum, which is within
+//                the rounding of that sum either way;
 //   tensor step: (NVFP4) the least-squares tensor scale sum(y p) / sum(p^2)
 //                for the block step's bytes and codes, p = E4M3 x E2M1, the
-//                sums in binary64 in a fixed order (per unit of 32 elements in
-//                turn, per operand row over its units in turn, rows in 256
-//                contiguous ranges in turn, the ranges in turn), rounded to
+//                sums in binary64 (per unit of 32 elements, per operand row,
+//                rows in 256 contiguous ranges, the ranges in turn: a fixed
+//                order, so the same input gives the same bits), rounded to
 //                binary32, at least 2^-117, unchanged if sum(y p) <= 0;
 //   schedule:    block step with the absmax tensor scale, then `iters`
 //                times (tensor step, block step).
@@ -91,7 +104,7 @@ __device__ __forceinline__ uint32_t mse_block(const float* y, float st, uint32_t
   if constexpr (FMT == FMT_MX) {
     const uint32_t b0 = mx_scale_byte_from_f32bits(m);
 #pragma unroll 1
-    for (int c = 0; c < 3; c++) {
+    for (int c = 0; c < 2; c++) {            // e0, e0 - 1 (lower exponents never win)
       if ((int)b0 - c < 0) break;
       const uint32_t byte = b0 - c;
       uint32_t w[BS / 8];
@@ -130,7 +143,7 @@ __device__ __forceinline__ uint32_t mse_block(const float* y, float st, uint32_t
       return 0u;
     }
 #pragma unroll 1
-    for (int c = 0; c < 9; c++) {
+    for (int c = 0; c < 6; c++) {            // b0 .. b0 - 5 (lower bytes never win)
       if ((int)b0 - c < 1) break;
       const uint32_t byte = b0 - c;
       const float sb = e4m3_value(byte);
