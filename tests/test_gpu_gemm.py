@@ -82,21 +82,35 @@ def test_gemm_writes_into_strided_output(oracle_mod):
     assert (host[:, :50] == 7.0).all() and (host[:, 146:] == 7.0).all()
 
 
+def stratified(n, block, nrand, rng):
+    """Indices 0 and n - 1, one random index inside every block of `block`
+    consecutive indices (so every output tile row / column is compared), and
+    nrand more at random."""
+    per_block = [int(rng.integers(b, min(b + block, n))) for b in range(0, n, block)]
+    extra = rng.choice(n, size=min(nrand, n), replace=False)
+    return np.unique(np.concatenate([[0, n - 1], per_block, extra]).astype(np.int64))
+
+
 def _sampled_check(mx, oracle_mod, qa, qb, oa, ob, fmt, what, nsample=48, seed=0):
+    """Full rows and full columns of C against the oracle: one row in every
+    256-row tile row and one column in every 128-column half tile, plus
+    rows / columns 0 and the last, plus nsample random ones each."""
     C = mx.mxfp4_gemm(qa, qb)
     torch.cuda.synchronize()
     rng = np.random.default_rng(seed)
     M, N = qa.rows, qb.rows
-    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, size=min(nsample, M), replace=False)]))
-    cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, size=min(nsample, N), replace=False)]))
+    rows = stratified(M, 256, nsample, rng)
+    cols = stratified(N, 128, nsample, rng)
     Cr = C[torch.from_numpy(rows).cuda()].cpu().numpy()
     Cc = C[:, torch.from_numpy(cols).cuda()].cpu().numpy()
+    del C
     # full rows and full columns of C
     Co_r, So_r = oracle_mod.gemm(fmt, oa, ob, rows=rows)
-    Co_c, So_c = oracle_mod.gemm(fmt, oa, ob, cols=cols)
     e1 = assert_gemm_within(Cr, Co_r, So_r, what + " rows")
+    del Co_r, So_r
+    Co_c, So_c = oracle_mod.gemm(fmt, oa, ob, cols=cols)
     e2 = assert_gemm_within(Cc, Co_c, So_c, what + " cols")
-    say(what, "max |err|/S", max(e1, e2))
+    say(what, f"{len(rows)} rows, {len(cols)} cols; max |err|/S", max(e1, e2))
 
 
 def test_gemm_headline_sampled(oracle_mod):
@@ -247,3 +261,92 @@ def test_gemm_is_deterministic(fmt, M, N, K):
     c2 = mx.mxfp4_gemm(qa, qb)
     torch.cuda.synchronize()
     assert torch.equal(c1.view(torch.int32), c2.view(torch.int32))
+
+
+# ---------------------------------------------------------------------------
+# Every configuration's GEMM shapes (forward XW^T, dgrad dY.W, wgrad dY^T.X),
+# with the operands quantized as the training step quantizes them: forward
+# operands round-to-nearest along K, backward operands stochastically rounded
+# along their own contraction axis (seeds 0..3 in order of use).
+# ---------------------------------------------------------------------------
+_TENSORS = {}
+
+
+def _tensor(cfg, name):
+    key = (cfg, name)
+    if key not in _TENSORS:
+        if len(_TENSORS) > 6:
+            _TENSORS.clear()
+        _TENSORS[key] = workloads.make_tensor(cfg, name)
+    return _TENSORS[key]
+
+
+def _training_pair(mx, oracle_mod, cfg, fmt, a, b, what, nsample=16):
+    """a, b = (tensor name, rounding, axis, seed): quantize both on the GPU and
+    in the oracle (bit-exact), then the sampled GEMM check."""
+    A, B = _tensor(cfg, a[0]), _tensor(cfg, b[0])
+    say(what, "quantize", a, b, A.shape, B.shape)
+    qa = mx.mxfp4_quantize(to_device_bf16(A), fmt, a[1], False, a[2], a[3])
+    qb = mx.mxfp4_quantize(to_device_bf16(B), fmt, b[1], False, b[2], b[3])
+    oa = oracle_mod.quantize(A, fmt, a[1], False, a[2], a[3])
+    ob = oracle_mod.quantize(B, fmt, b[1], False, b[2], b[3])
+    for g, o, t in ((q_to_host(qa), oa, "A"), (q_to_host(qb), ob, "B")):
+        assert np.array_equal(g[0], o[0]) and np.array_equal(g[1], o[1]) and g[2] == o[2], (what, t)
+    say(what, "gemm", qa.rows, qb.rows, qa.k, "ws", mx.mxfp4_gemm_workspace_bytes(qa, qb))
+    _sampled_check(mx, oracle_mod, qa, qb, oa, ob, fmt, what, nsample=nsample)
+
+
+def test_gemm_config5_qkv_forward(oracle_mod):
+    """NVFP4 16384 x 12288 x 4096: X [16384, 4096] t(3) times W_qkv^T."""
+    mx = need_gpu()
+    _training_pair(mx, oracle_mod, 5, "nv", ("X", "rtn", 1, 0), ("W_qkv", "rtn", 1, 0), "config5 qkv fwd")
+
+
+def test_gemm_config5_qkv_dgrad(oracle_mod):
+    """NVFP4 16384 x 4096 x 12288: dY_qkv [16384, 12288] along its rows times
+    W_qkv quantized along its rows' other axis (axis 0, [4096, 12288])."""
+    mx = need_gpu()
+    _training_pair(mx, oracle_mod, 5, "nv", ("dY_qkv", "sr", 1, 0), ("W_qkv", "sr", 0, 1), "config5 qkv dgrad")
+
+
+def test_gemm_config5_qkv_wgrad(oracle_mod):
+    """NVFP4 12288 x 4096 x 16384 (a contraction over all 16384 tokens, one
+    fp32 accumulator per output: 688 tiles, no split): dY_qkv^T X."""
+    mx = need_gpu()
+    _training_pair(mx, oracle_mod, 5, "nv", ("dY_qkv", "sr", 0, 2), ("X", "sr", 0, 3), "config5 qkv wgrad")
+
+
+def test_gemm_config5_down_wgrad(oracle_mod):
+    """NVFP4 4096 x 11008 x 16384: dY_down^T X_down (1024 fp16-MFMA steps per
+    accumulator, no split)."""
+    mx = need_gpu()
+    _training_pair(mx, oracle_mod, 5, "nv", ("dY_down", "sr", 0, 2), ("X_down", "sr", 0, 3), "config5 down wgrad")
+
+
+def test_gemm_config4_fc1_forward_and_dgrad(oracle_mod):
+    """MXFP4 50432 x 3072 x 768 (forward, RTN) and 50432 x 768 x 3072 (dgrad,
+    stochastic rounding: dY1 along its rows, W1 along axis 0)."""
+    mx = need_gpu()
+    _training_pair(mx, oracle_mod, 4, "mx", ("X1", "rtn", 1, 0), ("W1", "rtn", 1, 0), "config4 fc1 fwd")
+    _training_pair(mx, oracle_mod, 4, "mx", ("dY1", "sr", 1, 0), ("W1", "sr", 0, 1), "config4 fc1 dgrad")
+
+
+def test_gemm_config3_down_projection(oracle_mod):
+    """MXFP4 with block Hadamard: prefill 4096 x 4096 x 14336 (exactly 256
+    output tiles, so the 14336 contraction runs unsplit in one accumulator)
+    and decode 16 x 4096 x 14336."""
+    mx = need_gpu()
+    W = _tensor(3, "W_down")
+    say("config3 down quantize weights")
+    qw = mx.mxfp4_quantize(to_device_bf16(W), "mx", "rtn", True)
+    ow = oracle_mod.quantize(W, "mx", "rtn", True)
+    gw = q_to_host(qw)
+    assert np.array_equal(gw[0], ow[0]) and np.array_equal(gw[1], ow[1])
+    for name in ("x_pre_down", "x_dec_down"):
+        X = _tensor(3, name)
+        qx = mx.mxfp4_quantize(to_device_bf16(X), "mx", "rtn", True)
+        ox = oracle_mod.quantize(X, "mx", "rtn", True)
+        gx = q_to_host(qx)
+        assert np.array_equal(gx[0], ox[0]) and np.array_equal(gx[1], ox[1])
+        say("config3 down", name, "ws", mx.mxfp4_gemm_workspace_bytes(qx, qw))
+        _sampled_check(mx, oracle_mod, qx, qw, ox, ow, "mx", "config3 down " + name, nsample=16)
