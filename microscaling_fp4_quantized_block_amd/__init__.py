@@ -79,6 +79,8 @@ def _load_library() -> ctypes.CDLL:
     lib.mxfp4_quantization_noise_workspace_bytes.argtypes = [P(MxTensorStruct), P(sz)]
     lib.mxfp4_quantization_noise.restype = i32
     lib.mxfp4_quantization_noise.argtypes = [vp, i64, i32, P(MxTensorStruct), vp, vp, sz, vp]
+    lib.mxfp4_noise_ratio.restype = i32
+    lib.mxfp4_noise_ratio.argtypes = [P(ctypes.c_double), P(ctypes.c_double), P(i32)]
     return lib
 
 
@@ -106,6 +108,54 @@ def _stream(device: torch.device):
 
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_operands(*qs: "QTensor") -> torch.device:
+    """Quantized tensors must live on one GPU device, in contiguous buffers of
+    exactly the sizes their rows and k call for (the library reads and writes
+    that many bytes); returns the device."""
+    dev = qs[0].codes.device
+    for q in qs:
+        if q.fmt not in FMT or q.rows < 0 or q.k < 0 or q.k % BLOCK[q.fmt]:
+            raise ValueError("quantized tensor with a bad format or shape")
+        if q.codes.dtype != torch.uint8 or q.scales.dtype != torch.uint8:
+            raise ValueError("codes and scales must be uint8 tensors")
+        if q.codes.numel() != q.rows * (q.k // 2) or q.scales.numel() != q.rows * (q.k // BLOCK[q.fmt]):
+            raise ValueError("codes / scales sizes do not match the quantized tensor's rows and k")
+        if not q.codes.is_contiguous() or not q.scales.is_contiguous():
+            raise ValueError("codes and scales must be contiguous")
+        if q.fmt == "nv" and (q.tensor_scale is None or q.tensor_scale.dtype != torch.float32
+                              or q.tensor_scale.numel() < 1):
+            raise ValueError("an NVFP4 tensor needs a float32 tensor scale")
+        for t in (q.codes, q.scales) + ((q.tensor_scale,) if q.tensor_scale is not None else ()):
+            if not t.is_cuda or t.device != dev:
+                raise ValueError("quantized tensors must live on one CUDA/HIP device")
+    return dev
+
+
+def _nbytes(workspace: Optional[torch.Tensor], device) -> int:
+    """Byte size of a caller's workspace (0 for none); it must be contiguous
+    and on the call's device."""
+    if workspace is None:
+        return 0
+    if not workspace.is_contiguous() or not workspace.is_cuda or workspace.device != torch.device(device):
+        raise ValueError("workspace must be a contiguous tensor on the call's device")
+    return workspace.numel() * workspace.element_size()
+
+
+def _check_out(out: torch.Tensor, shape, dtype, device: torch.device, name: str = "out") -> None:
+    """The library cannot see buffer sizes: an output must be a 2-D tensor of
+    exactly this shape and dtype on this device, with unit stride along its
+    last dimension (any row stride >= its width), or the kernels would write
+    past it."""
+    if not isinstance(out, torch.Tensor) or out.dtype != dtype or out.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D {dtype} tensor")
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(out.shape)}, expected {tuple(shape)}")
+    if out.numel() and out.stride(1) != 1:
+        raise ValueError(f"{name} must have unit stride along its last dimension")
+    if not out.is_cuda or out.device != device:
+        raise ValueError(f"{name} must live on {device}")
 
 
 @dataclass
@@ -162,22 +212,25 @@ def mxfp4_quantize(x: torch.Tensor, fmt: str = "mx", rounding: str = "rtn", hada
     rows, k = (R, C) if axis == 1 else (C, R)
     if out is None:
         out = empty_qtensor(fmt, rows, k, hadamard, x.device)
+    if _check_operands(out) != x.device:
+        raise ValueError("out must live on x's device")
     ws_bytes = mxfp4_quantize_workspace_bytes(fmt, R, C, axis)
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
     st = out.as_struct()
     _check(lib.mxfp4_quantize(_ptr(x), R, C, x.stride(0), FMT[fmt], ROUNDING[rounding], int(bool(hadamard)),
                               int(axis), int(seed) & (2 ** 64 - 1), ctypes.byref(st), _ptr(workspace),
-                              workspace.numel() if workspace is not None else 0, _stream(x.device)))
+                              _nbytes(workspace, x.device), _stream(x.device)))
     return out
 
 
 def mxfp4_dequantize(q: QTensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    dev = _check_operands(q)
     if out is None:
-        out = torch.empty((q.rows, q.k), dtype=torch.float32, device=q.codes.device)
+        out = torch.empty((q.rows, q.k), dtype=torch.float32, device=dev)
+    _check_out(out, (q.rows, q.k), torch.float32, dev)
     st = q.as_struct()
-    _check(lib.mxfp4_dequantize(ctypes.byref(st), _ptr(out), out.stride(0) if out.dim() == 2 else q.k,
-                                _stream(q.codes.device)))
+    _check(lib.mxfp4_dequantize(ctypes.byref(st), _ptr(out), max(out.stride(0), q.k), _stream(dev)))
     return out
 
 
@@ -191,14 +244,16 @@ def mxfp4_gemm_workspace_bytes(qa: QTensor, qb: QTensor) -> int:
 def mxfp4_gemm(qa: QTensor, qb: QTensor, out: Optional[torch.Tensor] = None,
                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """C[M, N] = A B^T in FP32 over the dequantized operands."""
+    dev = _check_operands(qa, qb)
     if out is None:
-        out = torch.empty((qa.rows, qb.rows), dtype=torch.float32, device=qa.codes.device)
+        out = torch.empty((qa.rows, qb.rows), dtype=torch.float32, device=dev)
+    _check_out(out, (qa.rows, qb.rows), torch.float32, dev)
     ws_bytes = mxfp4_gemm_workspace_bytes(qa, qb)
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=qa.codes.device)
     sa, sb = qa.as_struct(), qb.as_struct()
-    _check(lib.mxfp4_gemm(ctypes.byref(sa), ctypes.byref(sb), _ptr(out), out.stride(0), _ptr(workspace),
-                          workspace.numel() if workspace is not None else 0, _stream(qa.codes.device)))
+    _check(lib.mxfp4_gemm(ctypes.byref(sa), ctypes.byref(sb), _ptr(out), max(out.stride(0), qb.rows), _ptr(workspace),
+                          _nbytes(workspace, dev), _stream(dev)))
     return out
 
 
@@ -206,16 +261,17 @@ def mxfp4_gemm_bf16(qa: QTensor, qb: QTensor, out: Optional[torch.Tensor] = None
                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """C[M, N] = A B^T as mxfp4_gemm computes it, rounded to bfloat16 (nearest
     even)."""
+    dev = _check_operands(qa, qb)
     if out is None:
-        out = torch.empty((qa.rows, qb.rows), dtype=torch.bfloat16, device=qa.codes.device)
-    if out.dtype != torch.bfloat16 or out.dim() != 2 or (out.numel() and out.stride(1) != 1):
-        raise ValueError("out must be a 2-D bfloat16 tensor with unit stride along its last dimension")
+        out = torch.empty((qa.rows, qb.rows), dtype=torch.bfloat16, device=dev)
+    _check_out(out, (qa.rows, qb.rows), torch.bfloat16, dev)
     ws_bytes = mxfp4_gemm_workspace_bytes(qa, qb)
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=qa.codes.device)
     sa, sb = qa.as_struct(), qb.as_struct()
-    _check(lib.mxfp4_gemm_bf16(ctypes.byref(sa), ctypes.byref(sb), _ptr(out), out.stride(0), _ptr(workspace),
-                               workspace.numel() if workspace is not None else 0, _stream(qa.codes.device)))
+    _check(lib.mxfp4_gemm_bf16(ctypes.byref(sa), ctypes.byref(sb), _ptr(out), max(out.stride(0), qb.rows),
+                               _ptr(workspace),
+                               _nbytes(workspace, dev), _stream(dev)))
     return out
 
 
@@ -236,14 +292,18 @@ def mxfp4_quantize_gemm(x: torch.Tensor, qb: QTensor, hadamard: bool = False, ou
     if x.stride(1) != 1:
         raise ValueError("x must have unit stride along its last dimension")
     M, K = x.shape
+    dev = _check_operands(qb)
+    if x.device != dev:
+        raise ValueError("x and the weights must live on one device")
     if out is None:
-        out = torch.empty((M, qb.rows), dtype=torch.float32, device=x.device)
+        out = torch.empty((M, qb.rows), dtype=torch.float32, device=dev)
+    _check_out(out, (M, qb.rows), torch.float32, dev)
     ws_bytes = mxfp4_quantize_gemm_workspace_bytes(M, K, hadamard, qb)
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
     sb = qb.as_struct()
     _check(lib.mxfp4_quantize_gemm(_ptr(x), M, K, x.stride(0), int(bool(hadamard)), ctypes.byref(sb), _ptr(out),
-                                   out.stride(0), _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                   max(out.stride(0), qb.rows), _ptr(workspace), _nbytes(workspace, x.device),
                                    _stream(x.device)))
     return out
 
@@ -264,12 +324,14 @@ def mxfp4_quantize_mse(x: torch.Tensor, fmt: str = "nv", hadamard: bool = False,
     rows, k = (R, C) if axis == 1 else (C, R)
     if out is None:
         out = empty_qtensor(fmt, rows, k, hadamard, x.device)
+    if _check_operands(out) != x.device:
+        raise ValueError("out must live on x's device")
     ws_bytes = mxfp4_quantize_mse_workspace_bytes(fmt, hadamard, R, C, axis)
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
     st = out.as_struct()
     _check(lib.mxfp4_quantize_mse(_ptr(x), R, C, x.stride(0), FMT[fmt], int(bool(hadamard)), int(axis), int(iters),
-                                  ctypes.byref(st), _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                  ctypes.byref(st), _ptr(workspace), _nbytes(workspace, x.device),
                                   _stream(x.device)))
     return out
 
@@ -288,14 +350,18 @@ def mxfp4_quantization_noise(x: torch.Tensor, q: QTensor, axis: int = 1, out: Op
     contraction rows, rotated when q is), Q(y) their dequantized values."""
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda or x.stride(1) != 1:
         raise ValueError("x must be a 2-D bfloat16 CUDA/HIP tensor with unit stride along its last dimension")
+    if _check_operands(q) != x.device:
+        raise ValueError("x and q must live on one device")
     if out is None:
         out = torch.empty(3, dtype=torch.float64, device=x.device)
+    if out.dtype != torch.float64 or out.numel() < 3 or not out.is_contiguous() or out.device != x.device:
+        raise ValueError("out must be a contiguous float64 tensor of 3 elements on x's device")
     ws_bytes = mxfp4_quantization_noise_workspace_bytes(q)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
     sq = q.as_struct()
     _check(lib.mxfp4_quantization_noise(_ptr(x), x.stride(0), int(axis), ctypes.byref(sq), _ptr(out),
-                                        _ptr(workspace), workspace.numel(), _stream(x.device)))
+                                        _ptr(workspace), _nbytes(workspace, x.device), _stream(x.device)))
     return out
 
 
@@ -317,25 +383,38 @@ def mxfp4_quantize_noise(x: torch.Tensor, fmt: str = "mx", rounding: str = "sr",
     rows, k = (R, C) if axis == 1 else (C, R)
     if out is None:
         out = empty_qtensor(fmt, rows, k, hadamard, x.device)
+    if _check_operands(out) != x.device:
+        raise ValueError("out must live on x's device")
     if stats is None:
         stats = torch.empty(3, dtype=torch.float64, device=x.device)
+    if stats.dtype != torch.float64 or stats.numel() < 3 or not stats.is_contiguous() or stats.device != x.device:
+        raise ValueError("stats must be a contiguous float64 tensor of 3 elements on x's device")
     ws_bytes = mxfp4_quantize_noise_workspace_bytes(fmt, hadamard, R, C, axis)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
     st = out.as_struct()
     _check(lib.mxfp4_quantize_noise(_ptr(x), R, C, x.stride(0), FMT[fmt], ROUNDING[rounding], int(bool(hadamard)),
                                     int(axis), int(seed) & (2 ** 64 - 1), ctypes.byref(st), _ptr(stats),
-                                    _ptr(workspace), workspace.numel(), _stream(x.device)))
+                                    _ptr(workspace), _nbytes(workspace, x.device), _stream(x.device)))
     return out, stats
 
 
+def mxfp4_noise_ratio(stats) -> tuple:
+    """(ratio, below) of the sqrt(3) test ("FP4 All the Way", abstract) from
+    the three sums of mxfp4_quantization_noise / mxfp4_quantize_noise (a host
+    sequence or tensor): computed by the library's mxfp4_noise_ratio."""
+    if isinstance(stats, torch.Tensor):
+        stats = stats.detach().cpu().tolist()
+    arr = (ctypes.c_double * 3)(*[float(v) for v in stats])
+    ratio, below = ctypes.c_double(), ctypes.c_int()
+    _check(lib.mxfp4_noise_ratio(arr, ctypes.byref(ratio), ctypes.byref(below)))
+    return ratio.value, bool(below.value)
+
+
 def gradient_noise_ratio(x: torch.Tensor, q: QTensor, axis: int = 1):
-    """(ratio, below): ratio = ||y|| / ||Q(y) - y|| for the quantized operand,
-    and whether it falls below sqrt(3), the threshold under which quantized
-    training loses effectiveness ("FP4 All the Way", abstract)."""
-    s = mxfp4_quantization_noise(x, q, axis).cpu().tolist()
-    ratio = float("inf") if s[1] == 0.0 else (s[0] / s[1]) ** 0.5
-    return ratio, ratio < 3.0 ** 0.5
+    """(ratio, below) for the quantized operand q of x: the noise sums on the
+    GPU, then the library's sqrt(3) test on them."""
+    return mxfp4_noise_ratio(mxfp4_quantization_noise(x, q, axis))
 
 
 quantize = mxfp4_quantize
@@ -347,6 +426,7 @@ __all__ = ["QTensor", "MxFp4Error", "mxfp4_tensor_bytes", "mxfp4_quantize_worksp
            "mxfp4_dequantize", "mxfp4_gemm_workspace_bytes", "mxfp4_gemm", "mxfp4_gemm_bf16", "mxfp4_status_string",
            "mxfp4_quantize_gemm_workspace_bytes", "mxfp4_quantize_gemm",
            "mxfp4_quantization_noise_workspace_bytes", "mxfp4_quantization_noise", "gradient_noise_ratio",
+           "mxfp4_noise_ratio",
            "mxfp4_quantize_noise_workspace_bytes", "mxfp4_quantize_noise",
            "mxfp4_quantize_mse_workspace_bytes", "mxfp4_quantize_mse",
            "quantize", "dequantize", "gemm", "quantize_gemm", "empty_qtensor", "lib", "LIB_PATH"]

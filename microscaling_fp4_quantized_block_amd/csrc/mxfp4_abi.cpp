@@ -39,6 +39,15 @@ const char* mxfp4_status_string(int status) {
   }
 }
 
+mxfp4_status mxfp4_noise_ratio(const double* stats, double* ratio, int* below_threshold) {
+  if (!stats || !ratio || !below_threshold) return MXFP4_ERR_INVALID_ARG;
+  const double signal = stats[0], noise = stats[1];
+  if (!(signal >= 0.0) || !(noise >= 0.0)) return MXFP4_ERR_INVALID_ARG;   // also rejects NaN
+  *ratio = noise == 0.0 ? __builtin_inf() : __builtin_sqrt(signal / noise);
+  *below_threshold = *ratio < __builtin_sqrt(3.0) ? 1 : 0;
+  return MXFP4_OK;
+}
+
 mxfp4_status mxfp4_tensor_bytes(int fmt, int64_t rows, int64_t k, size_t* codes_bytes, size_t* scales_bytes) {
   if (!fmt_ok(fmt) || rows < 0 || k < 0 || !codes_bytes || !scales_bytes) return MXFP4_ERR_INVALID_ARG;
   if (k % block_of(fmt) != 0) return MXFP4_ERR_UNSUPPORTED_SHAPE;

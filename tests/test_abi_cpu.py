@@ -345,3 +345,53 @@ def test_quantize_mse_workspace_bytes(mx):
     assert mx.mxfp4_quantize_mse_workspace_bytes("nv", False, 10, 80) == 4096 + 10 * 5 * 16 + 10 * 16
     # axis 0: rows = C, k = R
     assert mx.mxfp4_quantize_mse_workspace_bytes("nv", True, 256, 64, 0) == 4096 + 64 * 8 * 16 + 64 * 16
+
+
+def test_noise_ratio_is_the_sqrt3_test(mx):
+    """mxfp4_noise_ratio: sqrt(signal / noise) against sqrt(3) ("FP4 All the
+    Way", abstract), host arithmetic only."""
+    assert mx.mxfp4_noise_ratio([12.0, 3.0, 0.0]) == (2.0, False)
+    r, below = mx.mxfp4_noise_ratio([2.0, 1.0, 0.0])
+    assert r == 2.0 ** 0.5 and below
+    r, below = mx.mxfp4_noise_ratio([3.0, 1.0, 0.0])      # exactly sqrt(3): not below
+    assert not below
+    assert mx.mxfp4_noise_ratio([1.0, 0.0, 0.0]) == (float("inf"), False)
+    d = ctypes.c_double()
+    i = ctypes.c_int()
+    bad = (ctypes.c_double * 3)(float("nan"), 1.0, 0.0)
+    assert mx.lib.mxfp4_noise_ratio(bad, ctypes.byref(d), ctypes.byref(i)) == INVALID
+    neg = (ctypes.c_double * 3)(1.0, -1.0, 0.0)
+    assert mx.lib.mxfp4_noise_ratio(neg, ctypes.byref(d), ctypes.byref(i)) == INVALID
+    assert mx.lib.mxfp4_noise_ratio(None, ctypes.byref(d), ctypes.byref(i)) == INVALID
+
+
+def test_binding_rejects_outputs_the_kernels_would_overrun(mx):
+    """The library cannot see buffer sizes, so the binding checks every output
+    and operand buffer before anything is launched (all raises below happen
+    on the host; no GPU is needed)."""
+    import torch
+    dev = torch.device("cuda", 0)
+    with pytest.raises(ValueError, match="2-D"):
+        mx._check_out(torch.empty(4, 5, dtype=torch.bfloat16), (4, 5), torch.float32, dev)
+    with pytest.raises(ValueError, match="shape"):
+        mx._check_out(torch.empty(4, 4), (4, 5), torch.float32, dev)
+    with pytest.raises(ValueError, match="stride"):
+        mx._check_out(torch.empty(5, 4).t(), (4, 5), torch.float32, dev)
+    with pytest.raises(ValueError, match="live on"):
+        mx._check_out(torch.empty(4, 5), (4, 5), torch.float32, dev)
+    qa = mx.empty_qtensor("mx", 64, 256, False, "cpu")
+    qb = mx.empty_qtensor("mx", 32, 256, False, "cpu")
+    with pytest.raises(ValueError, match="device"):
+        mx.mxfp4_gemm(qa, qb)
+    with pytest.raises(ValueError, match="device"):
+        mx.mxfp4_dequantize(qa)
+    short = mx.QTensor("mx", False, 64, 256, torch.empty(64 * 127, dtype=torch.uint8),
+                       torch.empty(64 * 8, dtype=torch.uint8), None)
+    with pytest.raises(ValueError, match="sizes"):
+        mx._check_operands(short)
+    nv = mx.QTensor("nv", False, 16, 64, torch.empty(16, 32, dtype=torch.uint8),
+                    torch.empty(16, 4, dtype=torch.uint8), None)
+    with pytest.raises(ValueError, match="tensor scale"):
+        mx._check_operands(nv)
+    with pytest.raises(ValueError, match="workspace"):
+        mx._nbytes(torch.empty(16, dtype=torch.uint8), dev)
