@@ -623,7 +623,7 @@ static int64_t launch_cols(ColArgs a, bool tiled, bool vec, bool launch, hipStre
     }
     const int64_t wgs = (int64_t)grid.x * grid.y;
     n += wgs;
-    if (STATS) a.parts += 3 * wgs;
+    if (STATS && a.parts) a.parts += 3 * wgs;   // (null when only counting)
   }
   return n;
 }
@@ -646,7 +646,7 @@ static int64_t launch_rows_sliced(const uint16_t* x, int64_t R, int64_t C, int64
   auto go = [&](int load) {
     const int64_t g = launch_rows<FMT, RND, HAD, STATS>(a, load, launch, s);
     n += g;
-    if (STATS) a.parts += 3 * g;
+    if (STATS && a.parts) a.parts += 3 * g;   // (null when only counting)
   };
   const int elem = aligned16 ? 0 : 1;
   auto packed_range = [&](const uint16_t* xr, uint64_t t0, uint64_t m_all) {
