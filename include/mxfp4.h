@@ -115,6 +115,24 @@ mxfp4_status mxfp4_quantize(const uint16_t *x, int64_t R, int64_t C, int64_t ldx
                             mxfp4_tensor *out, void *workspace, size_t ws_bytes,
                             hipStream_t stream);
 
+/* mxfp4_quantize for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments and the same output bits, with no workspace argument.
+ * The NVFP4 tensor-amax partials go to a static device array inside the
+ * library instead: 1 MiB per device (262144 partials, one per 16 Ki input
+ * elements), held by each device the library runs on until the process
+ * ends.  Inputs whose partials would not fit (mxfp4_quantize_workspace_bytes
+ * above 1 MiB, i.e. NVFP4 tensors of more than about 4.29e9 elements) are
+ * rejected with MXFP4_ERR_WORKSPACE before anything is launched.  Calls on
+ * one device share that array: calls that overlap on one device (other
+ * streams, other host threads) race on it and must be serialized by the
+ * caller.  The call allocates and frees nothing; the first call on a device
+ * looks the array's address up (MXFP4_ERR_HIP if that fails).  MXFP4 needs no
+ * scratch. */
+mxfp4_status mxfp4_quantize_noalloc(const uint16_t *x, int64_t R, int64_t C, int64_t ldx,
+                                    int fmt, int rounding, int hadamard, int axis, uint64_t seed,
+                                    mxfp4_tensor *out, hipStream_t stream);
+
 /* Dequantize q into y [q->rows, q->k] FP32 (device, leading dimension ldy >=
  * q->k): value = E2M1(code) * scale (NVFP4: * tensor_scale).  A rotated
  * tensor stays in the rotated domain. */

@@ -54,6 +54,8 @@ def _load_library() -> ctypes.CDLL:
     lib.mxfp4_quantize_workspace_bytes.argtypes = [i32, i64, i64, i32, P(sz)]
     lib.mxfp4_quantize.restype = i32
     lib.mxfp4_quantize.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, u64, P(MxTensorStruct), vp, sz, vp]
+    lib.mxfp4_quantize_noalloc.restype = i32
+    lib.mxfp4_quantize_noalloc.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, u64, P(MxTensorStruct), vp]
     lib.mxfp4_dequantize.restype = i32
     lib.mxfp4_dequantize.argtypes = [P(MxTensorStruct), vp, i64, vp]
     lib.mxfp4_gemm_workspace_bytes.restype = i32
@@ -221,6 +223,24 @@ def mxfp4_quantize(x: torch.Tensor, fmt: str = "mx", rounding: str = "rtn", hada
     _check(lib.mxfp4_quantize(_ptr(x), R, C, x.stride(0), FMT[fmt], ROUNDING[rounding], int(bool(hadamard)),
                               int(axis), int(seed) & (2 ** 64 - 1), ctypes.byref(st), _ptr(workspace),
                               _nbytes(workspace, x.device), _stream(x.device)))
+    return out
+
+
+def mxfp4_quantize_noalloc(x: torch.Tensor, out: QTensor, fmt: str = "mx", rounding: str = "rtn",
+                           hadamard: bool = False, axis: int = 1, seed: int = 0) -> QTensor:
+    """mxfp4_quantize into a caller-allocated out, with no workspace: the
+    library's entry point for callers that cannot allocate (the NVFP4 amax
+    partials live in a static 1 MiB device array; overlapping calls on one
+    device race on it)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bfloat16 CUDA/HIP tensor with unit stride along its last dimension")
+    R, C = x.shape
+    rows, k = (R, C) if axis == 1 else (C, R)
+    if _check_operands(out) != x.device or (out.rows, out.k, out.fmt) != (rows, k, fmt):
+        raise ValueError("out must match the call (rows, k, fmt) and live on x's device")
+    st = out.as_struct()
+    _check(lib.mxfp4_quantize_noalloc(_ptr(x), R, C, x.stride(0), FMT[fmt], ROUNDING[rounding], int(bool(hadamard)),
+                                      int(axis), int(seed) & (2 ** 64 - 1), ctypes.byref(st), _stream(x.device)))
     return out
 
 
@@ -423,6 +443,7 @@ gemm = mxfp4_gemm
 quantize_gemm = mxfp4_quantize_gemm
 
 __all__ = ["QTensor", "MxFp4Error", "mxfp4_tensor_bytes", "mxfp4_quantize_workspace_bytes", "mxfp4_quantize",
+           "mxfp4_quantize_noalloc",
            "mxfp4_dequantize", "mxfp4_gemm_workspace_bytes", "mxfp4_gemm", "mxfp4_gemm_bf16", "mxfp4_status_string",
            "mxfp4_quantize_gemm_workspace_bytes", "mxfp4_quantize_gemm",
            "mxfp4_quantization_noise_workspace_bytes", "mxfp4_quantization_noise", "gradient_noise_ratio",

@@ -62,9 +62,15 @@ mxfp4_status mxfp4_quantize_workspace_bytes(int fmt, int64_t R, int64_t C, int a
   return MXFP4_OK;
 }
 
-mxfp4_status mxfp4_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int fmt, int rounding,
-                            int hadamard, int axis, uint64_t seed, mxfp4_tensor* out, void* workspace,
-                            size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of mxfp4_quantize (and its no-allocation variant); OK with
+// *empty set when there is nothing to do.
+mxfp4_status check_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int fmt, int rounding,
+                            int hadamard, int axis, const mxfp4_tensor* out, bool* empty) {
+  *empty = false;
   if (!fmt_ok(fmt) || (rounding != MXFP4_RTN && rounding != MXFP4_SR) || (hadamard != 0 && hadamard != 1) ||
       (axis != 0 && axis != 1) || !out)
     return MXFP4_ERR_INVALID_ARG;
@@ -74,16 +80,49 @@ mxfp4_status mxfp4_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx
   if (R > 0 && C > kMaxElems / R) return MXFP4_ERR_UNSUPPORTED_SHAPE;
   if (out->fmt != fmt || out->rows != rows || out->k != k || out->hadamard != hadamard)
     return MXFP4_ERR_INVALID_ARG;
-  if (rows == 0 || k == 0) return MXFP4_OK;
+  if (rows == 0 || k == 0) {
+    *empty = true;
+    return MXFP4_OK;
+  }
   if (!x || !out->codes || !out->scales) return MXFP4_ERR_INVALID_ARG;
   // the kernels store codes as aligned 32-bit (rows) or 8/16-byte (transposed) words
   if (!aligned(out->codes, 16)) return MXFP4_ERR_INVALID_ARG;
+  if (fmt == MXFP4_FMT_NV && !out->tensor_scale) return MXFP4_ERR_INVALID_ARG;
+  return MXFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mxfp4_status mxfp4_quantize(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int fmt, int rounding,
+                            int hadamard, int axis, uint64_t seed, mxfp4_tensor* out, void* workspace,
+                            size_t ws_bytes, hipStream_t stream) {
+  bool empty;
+  const mxfp4_status st = check_quantize(x, R, C, ldx, fmt, rounding, hadamard, axis, out, &empty);
+  if (st != MXFP4_OK || empty) return st;
   uint32_t* partials = nullptr;
   if (fmt == MXFP4_FMT_NV) {
-    if (!out->tensor_scale) return MXFP4_ERR_INVALID_ARG;
     if (!workspace || ws_bytes < mxfp4::quantize_workspace_bytes(fmt, R, C) || !aligned(workspace, 4))
       return MXFP4_ERR_WORKSPACE;
     partials = (uint32_t*)workspace;
+  }
+  hipError_t e = mxfp4::launch_quantize(x, R, C, ldx, fmt, rounding, hadamard, axis, seed, out->codes,
+                                        out->scales, out->tensor_scale, partials, stream);
+  return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
+}
+
+mxfp4_status mxfp4_quantize_noalloc(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int fmt, int rounding,
+                                    int hadamard, int axis, uint64_t seed, mxfp4_tensor* out, hipStream_t stream) {
+  bool empty;
+  const mxfp4_status st = check_quantize(x, R, C, ldx, fmt, rounding, hadamard, axis, out, &empty);
+  if (st != MXFP4_OK || empty) return st;
+  uint32_t* partials = nullptr;
+  if (fmt == MXFP4_FMT_NV) {
+    if (mxfp4::quantize_workspace_bytes(fmt, R, C) > mxfp4::noalloc_scratch_bytes()) return MXFP4_ERR_WORKSPACE;
+    void* p = nullptr;
+    if (mxfp4::noalloc_scratch(&p) != hipSuccess) return MXFP4_ERR_HIP;
+    partials = (uint32_t*)p;
   }
   hipError_t e = mxfp4::launch_quantize(x, R, C, ldx, fmt, rounding, hadamard, axis, seed, out->codes,
                                         out->scales, out->tensor_scale, partials, stream);

@@ -77,4 +77,9 @@ hipError_t launch_noise(const uint16_t* x, int64_t ldx, int axis, int fmt, int h
                         const uint8_t* codes, const uint8_t* scales, const float* ts, double* stats,
                         double* partials, hipStream_t stream);
 
+// The static device scratch of mxfp4_quantize_noalloc (noalloc.hip): its size,
+// and the current device's address of it (looked up once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** out);
+
 }  // namespace mxfp4

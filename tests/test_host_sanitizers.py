@@ -18,7 +18,7 @@ CLANG = "/opt/rocm/lib/llvm/bin/clang"      # the host compiler hipcc drives: on
 
 @pytest.mark.skipif(not os.path.exists(HIPCC) or not os.path.exists(CLANG), reason="needs hipcc and ROCm clang")
 def test_abi_and_oracle_clean_under_host_sanitizers(tmp_path):
-    srcs = [os.path.join(CSRC, s) for s in ("quantize.hip", "gemm.hip", "noise.hip", "mse.hip", "mxfp4_abi.cpp")]
+    srcs = [os.path.join(CSRC, s) for s in ("quantize.hip", "gemm.hip", "noise.hip", "mse.hip", "noalloc.hip", "mxfp4_abi.cpp")]
     lib = str(tmp_path / "libmxfp4_san.so")
     # sanitizers on the host code only: each -fsanitize= right after -Xarch_host
     cmd = [HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, "-o", lib]
