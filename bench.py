@@ -318,6 +318,69 @@ def settle_trace(out_md, steps=1500):
     print(open(out_md).read())
 
 
+class ClockStamps:
+    """Shader-clock stamps around the timed steps (libmxclock.so, built next to
+    libmxfp4.so): each XCD's average shader clock over the steps is
+    d(s_memtime) / d(s_memrealtime) times the real-time counter's rate."""
+
+    def __init__(self, device):
+        import ctypes
+        import torch
+        here = os.path.join(ROOT, "microscaling_fp4_quantized_block_amd", "libmxclock.so")
+        self.lib = ctypes.CDLL(here)
+        self.lib.mxclock_stamp.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.mxclock_stamp.restype = ctypes.c_int
+        self.lib.mxclock_stamp_slots.restype = ctypes.c_int
+        self.lib.mxclock_wall_rate_khz.restype = ctypes.c_int
+        n = self.lib.mxclock_stamp_slots()
+        self.buf = [torch.zeros(n, dtype=torch.int64, device=device) for _ in range(2)]
+        self.device = device
+        self.ctypes = ctypes
+
+    def stamp(self, i):
+        import torch
+        stream = self.ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
+        if self.lib.mxclock_stamp(self.ctypes.c_void_p(self.buf[i].data_ptr()), stream) != 0:
+            raise RuntimeError("clock stamp launch failed")
+
+    def summary(self):
+        rate_khz = self.lib.mxclock_wall_rate_khz()
+        a, b = (t.cpu().numpy().view(np.uint64).reshape(-1, 3) for t in self.buf)
+        # one stamp per place (XCD + compute unit) and launch; the clock of a
+        # place that ran a workgroup of both launches
+        s0 = {int(r[0]): r for r in a}
+        s1 = {int(r[0]): r for r in b}
+        mhz = {}
+        for key in sorted(set(s0) & set(s1)):
+            dt = int(s1[key][1]) - int(s0[key][1])
+            dr = int(s1[key][2]) - int(s0[key][2])
+            if dr > 0 and dt > 0:
+                mhz[key] = dt / (dr / (rate_khz * 1e3)) / 1e6
+        vals = np.array(list(mhz.values()))
+        per_xcd = {}
+        for key, v in mhz.items():
+            per_xcd.setdefault(key >> 8, []).append(v)
+        wall = float(np.median(b[:, 2].astype(np.int64) - a[:, 2].astype(np.int64))) / (rate_khz * 1e3) if rate_khz else None
+        return {"sclk_mhz_median": round(float(np.median(vals)), 1) if len(vals) else None,
+                "sclk_mhz_min": round(float(vals.min()), 1) if len(vals) else None,
+                "sclk_mhz_max": round(float(vals.max()), 1) if len(vals) else None,
+                "sclk_mhz_per_xcd": [round(float(np.median(per_xcd[x])), 1) for x in sorted(per_xcd)],
+                "compute_units_paired": int(len(vals)),
+                "wall_s": round(wall, 6) if wall is not None else None,
+                "source": "s_memtime / s_memrealtime of each compute unit, stamped before and after the timed steps"}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline():
     """The CPU oracle on a bounded sample of the step, scaled to the whole step."""
     import oracle
@@ -343,6 +406,7 @@ def cpu_baseline():
         "value": 2.0 * M * N * K / step_s / 1e12,
         "unit": "TFLOP/s",
         "cores": cores,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"quantize {qa_rows} of {M} rows of A and {qb_rows} of {N} rows of B, "
                    f"fp64 GEMM of {g_rows}x{g_cols} outputs (K={K}); each part scaled to the full step"),
@@ -683,10 +747,13 @@ def main():
     torch.cuda.synchronize()
     new_events = lambda: [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     events = new_events()
+    clock = ClockStamps(dev)
     torch.cuda.synchronize()
+    clock.stamp(0)
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
+    clock.stamp(1)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -733,6 +800,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1), "peak": PEAK_FP4_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
                      "traffic": traffic},
+        "clock": clock.summary(),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()

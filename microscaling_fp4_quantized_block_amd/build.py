@@ -27,16 +27,26 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, "-o", LIB + ".tmp"]
+# The benchmark's shader-clock stamps: a separate library, not part of libmxfp4.
+CLOCK_LIB = os.path.join(HERE, "libmxclock.so")
+CLOCK_SOURCES = ["clock_stamp.hip"]
+
+
+def _hipcc(sources, out, verbose):
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libmxfp4.so")
-    os.replace(LIB + ".tmp", LIB)
+        raise RuntimeError(f"hipcc failed building {os.path.basename(out)}")
+    os.replace(out + ".tmp", out)
+
+
+def build(verbose: bool = False) -> str:
+    _hipcc(SOURCES, LIB, verbose)
+    _hipcc(CLOCK_SOURCES, CLOCK_LIB, verbose)
     return LIB
 
 
