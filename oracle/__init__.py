@@ -83,6 +83,10 @@ def _load():
     lib.mxo_mse_check.argtypes = [vp, i64, i64, i64, i32, i32, i32, ctypes.c_float, vp, vp, ctypes.c_double, vp]
     lib.mxo_mse_tensor_step.restype = i32
     lib.mxo_mse_tensor_step.argtypes = [vp, i64, i64, i64, i32, i32, vp, vp, ctypes.c_float, vp]
+    lib.mxo_quantize_f32.restype = i32
+    lib.mxo_quantize_f32.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, u64, vp, vp, vp]
+    lib.mxo_qema_quantize.restype = i32
+    lib.mxo_qema_quantize.argtypes = [vp, i64, i64, i64, vp, i64, ctypes.c_float, i32, vp, vp]
     lib.mxo_noise_stats.restype = i32
     lib.mxo_noise_stats.argtypes = [vp, i64, i64, i64, i32, i32, i32, vp, vp, vp, vp]
     _lib = lib
@@ -303,3 +307,37 @@ def mse_tensor_step(x_bits: np.ndarray, q, hadamard: bool = False, axis: int = 1
     if rc != 0:
         raise ValueError("oracle mse_tensor_step rejected its arguments")
     return float(out[0])
+
+
+def quantize_f32(x: np.ndarray, fmt: str = "mx", rounding: str = "rtn", hadamard: bool = False, axis: int = 1,
+                 seed: int = 0):
+    """quantize() on a binary32 [R, C] input (values used as they are)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    R, C = x.shape
+    rows, K = (R, C) if axis == 1 else (C, R)
+    bs = BLOCK[fmt]
+    codes = np.zeros((rows, K // 2), dtype=np.uint8)
+    scales = np.zeros((rows, K // bs), dtype=np.uint8)
+    ts = np.zeros(1, dtype=np.float32) if fmt == "nv" else None
+    rc = _load().mxo_quantize_f32(_ptr(x), R, C, C, FMT[fmt], ROUNDING[rounding], int(bool(hadamard)), int(axis),
+                                  int(seed), _ptr(codes), _ptr(scales), _ptr(ts))
+    if rc != 0:
+        raise ValueError("oracle quantize_f32 rejected its arguments")
+    return codes, scales, (float(ts[0]) if ts is not None else None)
+
+
+def qema_quantize(w_bits: np.ndarray, ema: np.ndarray, beta: float, hadamard: bool = False):
+    """Q-EMA step (reading, parity unpinned as to the method): ema <- RN(RN(beta
+    ema) + RN((1 - beta) w)) in binary32, then MXFP4 round-to-nearest of the
+    updated ema along its rows.  Returns (new ema, (codes, scales, None))."""
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    m = np.ascontiguousarray(ema, dtype=np.float32).copy()
+    R, C = w.shape
+    assert m.shape == (R, C)
+    codes = np.zeros((R, C // 2), dtype=np.uint8)
+    scales = np.zeros((R, C // 32), dtype=np.uint8)
+    rc = _load().mxo_qema_quantize(_ptr(w), R, C, C, _ptr(m), C, float(beta), int(bool(hadamard)), _ptr(codes),
+                                   _ptr(scales))
+    if rc != 0:
+        raise ValueError("oracle qema_quantize rejected its arguments")
+    return m, (codes, scales, None)

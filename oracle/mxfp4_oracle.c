@@ -233,13 +233,23 @@ void mxo_fwht32(float x[32])
  * tensor_scale: one float (NV only).
  * Returns 0, or -1 on an invalid argument. */
 
+/* Contraction row i of the operand: bf16 input x, or binary32 input xf when
+ * x is NULL (used by the EMA quantizer below). */
+static void load_row_any(const uint16_t *x, const float *xf, int64_t ldx, int axis,
+                         int64_t i, int64_t K, int hadamard, float *v)
+{
+    for (int64_t k = 0; k < K; k++) {
+        const int64_t at = axis == 1 ? i * ldx + k : k * ldx + i;
+        v[k] = x ? bf16_to_f32(x[at]) : xf[at];
+    }
+    if (hadamard)
+        for (int64_t k0 = 0; k0 < K; k0 += 32) mxo_fwht32(v + k0);
+}
+
 static void load_contraction_row(const uint16_t *x, int64_t ldx, int axis,
                                  int64_t i, int64_t K, int hadamard, float *v)
 {
-    for (int64_t k = 0; k < K; k++)
-        v[k] = bf16_to_f32(axis == 1 ? x[i * ldx + k] : x[k * ldx + i]);
-    if (hadamard)
-        for (int64_t k0 = 0; k0 < K; k0 += 32) mxo_fwht32(v + k0);
+    load_row_any(x, NULL, ldx, axis, i, K, hadamard, v);
 }
 
 /* NVFP4 per-tensor scale.  READING: s_t = RN_f32(amax_t / (6 * 448)) so the
@@ -258,11 +268,11 @@ float mxo_nv_tensor_scale(float amax_t)
 /* l0: stream index of the operand's element (0, 0); 0 for a whole tensor
  * (mxo_quantize), row0 * K for rows row0.. of a larger MXFP4 tensor
  * quantized along axis 1 (mxo_quantize_rows_at). */
-static int quantize_impl(const uint16_t *x, int64_t R, int64_t C, int64_t ldx,
+static int quantize_impl(const uint16_t *x, const float *xf, int64_t R, int64_t C, int64_t ldx,
                          int fmt, int rounding, int hadamard, int axis, uint64_t seed,
                          uint64_t l0, uint8_t *codes, uint8_t *scales, float *tensor_scale)
 {
-    if (!x || !codes || !scales || R < 0 || C < 0 || ldx < C) return -1;
+    if ((!x && !xf) || !codes || !scales || R < 0 || C < 0 || ldx < C) return -1;
     if (fmt != FMT_MX && fmt != FMT_NV) return -1;
     if (rounding != RND_RTN && rounding != RND_SR) return -1;
     if (axis != 0 && axis != 1) return -1;
@@ -286,7 +296,7 @@ static int quantize_impl(const uint16_t *x, int64_t R, int64_t C, int64_t ldx,
             float local = 0.0f;
             #pragma omp for
             for (int64_t i = 0; i < rows; i++) {
-                load_contraction_row(x, ldx, axis, i, K, hadamard, v);
+                load_row_any(x, xf, ldx, axis, i, K, hadamard, v);
                 for (int64_t k = 0; k < K; k++) {
                     float a = fabsf(v[k]);
                     if (isfinite(a) && a > local) local = a;
@@ -305,7 +315,7 @@ static int quantize_impl(const uint16_t *x, int64_t R, int64_t C, int64_t ldx,
         float *v = (float *)malloc(sizeof(float) * K);
         #pragma omp for
         for (int64_t i = 0; i < rows; i++) {
-            load_contraction_row(x, ldx, axis, i, K, hadamard, v);
+            load_row_any(x, xf, ldx, axis, i, K, hadamard, v);
             for (int64_t b = 0; b < K / bs; b++) {
                 const float *blk = v + b * bs;
                 /* block absmax; a non-finite entry makes the block NaN */
@@ -370,7 +380,17 @@ int mxo_quantize(const uint16_t *x, int64_t R, int64_t C, int64_t ldx,
                  int fmt, int rounding, int hadamard, int axis, uint64_t seed,
                  uint8_t *codes, uint8_t *scales, float *tensor_scale)
 {
-    return quantize_impl(x, R, C, ldx, fmt, rounding, hadamard, axis, seed, 0, codes, scales, tensor_scale);
+    return quantize_impl(x, NULL, R, C, ldx, fmt, rounding, hadamard, axis, seed, 0, codes, scales, tensor_scale);
+}
+
+/* The same quantizer on a binary32 input (the values are used as they are;
+ * for bf16-representable values it equals mxo_quantize bit for bit). */
+int mxo_quantize_f32(const float *x, int64_t R, int64_t C, int64_t ldx,
+                     int fmt, int rounding, int hadamard, int axis, uint64_t seed,
+                     uint8_t *codes, uint8_t *scales, float *tensor_scale)
+{
+    if (!x) return -1;
+    return quantize_impl(NULL, x, R, C, ldx, fmt, rounding, hadamard, axis, seed, 0, codes, scales, tensor_scale);
 }
 
 /* Rows row0 .. row0 + R - 1 of a larger tensor, MXFP4 along axis 1: every
@@ -380,7 +400,7 @@ int mxo_quantize_rows_at(const uint16_t *x, int64_t R, int64_t C, int64_t ldx, i
                          uint64_t seed, int64_t row0, uint8_t *codes, uint8_t *scales)
 {
     if (row0 < 0) return -1;
-    return quantize_impl(x, R, C, ldx, FMT_MX, rounding, hadamard, 1, seed, (uint64_t)row0 * (uint64_t)C,
+    return quantize_impl(x, NULL, R, C, ldx, FMT_MX, rounding, hadamard, 1, seed, (uint64_t)row0 * (uint64_t)C,
                          codes, scales, NULL);
 }
 
@@ -878,4 +898,34 @@ int mxo_mse_tensor_step(const uint16_t *x, int64_t R, int64_t C, int64_t ldx, in
     *st_out = ls_tensor_scale(Y, rows, K, codes, scales, st_prev);
     free(Y);
     return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Q-EMA weight quantizer [TJ abstract: Q-EMA is named among the methods */
+/* that reduce weight oscillation in MXFP4 training; the page gives no   */
+/* rule].  PARITY UNPINNED as to the method: the rule below is this      */
+/* build's reading, pinned only for its own arithmetic.                  */
+/* READING: the quantized weights come from an exponential moving        */
+/* average m of the latent weights w instead of w itself.  One call:     */
+/*   m <- RN(RN(beta * m) + RN(c * w)),  c = RN_f32(1 - beta),           */
+/* in binary32, w the bf16 latent weights [R, C] widened exactly, m the  */
+/* binary32 state [R, C] (updated in place, leading dimension lde), then */
+/* the updated m is quantized to MXFP4 round-to-nearest along its rows   */
+/* (the contraction axis of W in X W^T), with the block Hadamard first   */
+/* when hadamard = 1, exactly as mxo_quantize_f32 quantizes it.          */
+/* ------------------------------------------------------------------ */
+int mxo_qema_quantize(const uint16_t *w, int64_t R, int64_t C, int64_t ldw, float *ema, int64_t lde,
+                      float beta, int hadamard, uint8_t *codes, uint8_t *scales)
+{
+    if (!w || !ema || !codes || !scales || R < 0 || C < 0 || ldw < C || lde < C) return -1;
+    if (!(beta >= 0.0f && beta <= 1.0f) || C % 32 != 0) return -1;
+    const float c = 1.0f - beta;
+    #pragma omp parallel for
+    for (int64_t i = 0; i < R; i++)
+        for (int64_t k = 0; k < C; k++) {
+            float a = beta * ema[i * lde + k];
+            float b = c * bf16_to_f32(w[i * ldw + k]);
+            ema[i * lde + k] = a + b;
+        }
+    return quantize_impl(NULL, ema, R, C, lde, FMT_MX, RND_RTN, hadamard, 1, 0, 0, codes, scales, NULL);
 }
