@@ -303,6 +303,29 @@ mxfp4_status mxfp4_quantize_noise(const uint16_t *x, int64_t R, int64_t C, int64
  * device access. */
 mxfp4_status mxfp4_noise_ratio(const double *stats, double *ratio, int *below_threshold);
 
+/* Q-EMA weight quantization ("Oscillation-Reduced MXFP4 Training for Vision
+ * Transformers", abstract, names Q-EMA among the methods that reduce weight
+ * oscillation in MXFP4 training; the page gives no rule).  As read here: the
+ * forward pass quantizes an exponential moving average of the latent weights
+ * instead of the weights themselves, and this call fuses the average's update
+ * with the quantization in one pass over memory:
+ *   ema <- RN(RN(beta * ema) + RN(c * w)),  c = RN(1 - beta)   (binary32),
+ *   out  = MXFP4 round-to-nearest of the new ema along its rows (the
+ *          contraction axis of W in X W^T; block Hadamard first when
+ *          hadamard = 1), exactly as mxfp4_quantize encodes an input with
+ *          those values.
+ * w:   device, bf16 latent weights [R, C], row-major, leading dimension
+ *      ldw >= C, 16-byte aligned, ldw a multiple of 8.
+ * ema: device, binary32 state [R, C] (read, then overwritten with the new
+ *      average), leading dimension lde >= C, 16-byte aligned, lde a multiple
+ *      of 4.  The caller initializes it (e.g. to the weights).
+ * beta in [0, 1] (INVALID_ARG otherwise).  C % 32 == 0 and R * C / 8 < 2^31
+ * (UNSUPPORTED_SHAPE otherwise).  out: an MXFP4 descriptor [R, C] with
+ * out->hadamard == hadamard (INVALID_ARG otherwise), codes 16-byte aligned.
+ * No workspace. */
+mxfp4_status mxfp4_qema_quantize(const uint16_t *w, int64_t R, int64_t C, int64_t ldw, float *ema, int64_t lde,
+                                 float beta, int hadamard, mxfp4_tensor *out, hipStream_t stream);
+
 /* A static, human-readable description of a status code. */
 const char *mxfp4_status_string(int status);
 

@@ -56,6 +56,8 @@ def _load_library() -> ctypes.CDLL:
     lib.mxfp4_quantize.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, u64, P(MxTensorStruct), vp, sz, vp]
     lib.mxfp4_quantize_noalloc.restype = i32
     lib.mxfp4_quantize_noalloc.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, u64, P(MxTensorStruct), vp]
+    lib.mxfp4_qema_quantize.restype = i32
+    lib.mxfp4_qema_quantize.argtypes = [vp, i64, i64, i64, vp, i64, ctypes.c_float, i32, P(MxTensorStruct), vp]
     lib.mxfp4_dequantize.restype = i32
     lib.mxfp4_dequantize.argtypes = [P(MxTensorStruct), vp, i64, vp]
     lib.mxfp4_gemm_workspace_bytes.restype = i32
@@ -241,6 +243,26 @@ def mxfp4_quantize_noalloc(x: torch.Tensor, out: QTensor, fmt: str = "mx", round
     st = out.as_struct()
     _check(lib.mxfp4_quantize_noalloc(_ptr(x), R, C, x.stride(0), FMT[fmt], ROUNDING[rounding], int(bool(hadamard)),
                                       int(axis), int(seed) & (2 ** 64 - 1), ctypes.byref(st), _stream(x.device)))
+    return out
+
+
+def mxfp4_qema_quantize(w: torch.Tensor, ema: torch.Tensor, beta: float, hadamard: bool = False,
+                        out: Optional[QTensor] = None) -> QTensor:
+    """Q-EMA step: ema <- beta ema + (1 - beta) w (binary32, updated in place),
+    then the MXFP4 round-to-nearest quantization of the new ema along its rows
+    (block Hadamard first if asked), in one pass."""
+    if w.dtype != torch.bfloat16 or w.dim() != 2 or not w.is_cuda or w.stride(1) != 1:
+        raise ValueError("w must be a 2-D bfloat16 CUDA/HIP tensor with unit stride along its last dimension")
+    R, C = w.shape
+    if ema.dtype != torch.float32 or tuple(ema.shape) != (R, C) or ema.stride(1) != 1 or ema.device != w.device:
+        raise ValueError("ema must be a float32 tensor of w's shape on w's device, unit stride along its last dimension")
+    if out is None:
+        out = empty_qtensor("mx", R, C, hadamard, w.device)
+    if _check_operands(out) != w.device or (out.fmt, out.rows, out.k) != ("mx", R, C):
+        raise ValueError("out must be an MXFP4 tensor [R, C] on w's device")
+    st = out.as_struct()
+    _check(lib.mxfp4_qema_quantize(_ptr(w), R, C, max(w.stride(0), C), _ptr(ema), max(ema.stride(0), C), float(beta),
+                                   int(bool(hadamard)), ctypes.byref(st), _stream(w.device)))
     return out
 
 
@@ -443,7 +465,7 @@ gemm = mxfp4_gemm
 quantize_gemm = mxfp4_quantize_gemm
 
 __all__ = ["QTensor", "MxFp4Error", "mxfp4_tensor_bytes", "mxfp4_quantize_workspace_bytes", "mxfp4_quantize",
-           "mxfp4_quantize_noalloc",
+           "mxfp4_quantize_noalloc", "mxfp4_qema_quantize",
            "mxfp4_dequantize", "mxfp4_gemm_workspace_bytes", "mxfp4_gemm", "mxfp4_gemm_bf16", "mxfp4_status_string",
            "mxfp4_quantize_gemm_workspace_bytes", "mxfp4_quantize_gemm",
            "mxfp4_quantization_noise_workspace_bytes", "mxfp4_quantization_noise", "gradient_noise_ratio",

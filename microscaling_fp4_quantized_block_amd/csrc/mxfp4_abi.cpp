@@ -39,6 +39,22 @@ const char* mxfp4_status_string(int status) {
   }
 }
 
+mxfp4_status mxfp4_qema_quantize(const uint16_t* w, int64_t R, int64_t C, int64_t ldw, float* ema, int64_t lde,
+                                 float beta, int hadamard, mxfp4_tensor* out, hipStream_t stream) {
+  if (!out || (hadamard != 0 && hadamard != 1) || !(beta >= 0.0f && beta <= 1.0f)) return MXFP4_ERR_INVALID_ARG;
+  if (R < 0 || C < 0 || ldw < C || lde < C || ldw < 1 || lde < 1) return MXFP4_ERR_INVALID_ARG;
+  if (C % 32 != 0) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  if (R > 0 && C / 8 > (((int64_t)1 << 31) - 1) / R) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  if (out->fmt != MXFP4_FMT_MX || out->rows != R || out->k != C || out->hadamard != hadamard)
+    return MXFP4_ERR_INVALID_ARG;
+  if (R == 0 || C == 0) return MXFP4_OK;
+  if (!w || !ema || !out->codes || !out->scales) return MXFP4_ERR_INVALID_ARG;
+  if (!aligned(w, 16) || ldw % 8 != 0 || !aligned(ema, 16) || lde % 4 != 0 || !aligned(out->codes, 16))
+    return MXFP4_ERR_INVALID_ARG;
+  hipError_t e = mxfp4::launch_qema(w, R, C, ldw, ema, lde, beta, hadamard, out->codes, out->scales, stream);
+  return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
+}
+
 mxfp4_status mxfp4_noise_ratio(const double* stats, double* ratio, int* below_threshold) {
   if (!stats || !ratio || !below_threshold) return MXFP4_ERR_INVALID_ARG;
   const double signal = stats[0], noise = stats[1];

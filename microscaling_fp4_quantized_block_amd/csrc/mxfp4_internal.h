@@ -77,6 +77,12 @@ hipError_t launch_noise(const uint16_t* x, int64_t ldx, int axis, int fmt, int h
                         const uint8_t* codes, const uint8_t* scales, const float* ts, double* stats,
                         double* partials, hipStream_t stream);
 
+// Q-EMA weight quantizer (quantize.hip): ema <- RN(RN(beta ema) + RN((1 - beta) w)),
+// then MXFP4 round-to-nearest of the new ema along its rows.  Needs C % 32 == 0,
+// R * C / 8 < 2^31, w and ema rows 16-byte aligned.
+hipError_t launch_qema(const uint16_t* w, int64_t R, int64_t C, int64_t ldw, float* m, int64_t lde, float beta,
+                       int hadamard, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
 // The static device scratch of mxfp4_quantize_noalloc (noalloc.hip): its size,
 // and the current device's address of it (looked up once per device).
 size_t noalloc_scratch_bytes();

@@ -741,6 +741,121 @@ void launch_tensor_scale(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, i
   hipLaunchKernelGGL(amax_finalize_kernel, dim3(1), dim3(1024), 0, s, partials, nparts, tensor_scale);
 }
 
+// ---------------------------------------------------------------------------
+// Q-EMA weight quantizer ("Oscillation-Reduced MXFP4 Training for Vision
+// Transformers", abstract, names Q-EMA without giving its rule; the reading
+// here: the forward pass quantizes an exponential moving average of the latent
+// weights).  One pass: m <- RN(RN(beta m) + RN(c w)) with c = RN(1 - beta) in
+// binary32 (no fused multiply-add), the new m stored back, then MXFP4
+// round-to-nearest of the new m along its rows (block Hadamard first with HAD).
+// Lane = 8 consecutive elements of a row: a 16-byte load of w, two of m and
+// two 16-byte stores of the new m; a 32-block is a quad of lanes, as in the
+// row quantizer.  HBM bytes per element: 2 (w) + 4 + 4 (m in, out) + 0.5 + 1/32.
+// ---------------------------------------------------------------------------
+struct QemaArgs {
+  const uint16_t* w;
+  int64_t ldw;
+  float* m;
+  int64_t lde;
+  FastDiv cpr;            // chunks (8 elements) per row
+  uint32_t total;         // chunks in the tensor (< 2^31)
+  float beta, c;
+  uint8_t* codes;
+  uint8_t* scales;
+};
+
+template <bool HAD, bool PADDED>
+__global__ void __launch_bounds__(256) qema_kernel(QemaArgs a) {
+  constexpr int U = 2;
+  const uint32_t p = threadIdx.x & 3u;
+  const uint32_t base = blockIdx.x * (uint32_t)(256 * U) + threadIdx.x;
+  uint32_t wv[U][4];
+  f32x4 mv[U][2];
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    const uint32_t t = base + u * 256u;
+    if (t >= a.total) continue;
+    const uint16_t* ws;
+    float* ms;
+    if (PADDED) {
+      const uint32_t i = fastdiv(t, a.cpr), q = t - i * a.cpr.d;
+      ws = a.w + (int64_t)i * a.ldw + (int64_t)q * 8;
+      ms = a.m + (int64_t)i * a.lde + (int64_t)q * 8;
+    } else {
+      ws = a.w + (uint64_t)t * 8;
+      ms = a.m + (uint64_t)t * 8;
+    }
+    const u32v4 v = __builtin_nontemporal_load((const u32v4*)ws);
+    wv[u][0] = v[0]; wv[u][1] = v[1]; wv[u][2] = v[2]; wv[u][3] = v[3];
+    mv[u][0] = __builtin_nontemporal_load((const f32x4*)ms);
+    mv[u][1] = __builtin_nontemporal_load((const f32x4*)(ms + 4));
+  }
+#pragma unroll
+  for (int u = 0; u < U; u++) {
+    const uint32_t t = base + u * 256u;
+    if (t >= a.total) break;     // whole blocks leave together (total is a multiple of 4)
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const float w0 = bf16lo(wv[u][j]), w1 = bf16hi(wv[u][j]);
+      const float m0 = mv[u][j >> 1][2 * (j & 1)], m1 = mv[u][j >> 1][2 * (j & 1) + 1];
+      y[2 * j] = a.beta * m0 + a.c * w0;          // built without FP contraction: three roundings
+      y[2 * j + 1] = a.beta * m1 + a.c * w1;
+    }
+    float* ms;
+    if (PADDED) {
+      const uint32_t i = fastdiv(t, a.cpr), q = t - i * a.cpr.d;
+      ms = a.m + (int64_t)i * a.lde + (int64_t)q * 8;
+    } else {
+      ms = a.m + (uint64_t)t * 8;
+    }
+    __builtin_nontemporal_store((f32x4){y[0], y[1], y[2], y[3]}, (f32x4*)ms);
+    __builtin_nontemporal_store((f32x4){y[4], y[5], y[6], y[7]}, (f32x4*)(ms + 4));
+    if (HAD) fwht32_quad(y, p);
+    uint32_t am = 0;
+#pragma unroll
+    for (int j = 0; j < 8; j++) am = max(am, __float_as_uint(y[j]) & 0x7FFFFFFFu);
+    am = max(am, dpp_xor1(am));
+    am = max(am, dpp_xor2(am));
+    uint32_t packed = 0, byte = 0xFFu;
+    if (am < 0x7F800000u) {
+      byte = mx_scale_byte_from_f32bits(am);
+      const float sc = e8m0_as_cvt_scale(byte);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[0], y[1], sc, 0);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[2], y[3], sc, 1);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[4], y[5], sc, 2);
+      packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[6], y[7], sc, 3);
+    }
+    __builtin_nontemporal_store(packed, (uint32_t*)(a.codes + (uint64_t)t * 4));
+    if (p == 0) __builtin_nontemporal_store((uint8_t)byte, a.scales + t / 4);
+  }
+}
+
+hipError_t launch_qema(const uint16_t* w, int64_t R, int64_t C, int64_t ldw, float* m, int64_t lde, float beta,
+                       int hadamard, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  QemaArgs a;
+  a.w = w;
+  a.ldw = ldw;
+  a.m = m;
+  a.lde = lde;
+  a.cpr = make_fastdiv((uint32_t)(C / 8));
+  a.total = (uint32_t)(R * (C / 8));
+  a.beta = beta;
+  a.c = 1.0f - beta;
+  a.codes = codes;
+  a.scales = scales;
+  const bool padded = ldw != C || lde != C;
+  const unsigned grid = (unsigned)((a.total + 511) / 512);
+  if (hadamard) {
+    if (padded) hipLaunchKernelGGL((qema_kernel<true, true>), dim3(grid), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((qema_kernel<true, false>), dim3(grid), dim3(256), 0, stream, a);
+  } else {
+    if (padded) hipLaunchKernelGGL((qema_kernel<false, true>), dim3(grid), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((qema_kernel<false, false>), dim3(grid), dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
 size_t quantize_workspace_bytes(int fmt, int64_t R, int64_t C) {
   if (fmt != FMT_NV) return 0;
   // partials written by launch_tensor_scale's unrotated scan, range by range

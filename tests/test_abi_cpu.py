@@ -395,3 +395,26 @@ def test_binding_rejects_outputs_the_kernels_would_overrun(mx):
         mx._check_operands(nv)
     with pytest.raises(ValueError, match="workspace"):
         mx._nbytes(torch.empty(16, dtype=torch.uint8), dev)
+
+
+def test_qema_rejects_bad_arguments(mx):
+    """mxfp4_qema_quantize: argument errors before any launch."""
+    out = mx.MxTensorStruct(0, 0, 64, 256, FAKE, FAKE, None)
+    f = mx.lib.mxfp4_qema_quantize
+    ok = dict(w=FAKE, R=64, C=256, ldw=256, ema=FAKE, lde=256, beta=0.9, had=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        o = kw.get("out", out)
+        return f(ctypes.c_void_p(a["w"]) if a["w"] else None, a["R"], a["C"], a["ldw"],
+                 ctypes.c_void_p(a["ema"]) if a["ema"] else None, a["lde"], a["beta"], a["had"], ctypes.byref(o), None)
+
+    assert call(beta=1.5) == INVALID
+    assert call(beta=float("nan")) == INVALID
+    assert call(C=250, ldw=256, lde=256) == SHAPE
+    assert call(ldw=200) == INVALID
+    assert call(w=0) == INVALID
+    assert call(ema=FAKE + 4) == INVALID
+    assert call(ldw=260) == INVALID                       # not a multiple of 8
+    assert call(had=1) == INVALID                          # out->hadamard differs
+    assert call(out=mx.MxTensorStruct(1, 0, 64, 256, FAKE, FAKE, FAKE)) == INVALID   # NVFP4 out
