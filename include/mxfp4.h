@@ -175,6 +175,34 @@ mxfp4_status mxfp4_gemm(const mxfp4_tensor *A, const mxfp4_tensor *B, float *C, 
 mxfp4_status mxfp4_gemm_bf16(const mxfp4_tensor *A, const mxfp4_tensor *B, uint16_t *C, int64_t ldc,
                              void *workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Workspace needed by mxfp4_gemm_quantize for these operands and output: 0
+ * when the quantization is fused into the GEMM's epilogue (MXFP4 operands and
+ * no K split), else room for the bf16 C (M * N * 2 bytes, padded to 16) and
+ * the GEMM's own workspace.  Argument errors as for mxfp4_gemm_quantize. */
+mxfp4_status mxfp4_gemm_quantize_workspace_bytes(const mxfp4_tensor *A, const mxfp4_tensor *B, int hadamard,
+                                                 const mxfp4_tensor *out, size_t *bytes);
+
+/* GEMM whose output is quantized for the next layer: the output epilogue of
+ * the fused pipeline of "Bridging the Gap Between Promise and Performance for
+ * Microscaling FP4 Quantization", abstract (quantization costs fused into the
+ * FP4 GEMM kernels; the next layer's activations rotated and quantized on the
+ * fly).  out = mxfp4_quantize(C, MXFP4, RTN, hadamard, axis 1) of the bf16 C
+ * that mxfp4_gemm_bf16 writes for the same operands -- bit for bit: C = A B^T
+ * in FP32, rounded to nearest-even bf16, then each aligned block of 32 along
+ * a row of C (block Hadamard first when hadamard = 1) gets its E8M0 byte and
+ * round-to-nearest codes.  The next layer's GEMM contracts over C's columns,
+ * so out is already in its contraction-major layout.  For MXFP4 operands
+ * without a K split, the GEMM kernel's epilogue encodes C in registers and
+ * writes only codes and scales (0.53 bytes per output instead of 4);
+ * otherwise (NVFP4 operands, split contractions) the bf16 C goes through the
+ * workspace.  Operands as for mxfp4_gemm; N = B->rows must be a multiple of
+ * 32 (UNSUPPORTED_SHAPE).  out: MXFP4 descriptor [A->rows, B->rows] with
+ * out->hadamard == hadamard, codes 16-byte aligned (INVALID_ARG otherwise).
+ * workspace: device, 16-byte aligned, at least
+ * mxfp4_gemm_quantize_workspace_bytes (NULL if that is 0). */
+mxfp4_status mxfp4_gemm_quantize(const mxfp4_tensor *A, const mxfp4_tensor *B, int hadamard, mxfp4_tensor *out,
+                                 void *workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Workspace needed by mxfp4_quantize_gemm for activations [M, K] against B:
  * the split-K partial sums when the quantization is fused into the GEMM,
  * else room for the quantized activations (codes, then scales, each padded

@@ -66,6 +66,11 @@ def _load_library() -> ctypes.CDLL:
     lib.mxfp4_gemm.argtypes = [P(MxTensorStruct), P(MxTensorStruct), vp, i64, vp, sz, vp]
     lib.mxfp4_gemm_bf16.restype = i32
     lib.mxfp4_gemm_bf16.argtypes = [P(MxTensorStruct), P(MxTensorStruct), vp, i64, vp, sz, vp]
+    lib.mxfp4_gemm_quantize_workspace_bytes.restype = i32
+    lib.mxfp4_gemm_quantize_workspace_bytes.argtypes = [P(MxTensorStruct), P(MxTensorStruct), i32, P(MxTensorStruct),
+                                                        P(sz)]
+    lib.mxfp4_gemm_quantize.restype = i32
+    lib.mxfp4_gemm_quantize.argtypes = [P(MxTensorStruct), P(MxTensorStruct), i32, P(MxTensorStruct), vp, sz, vp]
     lib.mxfp4_quantize_gemm_workspace_bytes.restype = i32
     lib.mxfp4_quantize_gemm_workspace_bytes.argtypes = [i64, i64, i32, P(MxTensorStruct), P(sz)]
     lib.mxfp4_quantize_gemm.restype = i32
@@ -317,6 +322,34 @@ def mxfp4_gemm_bf16(qa: QTensor, qb: QTensor, out: Optional[torch.Tensor] = None
     return out
 
 
+def mxfp4_gemm_quantize_workspace_bytes(qa: QTensor, qb: QTensor, hadamard: bool, out: QTensor) -> int:
+    b = ctypes.c_size_t()
+    sa, sb, so = qa.as_struct(), qb.as_struct(), out.as_struct()
+    _check(lib.mxfp4_gemm_quantize_workspace_bytes(ctypes.byref(sa), ctypes.byref(sb), int(bool(hadamard)),
+                                                   ctypes.byref(so), ctypes.byref(b)))
+    return b.value
+
+
+def mxfp4_gemm_quantize(qa: QTensor, qb: QTensor, hadamard: bool = False, out: Optional[QTensor] = None,
+                        workspace: Optional[torch.Tensor] = None) -> QTensor:
+    """Q(bf16(A B^T)): the GEMM with its output quantized to MXFP4 (round to
+    nearest, along rows, block Hadamard first if asked) for the next layer --
+    the same bits as mxfp4_quantize(mxfp4_gemm_bf16(qa, qb), "mx", "rtn",
+    hadamard)."""
+    dev = _check_operands(qa, qb)
+    if out is None:
+        out = empty_qtensor("mx", qa.rows, qb.rows, hadamard, dev)
+    if _check_operands(out) != dev:
+        raise ValueError("out must live on the operands' device")
+    ws_bytes = mxfp4_gemm_quantize_workspace_bytes(qa, qb, hadamard, out)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    sa, sb, so = qa.as_struct(), qb.as_struct(), out.as_struct()
+    _check(lib.mxfp4_gemm_quantize(ctypes.byref(sa), ctypes.byref(sb), int(bool(hadamard)), ctypes.byref(so),
+                                   _ptr(workspace), _nbytes(workspace, dev), _stream(dev)))
+    return out
+
+
 def mxfp4_quantize_gemm_workspace_bytes(M: int, K: int, hadamard: bool, qb: QTensor) -> int:
     b = ctypes.c_size_t()
     sb = qb.as_struct()
@@ -465,7 +498,8 @@ gemm = mxfp4_gemm
 quantize_gemm = mxfp4_quantize_gemm
 
 __all__ = ["QTensor", "MxFp4Error", "mxfp4_tensor_bytes", "mxfp4_quantize_workspace_bytes", "mxfp4_quantize",
-           "mxfp4_quantize_noalloc", "mxfp4_qema_quantize",
+           "mxfp4_quantize_noalloc", "mxfp4_qema_quantize", "mxfp4_gemm_quantize",
+           "mxfp4_gemm_quantize_workspace_bytes",
            "mxfp4_dequantize", "mxfp4_gemm_workspace_bytes", "mxfp4_gemm", "mxfp4_gemm_bf16", "mxfp4_status_string",
            "mxfp4_quantize_gemm_workspace_bytes", "mxfp4_quantize_gemm",
            "mxfp4_quantization_noise_workspace_bytes", "mxfp4_quantization_noise", "gradient_noise_ratio",

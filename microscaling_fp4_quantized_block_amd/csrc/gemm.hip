@@ -84,6 +84,11 @@ struct GemmArgs {
   const uint16_t* x;
   int64_t ldx;
   int x_vec;                // x 16-byte aligned and ldx a multiple of 8: 16-byte loads
+  // quantized output (OUT_MXQ): C rounded to bf16, then MXFP4 round-to-nearest
+  // along its rows (block Hadamard first when qhad): codes [M, N/2], scales [M, N/32]
+  uint8_t* qcodes;
+  uint8_t* qscales;
+  int qhad;
 };
 
 // Tile order: consecutive workgroup ids go to consecutive XCDs, so gather
@@ -249,7 +254,9 @@ __device__ __forceinline__ void block_barrier() {
 //   OUT_BF16  C rounded to bf16 (round to nearest even, hardware convert).
 // The choice is a kernel template parameter: two epilogues in one kernel cost
 // the wide kernel ~35 %.
-constexpr int OUT_F32 = 0, OUT_PART = 1, OUT_BF16 = 2;
+//   OUT_MXQ   C rounded to bf16 and quantized to MXFP4 for the next layer
+//             (quantize_tile below); nothing else is written.
+constexpr int OUT_F32 = 0, OUT_PART = 1, OUT_BF16 = 2, OUT_MXQ = 3;
 
 //
 // bf16 whole blocks: the two column blocks tn, tn + 1 of a row are paired so
@@ -319,6 +326,79 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, float* Cz, int64_t
         }
       }
     }
+  }
+}
+
+// Quantizing epilogue (OUT_MXQ): the wave's TM x TN grid of 32x32 FP32
+// accumulators with top-left output (mb, nb) becomes MXFP4 codes and E8M0
+// bytes of C rounded to bf16 -- exactly what mxfp4_quantize (round-to-nearest,
+// along rows, block Hadamard first when p.qhad) writes for the bf16 C of
+// mxfp4_gemm_bf16.  A 32-block of a C row lies in one accumulator register
+// across 32 lanes; the wave turns it around through its own slice of LDS, one
+// 32-row block row at a time: the bf16 values go in as 4-byte column pairs (the
+// pairing of the bf16 epilogue), then each lane reads whole 64-byte blocks
+// (row l % 32) and encodes them in its registers with the quantizer's block
+// encoder, storing 16 bytes of codes and one scale byte per block.  Rows are
+// padded to 64 TN + 16 bytes so that 16 consecutive rows read conflict-free.
+// The caller has made every wave finish its main loop (LDS is free).
+template <int TM, int TN>
+__device__ __forceinline__ void quantize_tile(const GemmArgs& p, uint8_t* smem, int64_t mb, int64_t nb,
+                                              const v16f (&acc)[TM][TN]) {
+  static_assert(TN % 2 == 0, "column pairs");
+  constexpr int RB = 64 * TN + 16;                 // bytes per LDS row
+  const int l = threadIdx.x & 63, g = l >> 5, w = threadIdx.x >> 6;
+  uint8_t* slab = smem + w * 32 * RB;
+  const bool odd = l & 1;
+  const int64_t qrow = p.N / 2, srow = p.N / 32;
+#pragma unroll
+  for (int tm = 0; tm < TM; tm++) {
+    // C rows 32 tm .. + 31 of the wave, as bf16, into the slab (row r at r * RB)
+#pragma unroll
+    for (int v = 0; v < 16; v++) {
+      const int r = 8 * (v >> 2) + 4 * g + (v & 3);
+#pragma unroll
+      for (int tn = 0; tn < TN; tn += 2) {
+        const float x = acc[tm][tn][v], y = acc[tm][tn + 1][v];
+        const float got = dpp_swap_pairs(odd ? x : y);
+        const float lo = odd ? got : x, hi = odd ? y : got;
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        const int col = tn * 32 + (l & 30) + (odd ? 32 : 0);
+        *(bf16x2_t*)(slab + r * RB + 2 * col) = (bf16x2_t){(__bf16)lo, (__bf16)hi};
+      }
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0): the slab is written
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    const int r = l & 31;
+    const int64_t row = mb + 32 * tm + r;
+#pragma unroll
+    for (int j = 0; j < TN / 2; j++) {
+      const int b = g + 2 * j;                      // block (32 columns) of the wave's row
+      const uint8_t* src = slab + r * RB + 64 * b;
+      float y[32];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const u32v4 v = *(const u32v4*)(src + 16 * q);
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          y[8 * q + 2 * t] = __uint_as_float(v[t] << 16);
+          y[8 * q + 2 * t + 1] = __uint_as_float(v[t] & 0xFFFF0000u);
+        }
+      }
+      const int64_t col = nb + 32 * b;
+      if (row < p.M && col < p.N) {
+        if (p.qhad) fwht32_inlane(y);
+        uint32_t cw[4];
+        const uint32_t byte = mx_rtn_block32(y, cw);
+        __builtin_nontemporal_store((u32v4){cw[0], cw[1], cw[2], cw[3]}, (u32v4*)(p.qcodes + row * qrow + col / 2));
+        __builtin_nontemporal_store((uint8_t)byte, p.qscales + row * srow + col / 32);
+      }
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);            // the slab is read before the next block row overwrites it
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
   }
 }
 
@@ -744,7 +824,12 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& p, uint8_t* smem, int64_
     }
     wait_cnt<0, 0>();   // nothing may still write LDS when the workgroup exits
   }
-  store_tile<TM, TN, false, OUT>(p, Cz, m0 + wm * (32 * TM), n0 + wn * (32 * TN), acc);
+  if constexpr (OUT == OUT_MXQ) {
+    block_barrier();   // every wave is past its main loop: LDS is free for the epilogue
+    quantize_tile<TM, TN>(p, smem, m0 + wm * (32 * TM), n0 + wn * (32 * TN), acc);
+  } else {
+    store_tile<TM, TN, false, OUT>(p, Cz, m0 + wm * (32 * TM), n0 + wn * (32 * TN), acc);
+  }
 }
 
 // Work items.  Workgroups are dispatched in id order to whichever compute
@@ -1041,7 +1126,7 @@ template <int OUT>
 static void launch_gemm_kernel(bool nv, const GemmArgs& p, const GemmPlan& plan, int fused_had, dim3 grid,
                                dim3 ngrid, hipStream_t stream) {
   if (nv) {
-    hipLaunchKernelGGL(gemm_nv_kernel<OUT>, grid, dim3(256), 0, stream, p);
+    if constexpr (OUT != OUT_MXQ) hipLaunchKernelGGL(gemm_nv_kernel<OUT>, grid, dim3(256), 0, stream, p);
   } else if (plan.narrow_tm && fused_had >= 0) {
     // fused plans have 32-row tiles (fused_plan_ok)
     if (fused_had) hipLaunchKernelGGL((gemm_mx_fused_kernel<1, true, OUT>), ngrid, dim3(256), 0, stream, p);
@@ -1083,6 +1168,7 @@ static hipError_t launch_gemm_common(bool nv, GemmArgs p, void* C, int64_t ldc, 
   dim3 grid((unsigned)(tiles + p.rem), (unsigned)plan.splits);
   dim3 ngrid((unsigned)((p.N + 255) / 256), (unsigned)plan.splits);
   if (plan.splits > 1) launch_gemm_kernel<OUT_PART>(nv, p, plan, fused_had, grid, ngrid, stream);
+  else if (p.qcodes) launch_gemm_kernel<OUT_MXQ>(nv, p, plan, fused_had, grid, ngrid, stream);
   else if (c_bf16) launch_gemm_kernel<OUT_BF16>(nv, p, plan, fused_had, grid, ngrid, stream);
   else launch_gemm_kernel<OUT_F32>(nv, p, plan, fused_had, grid, ngrid, stream);
   if (plan.splits > 1) {
@@ -1123,6 +1209,19 @@ hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const
   p.a_ts = nullptr; p.b_ts = nullptr;
   p.M = M; p.N = N; p.K = K;
   return launch_gemm_common(false, p, C, ldc, c_bf16, workspace, plan, stream);
+}
+
+hipError_t launch_gemm_mx_quantize(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                                   const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, uint8_t* q_codes,
+                                   uint8_t* q_scales, int hadamard, const GemmPlan& plan, hipStream_t stream) {
+  GemmArgs p{};
+  p.a = a_codes; p.as = a_scales; p.b = b_codes; p.bs = b_scales;
+  p.a_ts = nullptr; p.b_ts = nullptr;
+  p.M = M; p.N = N; p.K = K;
+  p.qcodes = q_codes;
+  p.qscales = q_scales;
+  p.qhad = hadamard;
+  return launch_gemm_common(false, p, nullptr, N, 0, nullptr, plan, stream);
 }
 
 bool fused_plan_ok(const GemmPlan& plan) {

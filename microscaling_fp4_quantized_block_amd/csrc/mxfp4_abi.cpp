@@ -268,6 +268,68 @@ mxfp4_status mxfp4_gemm_bf16(const mxfp4_tensor* A, const mxfp4_tensor* B, uint1
   return gemm_impl(A, B, C, ldc, 1, workspace, ws_bytes, stream);
 }
 
+// GEMM with the output quantized for the next layer.  Fused into the GEMM's
+// epilogue for MXFP4 operands when the plan has no K split; otherwise the bf16
+// C goes through the workspace (mxfp4_gemm_bf16, then mxfp4_quantize).
+static mxfp4_status check_gemm_quantize(const mxfp4_tensor* A, const mxfp4_tensor* B, int hadamard,
+                                        const mxfp4_tensor* out) {
+  mxfp4_status s = check_gemm_operands(A, B);
+  if (s != MXFP4_OK) return s;
+  if (!out || (hadamard != 0 && hadamard != 1)) return MXFP4_ERR_INVALID_ARG;
+  if (B->rows % 32 != 0) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  if (out->fmt != MXFP4_FMT_MX || out->rows != A->rows || out->k != B->rows || out->hadamard != hadamard)
+    return MXFP4_ERR_INVALID_ARG;
+  if (A->rows > 0 && B->rows > kMaxElems / A->rows) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  return MXFP4_OK;
+}
+
+static size_t align16_bytes(size_t n) { return (n + 15) & ~(size_t)15; }
+
+static size_t gemm_quantize_ws(const mxfp4_tensor* A, const mxfp4_tensor* B, bool* fused) {
+  const mxfp4::GemmPlan pl = mxfp4::plan_gemm(A->fmt, A->rows, B->rows, A->k);
+  *fused = A->fmt == MXFP4_FMT_MX && pl.splits == 1;
+  if (*fused) return 0;
+  const size_t gemm_ws = pl.splits > 1 ? (size_t)pl.splits * (size_t)A->rows * (size_t)B->rows * sizeof(float) : 0;
+  return align16_bytes((size_t)A->rows * (size_t)B->rows * 2) + gemm_ws;
+}
+
+mxfp4_status mxfp4_gemm_quantize_workspace_bytes(const mxfp4_tensor* A, const mxfp4_tensor* B, int hadamard,
+                                                 const mxfp4_tensor* out, size_t* bytes) {
+  if (!bytes) return MXFP4_ERR_INVALID_ARG;
+  mxfp4_status s = check_gemm_quantize(A, B, hadamard, out);
+  if (s != MXFP4_OK) return s;
+  bool fused;
+  *bytes = gemm_quantize_ws(A, B, &fused);
+  return MXFP4_OK;
+}
+
+mxfp4_status mxfp4_gemm_quantize(const mxfp4_tensor* A, const mxfp4_tensor* B, int hadamard, mxfp4_tensor* out,
+                                 void* workspace, size_t ws_bytes, hipStream_t stream) {
+  mxfp4_status s = check_gemm_quantize(A, B, hadamard, out);
+  if (s != MXFP4_OK) return s;
+  const int64_t M = A->rows, N = B->rows, K = A->k;
+  if (M == 0 || N == 0) return MXFP4_OK;
+  if (!A->codes || !A->scales || !B->codes || !B->scales || !out->codes || !out->scales) return MXFP4_ERR_INVALID_ARG;
+  if (A->fmt == MXFP4_FMT_NV && (!A->tensor_scale || !B->tensor_scale)) return MXFP4_ERR_INVALID_ARG;
+  if (!aligned(A->codes, 16) || !aligned(B->codes, 16) || !aligned(A->scales, 4) || !aligned(B->scales, 4) ||
+      !aligned(out->codes, 16))
+    return MXFP4_ERR_INVALID_ARG;
+  bool fused;
+  const size_t need = gemm_quantize_ws(A, B, &fused);
+  if (need && (!workspace || ws_bytes < need || !aligned(workspace, 16))) return MXFP4_ERR_WORKSPACE;
+  if (fused) {
+    const mxfp4::GemmPlan pl = mxfp4::plan_gemm(A->fmt, M, N, K);
+    hipError_t e = mxfp4::launch_gemm_mx_quantize(A->codes, A->scales, B->codes, B->scales, M, N, K, out->codes,
+                                                  out->scales, hadamard, pl, stream);
+    return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
+  }
+  uint16_t* cb = (uint16_t*)workspace;
+  uint8_t* gws = (uint8_t*)workspace + align16_bytes((size_t)M * (size_t)N * 2);
+  s = gemm_impl(A, B, cb, N, 1, gws, ws_bytes - align16_bytes((size_t)M * (size_t)N * 2), stream);
+  if (s != MXFP4_OK) return s;
+  return mxfp4_quantize(cb, M, N, N, MXFP4_FMT_MX, MXFP4_RTN, hadamard, 1, 0, out, nullptr, 0, stream);
+}
+
 // Online activation quantization + GEMM: fused into the narrow GEMM when the
 // plan allows, else quantize into the workspace, then the GEMM.
 static mxfp4_status check_quantize_gemm(int64_t M, int64_t K, int hadamard, const mxfp4_tensor* B) {

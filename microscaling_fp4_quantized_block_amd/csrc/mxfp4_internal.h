@@ -37,6 +37,13 @@ hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const
                           const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* C, int64_t ldc,
                           int c_bf16, float* workspace, const GemmPlan& plan, hipStream_t stream);
 
+// MXFP4 GEMM whose epilogue quantizes C for the next layer: codes/scales of
+// Q_MX,RTN(bf16(A B^T)) along rows (block Hadamard first when hadamard); plans
+// without a K split only (splits == 1), N % 32 == 0.
+hipError_t launch_gemm_mx_quantize(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                                   const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, uint8_t* q_codes,
+                                   uint8_t* q_scales, int hadamard, const GemmPlan& plan, hipStream_t stream);
+
 // Fused activation quantization + MXFP4 GEMM (narrow plans with 32-row tiles,
 // M <= 32, whose splits hold at most 16 stages): A = Q_MX,RTN(x [M, K] bf16,
 // row stride ldx, block Hadamard when hadamard), C = A * B^T.

@@ -418,3 +418,23 @@ def test_qema_rejects_bad_arguments(mx):
     assert call(ldw=260) == INVALID                       # not a multiple of 8
     assert call(had=1) == INVALID                          # out->hadamard differs
     assert call(out=mx.MxTensorStruct(1, 0, 64, 256, FAKE, FAKE, FAKE)) == INVALID   # NVFP4 out
+
+
+def test_gemm_quantize_rejects_bad_arguments_and_sizes_its_workspace(mx):
+    a = desc(mx, 0, 0, 512, 1024)
+    b = desc(mx, 0, 0, 768, 1024)
+    out = desc(mx, 0, 0, 512, 768)
+    ws = ctypes.c_size_t()
+    f = mx.lib.mxfp4_gemm_quantize
+    fw = mx.lib.mxfp4_gemm_quantize_workspace_bytes
+    assert fw(ctypes.byref(a), ctypes.byref(b), 0, ctypes.byref(out), ctypes.byref(ws)) == OK and ws.value == 0
+    # a split contraction goes through a bf16 C in the workspace
+    a2, b2, o2 = desc(mx, 0, 0, 64, 8192), desc(mx, 0, 0, 96, 8192), desc(mx, 0, 0, 64, 96)
+    assert fw(ctypes.byref(a2), ctypes.byref(b2), 0, ctypes.byref(o2), ctypes.byref(ws)) == OK
+    assert ws.value >= 64 * 96 * 2
+    assert f(ctypes.byref(a2), ctypes.byref(b2), 0, ctypes.byref(o2), None, 0, None) == WORKSPACE
+    nb = desc(mx, 0, 0, 100, 1024)                       # N not a multiple of 32
+    assert f(ctypes.byref(a), ctypes.byref(nb), 0, ctypes.byref(desc(mx, 0, 0, 512, 100)), None, 0, None) == SHAPE
+    assert f(ctypes.byref(a), ctypes.byref(b), 1, ctypes.byref(out), None, 0, None) == INVALID   # out->hadamard
+    assert f(ctypes.byref(a), ctypes.byref(b), 0, ctypes.byref(desc(mx, 1, 0, 512, 768)), None, 0, None) == INVALID
+    assert f(ctypes.byref(a), ctypes.byref(desc(mx, 1, 0, 768, 1024)), 0, ctypes.byref(out), None, 0, None) == MISMATCH
