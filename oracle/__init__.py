@@ -87,6 +87,8 @@ def _load():
     lib.mxo_quantize_f32.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, u64, vp, vp, vp]
     lib.mxo_qema_quantize.restype = i32
     lib.mxo_qema_quantize.argtypes = [vp, i64, i64, i64, vp, i64, ctypes.c_float, i32, vp, vp]
+    lib.mxo_quantize_grid.restype = i32
+    lib.mxo_quantize_grid.argtypes = [vp, i64, i64, i64, i32, i32, ctypes.c_float, vp, vp]
     lib.mxo_noise_stats.restype = i32
     lib.mxo_noise_stats.argtypes = [vp, i64, i64, i64, i32, i32, i32, vp, vp, vp, vp]
     _lib = lib
@@ -341,3 +343,19 @@ def qema_quantize(w_bits: np.ndarray, ema: np.ndarray, beta: float, hadamard: bo
     if rc != 0:
         raise ValueError("oracle qema_quantize rejected its arguments")
     return m, (codes, scales, None)
+
+
+def quantize_grid(x_bits: np.ndarray, alpha: float, hadamard: bool = True, axis: int = 1):
+    """MXFP4 round-to-nearest with a fixed grid scale alpha: each block's E8M0
+    exponent chosen for RN(alpha * absmax) (reading of the digest of the
+    MR-GPTQ paper, step 1).  Returns (codes, scales, None)."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    R, C = x.shape
+    rows, K = (R, C) if axis == 1 else (C, R)
+    codes = np.zeros((rows, K // 2), dtype=np.uint8)
+    scales = np.zeros((rows, K // 32), dtype=np.uint8)
+    rc = _load().mxo_quantize_grid(_ptr(x), R, C, C, int(bool(hadamard)), int(axis), float(alpha), _ptr(codes),
+                                   _ptr(scales))
+    if rc != 0:
+        raise ValueError("oracle quantize_grid rejected its arguments")
+    return codes, scales, None

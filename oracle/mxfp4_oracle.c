@@ -929,3 +929,54 @@ int mxo_qema_quantize(const uint16_t *w, int64_t R, int64_t C, int64_t ldw, floa
         }
     return quantize_impl(NULL, ema, R, C, lde, FMT_MX, RND_RTN, hadamard, 1, 0, 0, codes, scales, NULL);
 }
+
+/* ------------------------------------------------------------------ */
+/* MXFP4 with a fixed grid scale [DIG step 1: for MXFP4 with Hadamard     */
+/* rotations one fixed scale of the quantization grid serves every model; */
+/* the page gives no value].  READING: every block's E8M0 exponent is the */
+/* smallest e with 6 * 2^e >= RN(alpha * amax), clamped to [-127, 127],   */
+/* alpha > 0 the fixed grid scale (one number for all blocks); alpha = 1  */
+/* is the absmax rule of mxo_quantize, alpha < 1 lets the block maximum   */
+/* saturate at +-6 for a finer grid.  Elements are then rounded to        */
+/* nearest exactly as mxo_quantize rounds them (y * 2^-e, saturating).    */
+/* Rotation (hadamard = 1) as in mxo_quantize.  PARITY UNPINNED as to the */
+/* value of alpha (a caller's argument).                                   */
+/* ------------------------------------------------------------------ */
+int mxo_quantize_grid(const uint16_t *x, int64_t R, int64_t C, int64_t ldx, int hadamard, int axis,
+                      float alpha, uint8_t *codes, uint8_t *scales)
+{
+    if (!x || !codes || !scales || R < 0 || C < 0 || ldx < C || (axis != 0 && axis != 1)) return -1;
+    if (!(alpha > 0.0f) || !isfinite(alpha)) return -1;
+    const int64_t rows = (axis == 1) ? R : C;
+    const int64_t K = (axis == 1) ? C : R;
+    if (K % 32 != 0) return -1;
+    if (rows == 0 || K == 0) return 0;
+    #pragma omp parallel
+    {
+        float *v = (float *)malloc(sizeof(float) * K);
+        #pragma omp for
+        for (int64_t i = 0; i < rows; i++) {
+            load_contraction_row(x, ldx, axis, i, K, hadamard, v);
+            for (int64_t b = 0; b < K / 32; b++) {
+                const float *blk = v + b * 32;
+                float amax;
+                int byte;
+                double step = 0.0;
+                const int finite = block_amax(blk, 32, &amax);
+                if (!finite) {
+                    byte = 0xFF;
+                } else {
+                    float a = alpha * amax;                 /* one binary32 multiply */
+                    int e = mxo_mx_scale_exponent(a);
+                    byte = e + 127;
+                    step = ldexp(1.0, -e);
+                }
+                scales[i * (K / 32) + b] = (uint8_t)byte;
+                for (int j = 0; j < 32; j++)
+                    put_code(codes, K, i, b * 32 + j, finite ? mxo_rtn_code((double)blk[j] * step) : 0);
+            }
+        }
+        free(v);
+    }
+    return 0;
+}
