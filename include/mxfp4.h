@@ -268,6 +268,21 @@ mxfp4_status mxfp4_quantize_mse(const uint16_t *x, int64_t R, int64_t C, int64_t
                                 int axis, int iters, mxfp4_tensor *out, void *workspace, size_t ws_bytes,
                                 hipStream_t stream);
 
+/* MXFP4 round-to-nearest with a fixed grid scale: the digest of the MR-GPTQ
+ * paper, step 1, says that for MXFP4 with Hadamard rotations one fixed scale of
+ * the quantization grid serves every model, without giving it; here it is the
+ * argument alpha.  Each block's E8M0 exponent is the smallest e with
+ * 6 * 2^e >= RN(alpha * absmax) (binary32 product; an overflowed product takes
+ * e = 127), then the elements are rounded to nearest for that scale exactly as
+ * mxfp4_quantize(MXFP4, RTN) rounds them (saturating at +-6).  alpha = 1 is
+ * mxfp4_quantize's absmax rule; alpha < 1 lets block maxima saturate for a
+ * finer grid.  alpha in (0, 65536] (INVALID_ARG otherwise); the block Hadamard
+ * is applied first when hadamard = 1 (the setting the page names, not a
+ * requirement).  Arguments and layout as mxfp4_quantize with fmt = MXFP4;
+ * k % 32 == 0; codes 16-byte aligned.  No workspace. */
+mxfp4_status mxfp4_quantize_grid(const uint16_t *x, int64_t R, int64_t C, int64_t ldx, int hadamard, int axis,
+                                 float alpha, mxfp4_tensor *out, hipStream_t stream);
+
 /* Workspace needed by mxfp4_quantization_noise for the quantized operand q
  * (three doubles per workgroup of the pass; never 0). */
 mxfp4_status mxfp4_quantization_noise_workspace_bytes(const mxfp4_tensor *q, size_t *bytes);

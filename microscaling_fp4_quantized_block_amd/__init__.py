@@ -58,6 +58,8 @@ def _load_library() -> ctypes.CDLL:
     lib.mxfp4_quantize_noalloc.argtypes = [vp, i64, i64, i64, i32, i32, i32, i32, u64, P(MxTensorStruct), vp]
     lib.mxfp4_qema_quantize.restype = i32
     lib.mxfp4_qema_quantize.argtypes = [vp, i64, i64, i64, vp, i64, ctypes.c_float, i32, P(MxTensorStruct), vp]
+    lib.mxfp4_quantize_grid.restype = i32
+    lib.mxfp4_quantize_grid.argtypes = [vp, i64, i64, i64, i32, i32, ctypes.c_float, P(MxTensorStruct), vp]
     lib.mxfp4_dequantize.restype = i32
     lib.mxfp4_dequantize.argtypes = [P(MxTensorStruct), vp, i64, vp]
     lib.mxfp4_gemm_workspace_bytes.restype = i32
@@ -268,6 +270,24 @@ def mxfp4_qema_quantize(w: torch.Tensor, ema: torch.Tensor, beta: float, hadamar
     st = out.as_struct()
     _check(lib.mxfp4_qema_quantize(_ptr(w), R, C, max(w.stride(0), C), _ptr(ema), max(ema.stride(0), C), float(beta),
                                    int(bool(hadamard)), ctypes.byref(st), _stream(w.device)))
+    return out
+
+
+def mxfp4_quantize_grid(x: torch.Tensor, alpha: float, hadamard: bool = True, axis: int = 1,
+                        out: Optional[QTensor] = None) -> QTensor:
+    """MXFP4 round-to-nearest with a fixed grid scale alpha (each block's
+    exponent chosen for RN(alpha * absmax)); alpha = 1 is mxfp4_quantize."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D bfloat16 CUDA/HIP tensor with unit stride along its last dimension")
+    R, C = x.shape
+    rows, k = (R, C) if axis == 1 else (C, R)
+    if out is None:
+        out = empty_qtensor("mx", rows, k, hadamard, x.device)
+    if _check_operands(out) != x.device or (out.fmt, out.rows, out.k) != ("mx", rows, k):
+        raise ValueError("out must be an MXFP4 tensor of the call's shape on x's device")
+    st = out.as_struct()
+    _check(lib.mxfp4_quantize_grid(_ptr(x), R, C, x.stride(0), int(bool(hadamard)), int(axis), float(alpha),
+                                   ctypes.byref(st), _stream(x.device)))
     return out
 
 
@@ -498,7 +518,7 @@ gemm = mxfp4_gemm
 quantize_gemm = mxfp4_quantize_gemm
 
 __all__ = ["QTensor", "MxFp4Error", "mxfp4_tensor_bytes", "mxfp4_quantize_workspace_bytes", "mxfp4_quantize",
-           "mxfp4_quantize_noalloc", "mxfp4_qema_quantize", "mxfp4_gemm_quantize",
+           "mxfp4_quantize_noalloc", "mxfp4_qema_quantize", "mxfp4_gemm_quantize", "mxfp4_quantize_grid",
            "mxfp4_gemm_quantize_workspace_bytes",
            "mxfp4_dequantize", "mxfp4_gemm_workspace_bytes", "mxfp4_gemm", "mxfp4_gemm_bf16", "mxfp4_status_string",
            "mxfp4_quantize_gemm_workspace_bytes", "mxfp4_quantize_gemm",

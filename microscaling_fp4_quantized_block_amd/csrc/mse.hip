@@ -298,6 +298,94 @@ __global__ void __launch_bounds__(256) mse_tensor_kernel(const double* __restric
   }
 }
 
+// ---------------------------------------------------------------------------
+// MXFP4 with a fixed grid scale (the digest of "Bridging the Gap Between
+// Promise and Performance for Microscaling FP4 Quantization", step 1: for
+// MXFP4 with Hadamard rotations one fixed scale of the quantization grid
+// serves every model; the value is the caller's alpha): each block's E8M0
+// exponent is the smallest e with 6 * 2^e >= RN(alpha * absmax), then the
+// absmax quantizer's round-to-nearest for that scale.  One thread per block of
+// 32, addressed and loaded as in the MSE block kernel.
+// ---------------------------------------------------------------------------
+template <bool HAD, int AXIS>
+__global__ void __launch_bounds__(256) grid_block_kernel(MseArgs a, float alpha) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= a.units) return;
+  const int64_t nu = a.K / 32;
+  int64_t i, b;
+  if (a.small) {
+    const uint32_t qd = fastdiv((uint32_t)u, a.div), rm = (uint32_t)u - qd * a.div.d;
+    if (AXIS == 1) { i = qd; b = rm; } else { b = qd; i = rm; }
+  } else if (AXIS == 1) {
+    i = u / nu; b = u - i * nu;
+  } else {
+    b = u / a.rows; i = u - b * a.rows;
+  }
+  const int64_t k0 = b * 32;
+  float y[32];
+  if (AXIS == 1) {
+    const uint16_t* src = a.x + i * a.ldx + k0;
+    if (a.vec) {
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const u32v4 v = *(const u32v4*)(src + 8 * q);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          y[8 * q + 2 * j] = __uint_as_float(v[j] << 16);
+          y[8 * q + 2 * j + 1] = __uint_as_float(v[j] & 0xFFFF0000u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 32; j++) y[j] = __uint_as_float((uint32_t)src[j] << 16);
+    }
+  } else {
+    const uint16_t* src = a.x + k0 * a.ldx + i;
+#pragma unroll
+    for (int j = 0; j < 32; j++) y[j] = __uint_as_float((uint32_t)src[(int64_t)j * a.ldx] << 16);
+  }
+  if constexpr (HAD) fwht32_inlane(y);
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 32; j++) m = max(m, __float_as_uint(y[j]) & 0x7FFFFFFFu);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  uint32_t byte = 0xFFu;
+  if (m < 0x7F800000u) {
+    const float scaled = alpha * __uint_as_float(m);
+    const uint32_t sb = __float_as_uint(scaled);
+    byte = sb >= 0x7F800000u ? 254u : mx_scale_byte_from_f32bits(sb);   // an overflowed product takes e = 127
+#pragma unroll
+    for (int q = 0; q < 4; q++) w[q] = cvt8(y + 8 * q, e8m0_as_cvt_scale(byte));
+  }
+  *(u32v4*)(a.codes + i * (a.K / 2) + k0 / 2) = (u32v4){w[0], w[1], w[2], w[3]};
+  a.scales[i * (a.K / 32) + b] = (uint8_t)byte;
+}
+
+hipError_t launch_quantize_grid(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int hadamard, int axis,
+                                float alpha, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  const int64_t rows = axis == 1 ? R : C, K = axis == 1 ? C : R;
+  MseArgs a{};
+  a.x = x;
+  a.ldx = ldx;
+  a.rows = rows;
+  a.K = K;
+  a.codes = codes;
+  a.scales = scales;
+  a.units = rows * (K / 32);
+  a.small = a.units < ((int64_t)1 << 31) ? 1 : 0;
+  a.div = make_fastdiv(a.small ? (uint32_t)(axis == 1 ? K / 32 : rows) : 1u);
+  a.vec = (((uintptr_t)x & 15) == 0 && ldx % 8 == 0) ? 1 : 0;
+  const unsigned g = (unsigned)((a.units + 255) / 256);
+  if (hadamard) {
+    if (axis == 1) hipLaunchKernelGGL((grid_block_kernel<true, 1>), dim3(g), dim3(256), 0, stream, a, alpha);
+    else hipLaunchKernelGGL((grid_block_kernel<true, 0>), dim3(g), dim3(256), 0, stream, a, alpha);
+  } else {
+    if (axis == 1) hipLaunchKernelGGL((grid_block_kernel<false, 1>), dim3(g), dim3(256), 0, stream, a, alpha);
+    else hipLaunchKernelGGL((grid_block_kernel<false, 0>), dim3(g), dim3(256), 0, stream, a, alpha);
+  }
+  return hipGetLastError();
+}
+
 static int mse_unit(int fmt, int hadamard, int64_t K) {
   return (fmt == FMT_NV && !hadamard && K % 32 != 0) ? 16 : 32;
 }

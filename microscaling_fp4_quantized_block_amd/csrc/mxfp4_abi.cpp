@@ -55,6 +55,22 @@ mxfp4_status mxfp4_qema_quantize(const uint16_t* w, int64_t R, int64_t C, int64_
   return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
 }
 
+mxfp4_status mxfp4_quantize_grid(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int hadamard, int axis,
+                                 float alpha, mxfp4_tensor* out, hipStream_t stream) {
+  if (!out || (hadamard != 0 && hadamard != 1) || (axis != 0 && axis != 1)) return MXFP4_ERR_INVALID_ARG;
+  if (!(alpha > 0.0f) || !(alpha <= 65536.0f)) return MXFP4_ERR_INVALID_ARG;
+  if (R < 0 || C < 0 || ldx < C || ldx < 1) return MXFP4_ERR_INVALID_ARG;
+  const int64_t rows = axis == 1 ? R : C, k = axis == 1 ? C : R;
+  if (k % 32 != 0) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  if (R > 0 && C > kMaxElems / R) return MXFP4_ERR_UNSUPPORTED_SHAPE;
+  if (out->fmt != MXFP4_FMT_MX || out->rows != rows || out->k != k || out->hadamard != hadamard)
+    return MXFP4_ERR_INVALID_ARG;
+  if (rows == 0 || k == 0) return MXFP4_OK;
+  if (!x || !out->codes || !out->scales || !aligned(out->codes, 16)) return MXFP4_ERR_INVALID_ARG;
+  hipError_t e = mxfp4::launch_quantize_grid(x, R, C, ldx, hadamard, axis, alpha, out->codes, out->scales, stream);
+  return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP;
+}
+
 mxfp4_status mxfp4_noise_ratio(const double* stats, double* ratio, int* below_threshold) {
   if (!stats || !ratio || !below_threshold) return MXFP4_ERR_INVALID_ARG;
   const double signal = stats[0], noise = stats[1];

@@ -68,6 +68,11 @@ hipError_t launch_quantize_mse(const uint16_t* x, int64_t R, int64_t C, int64_t 
                                int axis, int iters, uint8_t* codes, uint8_t* scales, float* tensor_scale,
                                void* workspace, hipStream_t stream);
 
+// MXFP4 round-to-nearest with a fixed grid scale alpha (mse.hip): each block's
+// exponent chosen for RN(alpha * absmax).  K % 32 == 0.
+hipError_t launch_quantize_grid(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int hadamard, int axis,
+                                float alpha, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
 // Signal and quantization-noise sums of a quantized operand (noise.hip):
 // workspace = 3 doubles per workgroup of the pass.
 size_t noise_workspace_bytes(int fmt, int hadamard, int64_t rows, int64_t K);

@@ -438,3 +438,14 @@ def test_gemm_quantize_rejects_bad_arguments_and_sizes_its_workspace(mx):
     assert f(ctypes.byref(a), ctypes.byref(b), 1, ctypes.byref(out), None, 0, None) == INVALID   # out->hadamard
     assert f(ctypes.byref(a), ctypes.byref(b), 0, ctypes.byref(desc(mx, 1, 0, 512, 768)), None, 0, None) == INVALID
     assert f(ctypes.byref(a), ctypes.byref(desc(mx, 1, 0, 768, 1024)), 0, ctypes.byref(out), None, 0, None) == MISMATCH
+
+
+def test_quantize_grid_rejects_bad_arguments(mx):
+    out = desc(mx, 0, 1, 64, 256)
+    f = mx.lib.mxfp4_quantize_grid
+    x = ctypes.c_void_p(FAKE)
+    assert f(x, 64, 256, 256, 1, 1, ctypes.c_float(0.0), ctypes.byref(out), None) == INVALID
+    assert f(x, 64, 256, 256, 1, 1, ctypes.c_float(float("nan")), ctypes.byref(out), None) == INVALID
+    assert f(x, 64, 256, 256, 0, 1, ctypes.c_float(0.75), ctypes.byref(out), None) == INVALID     # hadamard differs
+    assert f(x, 64, 240, 240, 1, 1, ctypes.c_float(0.75), ctypes.byref(desc(mx, 0, 1, 64, 240)), None) == SHAPE
+    assert f(None, 64, 256, 256, 1, 1, ctypes.c_float(0.75), ctypes.byref(out), None) == INVALID
