@@ -654,6 +654,50 @@ def sweep(args):
                     rows.append((cfg, "quantize+gemm", f"{gname} ({label})", f"{Mg}x{Ng}x{Kg}", t * 1e6,
                                  flops / t / 1e12, "TFLOP/s", bound, bound_t / t))
                 del C, ws, gws
+            # prefill up with its output quantized (rotated) for the down
+            # projection, in the GEMM's epilogue, against the two launches it
+            # replaces (bf16 GEMM, then quantize); bytes: operands + 0.53 B out
+            qx, qw = qs[("x_pre_up", "rtn", 1)], qs[("W_up", "rtn", 1)]
+            Mg, Ng, Kg = qx.rows, qw.rows, qx.k
+            qo = mx.empty_qtensor("mx", Mg, Ng, True, dev)
+            Cb = torch.empty((Mg, Ng), dtype=torch.bfloat16, device=dev)
+            gws = torch.empty(max(mx.mxfp4_gemm_workspace_bytes(qx, qw), 4), dtype=torch.uint8, device=dev)
+            flops = 2.0 * Mg * Ng * Kg
+            t_f = timed(lambda: mx.mxfp4_gemm_quantize(qx, qw, True, out=qo), False)
+
+            def two_q():
+                mx.mxfp4_gemm_bf16(qx, qw, out=Cb, workspace=gws)
+                mx.mxfp4_quantize(Cb, "mx", "rtn", True, 1, 0, out=qo)
+            t_2 = timed(two_q, False)
+            nbytes = (Mg + Ng) * Kg * (0.5 + 1.0 / 32) + Mg * Ng * (0.5 + 1.0 / 32)
+            bound_t = max(flops / (PEAK_FP4_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBPS * 1e9))
+            for label, t in (("epilogue", t_f), ("bf16 GEMM + quantize", t_2)):
+                rows.append((cfg, "gemm+quantize C", f"prefill up, C quantized with H ({label})", f"{Mg}x{Ng}x{Kg}",
+                             t * 1e6, flops / t / 1e12, "TFLOP/s", "mfma", bound_t / t))
+            del qo, Cb, gws
+            # the weights with a fixed grid scale (alpha = 0.75, rotated)
+            for name in ("W_up", "W_down"):
+                x = tens[name]
+                R, Cc = x.shape
+                q = mx.empty_qtensor("mx", R, Cc, True, dev)
+                t = timed(lambda: mx.mxfp4_quantize_grid(x, 0.75, True, 1, out=q), True)
+                gbps = R * Cc * (2.0 + 0.5 + 1.0 / 32) / t / 1e9
+                rows.append((cfg, "quantize_grid", f"{name} alpha 0.75 H", f"{R}x{Cc}", t * 1e6, gbps, "GB/s", "hbm",
+                             gbps / PEAK_HBM_GBPS))
+                del q
+        if cfg == 4:
+            # Q-EMA step of the weights: bf16 w + fp32 average in, fp32
+            # average + codes + scales out (10.53 B per element)
+            for name in ("W1", "W2"):
+                w = tens[name] if name in tens else draw(cfg, name)
+                R, Cc = w.shape
+                m = w.float().clone()
+                q = mx.empty_qtensor("mx", R, Cc, False, dev)
+                t = timed(lambda: mx.mxfp4_qema_quantize(w, m, 0.999, False, out=q), True)
+                gbps = R * Cc * (2.0 + 4.0 + 4.0 + 0.5 + 1.0 / 32) / t / 1e9
+                rows.append((cfg, "qema", f"{name} beta 0.999", f"{R}x{Cc}", t * 1e6, gbps, "GB/s", "hbm",
+                             gbps / PEAK_HBM_GBPS))
+                del m, q
         del tens, qs
         torch.cuda.empty_cache()
     lines = ["| config | kernel | call | shape | time us | achieved | unit | bound | frac of roofline |",

@@ -97,6 +97,8 @@ struct GemmArgs {
 #ifndef MXFP4_GROUP_M
 #define MXFP4_GROUP_M 4
 #endif
+
+
 __device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn) {
   const int ntiles = p.ntm * p.ntn;
   int id = blockIdx.x;
@@ -519,17 +521,17 @@ __device__ __forceinline__ void mx_sched() {
 
 // Operand resources of one tile: they end at the operand's last row of the
 // tile (at most ROWS rows from its first), so rows past M or N read as zeros.
-// Each wave loads RPW = ROWS / 4 rows per stage, 8 rows per load.
+// Each of the NW waves loads RPW = ROWS / NW rows per stage, 8 rows per load.
 struct MxOperand {
   __amdgpu_buffer_rsrc_t codes, scales;
   uint32_t code_off[2];  // this lane's offset for loads 0 and 1 of the wave (load j: [j & 1] + (j >> 1) * 16 rows)
   uint32_t scale_off;    // this lane's row in the wave's 64-row scale piece
 };
 
-template <int ROWS>
+template <int ROWS, int NW = 4>
 __device__ __forceinline__ MxOperand mx_make_operand(const uint8_t* codes, const uint8_t* scales, int64_t rows_total,
                                                      int64_t row0, int64_t K, int w, int l) {
-  constexpr int RPW = ROWS / 4;
+  constexpr int RPW = ROWS / NW;
   const int64_t krow = K / 2, srow = K / 32;
   int64_t nrows = rows_total - row0;
   if (nrows > ROWS) nrows = ROWS;
@@ -545,8 +547,9 @@ __device__ __forceinline__ MxOperand mx_make_operand(const uint8_t* codes, const
     const int row = RPW * w + 8 * j + (l >> 3);
     o.code_off[j] = (uint32_t)(row * krow + (((l & 7) ^ ((row >> 1) & 7)) << 4));
   }
-  // scale piece w is rows 64w .. 64w + 63 (past ROWS: out of range, zeros)
-  o.scale_off = (uint32_t)((64 * w + l) * srow);
+  // scale piece w % 4 is rows 64 (w % 4) .. + 63 (past ROWS: out of range,
+  // zeros); with 8 waves, waves 0-3 load A's pieces and waves 4-7 B's
+  o.scale_off = (uint32_t)((64 * (w & 3) + l) * srow);
   return o;
 }
 
@@ -895,6 +898,127 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs p) {
   }
 }
 
+// Wide tiles with 8 waves (two per SIMD), for short contractions (at most
+// four stages): measured against the 4-wave kernel, 50432 x 3072 x 768 161 ->
+// 128 us and 1024^3 17.2 -> 13.0 us, but 10-23 % slower at K >= 3072 (the two
+// waves of a SIMD wait at the same barriers), so plan_gemm takes it for
+// K <= 1024 only.  Wave w owns rows 64 (w / 2) .. + 63
+// and columns (32 TN) (w % 2) .. of the 256 x (64 TN) tile, 2 x TN MFMA tiles
+// (128 accumulators at TN = 4).  The loop is deliberately simple -- each step
+// reads its fragments and waits for them -- because the other wave on the SIMD
+// issues its MFMAs meanwhile.  Stage a + 1's loads are issued right after the
+// barrier that frees its buffer and waited for at the end of stage a; scale
+// group G + 1 is loaded in stage 2G.  Same LDS layout as mx_tile.
+template <int TN, int OUT>
+__device__ __forceinline__ void mx8_tile(const GemmArgs& p, uint8_t* smem, int64_t m0, int64_t n0, int kt0, int kt1,
+                                         float* Cz) {
+  constexpr int TM = 2, NW = 8, WM = 4, WN = 2;
+  constexpr int LA = 4, LB = TN;                 // code loads (8 rows each) per wave per stage: A 32 rows, B 8 TN rows
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63, h = l >> 5;
+  const int wm = w / WN, wn = w % WN;
+  const int ra0 = wm * (32 * TM) + (l & 31), rb0 = wn * (32 * TN) + (l & 31);
+  auto pos = [&](int c) { return ((c ^ ((l >> 1) & 7)) << 4); };
+  const uint32_t sel = h ? 0x07050301u : 0x06040200u;
+  const int ksteps = (int)(p.K / 64);
+  v16f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; i++)
+#pragma unroll
+    for (int j = 0; j < TN; j++) acc[i][j] = (v16f){};
+  if (kt1 > kt0) {
+    const uint32_t krow16 = (uint32_t)(16 * (p.K / 2));
+    const MxOperand oa = mx_make_operand<256, NW>(p.a, p.as, p.M, m0, p.K, w, l);
+    const MxOperand ob = mx_make_operand<32 * TN * WN, NW>(p.b, p.bs, p.N, n0, p.K, w, l);
+    auto stage = [&](int a) { return smem + (a & 1) * MX_STAGE; };
+    auto group = [&](int G) { return smem + MX_GROUP_OFF + (G % MX_GROUPS) * 2 * MX_GROUP_OPND; };
+    auto issue_group = [&](int G) {               // waves 0-3 load A's pieces, 4-7 B's
+      const int side = w >> 2;
+      const __amdgpu_buffer_rsrc_t r = side ? ob.scales : oa.scales;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(group(G) + side * MX_GROUP_OPND + (w & 3) * 1024), 16,
+                                               oa.scale_off, 16 * G, 0, 0);
+    };
+    auto mask_of = [&](int a) -> uint32_t {
+      const int v = min(max(ksteps - 4 * a, 0), 4);
+      return (uint32_t)((1ull << (8 * v)) - 1ull);
+    };
+    issue_group(kt0 >> 1);
+    mx_issue_codes<0, LA + LB, LA, LB>(oa, ob, stage(kt0), kt0, krow16, w);
+    wait_cnt<0, 15>();
+    block_barrier();
+    for (int a = kt0; a < kt1; a++) {
+      const uint8_t* sa_ = stage(a);
+      const uint8_t* sb_ = stage(a) + MX_OPND;
+      if (a + 1 < kt1) mx_issue_codes<0, LA + LB, LA, LB>(oa, ob, stage(a + 1), a + 1, krow16, w);
+      if (!(a & 1) && a + 2 < kt1) issue_group((a >> 1) + 1);
+      // this stage's scale bytes: 8 per row (half a group), one byte per 64-wide step in each register
+      const uint8_t* ga = group(a >> 1) + 8 * (a & 1);
+      const uint8_t* gb = ga + MX_GROUP_OPND;
+      uint32_t sa[TM], sb[TN];
+      const uint32_t mask = mask_of(a);
+#pragma unroll
+      for (int t = 0; t < TM; t++) {
+        const uint2 v = *(const uint2*)(ga + (ra0 + 32 * t) * 16);
+        sa[t] = __builtin_amdgcn_perm(v.y, v.x, sel) & mask;
+      }
+#pragma unroll
+      for (int t = 0; t < TN; t++) {
+        const uint2 v = *(const uint2*)(gb + (rb0 + 32 * t) * 16);
+        sb[t] = __builtin_amdgcn_perm(v.y, v.x, sel) & mask;
+      }
+      MxFrag<TM, TN> f;
+      mx_read_frag<TM, TN>(sa_, sb_, ra0, rb0, pos(0 + h), f);
+      mx_mfma<0, TM, TN>(acc, f, sa, sb);
+      mx_read_frag<TM, TN>(sa_, sb_, ra0, rb0, pos(2 + h), f);
+      mx_mfma<1, TM, TN>(acc, f, sa, sb);
+      mx_read_frag<TM, TN>(sa_, sb_, ra0, rb0, pos(4 + h), f);
+      mx_mfma<2, TM, TN>(acc, f, sa, sb);
+      mx_read_frag<TM, TN>(sa_, sb_, ra0, rb0, pos(6 + h), f);
+      mx_mfma<3, TM, TN>(acc, f, sa, sb);
+      wait_cnt<0, 0>();      // this wave's loads of stage a + 1 (and scale pieces) landed; its reads done
+      block_barrier();
+    }
+  }
+  if constexpr (OUT == OUT_MXQ) {
+    block_barrier();
+    quantize_tile<TM, TN>(p, smem, m0 + wm * (32 * TM), n0 + wn * (32 * TN), acc);
+  } else {
+    store_tile<TM, TN, false, OUT>(p, Cz, m0 + wm * (32 * TM), n0 + wn * (32 * TN), acc);
+  }
+}
+
+// The wide kernel with 8 waves (mx8_tile): 64 x 128 per wave (half tiles
+// 64 x 64), 128 accumulators, two waves per SIMD.
+template <int OUT>
+__global__ void __launch_bounds__(512, 1) gemm_mx8_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[MX_LDS];
+  int b = blockIdx.x, z = blockIdx.y;
+  if (p.splits > 1) {
+    const int total = gridDim.x * gridDim.y, id = z * gridDim.x + b;
+    const int base = total >> 3, extra = total & 7, x = id & 7, slot = id >> 3;
+    const int pos = (x < extra ? x * (base + 1) : extra * (base + 1) + (x - extra) * base) + slot;
+    z = pos / gridDim.x;
+    b = pos - z * gridDim.x;
+  }
+  const int pairs = (p.k_tiles + 1) >> 1;
+  const int kt0 = 2 * (int)((int64_t)pairs * z / p.splits);
+  int kt1 = 2 * (int)((int64_t)pairs * (z + 1) / p.splits);
+  if (kt1 > p.k_tiles) kt1 = p.k_tiles;
+  float* Cz = p.C + (int64_t)z * p.split_stride;
+  const int R = p.rem, T = p.ntm * p.ntn;
+  int tm, tn;
+  const int F = T - R;
+  if (b >= R && b < R + F) {
+    tm = mx_walk(p, p.splits > 1 ? b : xcd_gather(b - R, F), tn);
+    mx8_tile<4, OUT>(p, smem, (int64_t)tm * BM, (int64_t)tn * BN, kt0, kt1, Cz);
+  } else {
+    const int second = b >= R + F;
+    const int i = second ? b - R - F : b;
+    tm = mx_walk(p, F + xcd_gather(i, R), tn);
+    mx8_tile<2, OUT>(p, smem, (int64_t)tm * BM, (int64_t)tn * BN + 128 * second, kt0, kt1, Cz);
+  }
+}
+
 // Narrow MXFP4 GEMM (M <= 32 TM <= 128: decode-shaped activations against
 // weights): 32 TM x 256 tiles, the four waves side by side along N, so no MFMA
 // work is spent on rows past M; these shapes stream the weights from HBM and
@@ -1078,6 +1202,7 @@ GemmPlan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
   GemmPlan pl;
   pl.k_tiles = (K + (mx ? MX_BK : BK) - 1) / (mx ? MX_BK : BK);
   pl.narrow_tm = 0;
+  pl.waves8 = 0;
   if (mx && M <= 128) {
     // narrow tiles (32 TM x 256), split along K (in stage pairs) into at most
     // one workgroup per compute unit, each split at least two pairs long
@@ -1092,6 +1217,7 @@ GemmPlan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
     return pl;
   }
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  pl.waves8 = mx && pl.k_tiles <= 4 ? 1 : 0;     // short contractions: the 8-wave kernel (mx8_tile)
   // the MXFP4 kernel splits in pairs of stages (one scale group)
   const int64_t units = mx ? (pl.k_tiles + 1) / 2 : pl.k_tiles;
   const int64_t min_units = mx ? 2 : 4;        // at least 4 stages of 256 / 128 per split
@@ -1137,6 +1263,8 @@ static void launch_gemm_kernel(bool nv, const GemmArgs& p, const GemmPlan& plan,
     hipLaunchKernelGGL((gemm_mx_narrow_kernel<2, OUT>), ngrid, dim3(256), 0, stream, p);
   } else if (plan.narrow_tm) {
     hipLaunchKernelGGL((gemm_mx_narrow_kernel<4, OUT>), ngrid, dim3(256), 0, stream, p);
+  } else if (plan.waves8) {
+    hipLaunchKernelGGL(gemm_mx8_kernel<OUT>, grid, dim3(512), 0, stream, p);
   } else {
     hipLaunchKernelGGL(gemm_mx_kernel<OUT>, grid, dim3(256), 0, stream, p);
   }

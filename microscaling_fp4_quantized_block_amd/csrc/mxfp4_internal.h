@@ -29,6 +29,7 @@ struct GemmPlan {
   int splits;
   int64_t k_tiles;     // contraction tiles of the kernel's K step
   int narrow_tm;       // MXFP4 with M <= 128: rows per narrow tile / 32 (1, 2 or 4); 0 = wide tiles
+  int waves8;          // MXFP4 wide tiles with at most four stages: the 8-wave kernel
 };
 GemmPlan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K);
 
