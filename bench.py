@@ -67,25 +67,35 @@ def parse():
     return ap.parse_args()
 
 
-GEMM_SRC = os.path.join(ROOT, "microscaling_fp4_quantized_block_amd", "csrc", "gemm.hip")
 COPY_BYTES = 1 << 30
 
 
-def source_digest(path=GEMM_SRC):
-    import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def _build_module():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "mxfp4_build", os.path.join(ROOT, "microscaling_fp4_quantized_block_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def kernel_digest(compile_if_stale=False):
+    """SHA-256 (16 hex digits) of the headline GEMM kernel's gfx950 assembly
+    (gemm_mx_kernel, FP32 C) as recorded by the build; None when the record is
+    missing or older than the sources (unless compile_if_stale)."""
+    return _build_module().kernel_digests(compile_if_stale).get("gemm_mx_kernel_f32")
 
 
 def gemm_traffic(path):
     """HBM bytes per launch of the GEMM kernel measured with rocprofv3 PMC
     counters (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads
     for a plain copy of known size); None when the file is missing or was
-    measured on a different GEMM source."""
+    measured on different kernel code."""
     try:
         with open(path) as f:
             d = json.loads(f.read().split("\n", 1)[1])
-        if d.get("gemm_source_sha256_16") != source_digest():
+        digest = kernel_digest()
+        if digest is None or d.get("gemm_isa_sha256_16") != digest:
             return None
         return float(d["bytes_per_launch"])
     except (OSError, ValueError, KeyError, IndexError):
@@ -127,7 +137,7 @@ def summarize_pmc(fetch_dir, write_dir, out_path):
          "algorithmic_bytes": algorithmic, "copy_calibration": {"bytes": COPY_BYTES, "fetch_counter": c_f,
                                                                 "write_counter": c_w},
          "gemm_counters": {"FETCH_SIZE": g_f, "WRITE_SIZE": g_w},
-         "gemm_source_sha256_16": source_digest()}
+         "gemm_isa_sha256_16": kernel_digest(compile_if_stale=True)}
     with open(out_path, "w") as f:
         f.write("HBM traffic of gemm_mx_kernel, 4096x14336x8192 MXFP4 (rocprofv3 PMC FETCH_SIZE / WRITE_SIZE, "
                 "scaled by a 1 GiB copy; commands in profiles/README.md)\n")

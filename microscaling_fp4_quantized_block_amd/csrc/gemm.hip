@@ -493,7 +493,6 @@ constexpr int MX_GROUP_OPND = 256 * 16;          // one operand's scale group: 4
 constexpr int MX_GROUP_OFF = 2 * MX_STAGE;       // 128 KB
 constexpr int MX_GROUPS = 3;                     // scale group buffers
 constexpr int MX_LDS = MX_GROUP_OFF + MX_GROUPS * 2 * MX_GROUP_OPND;   // 152 KB
-constexpr int MX_LOADS = 17;                     // buffer->LDS instructions per wave per stage
 
 // Per-wave operand blocks: TM row blocks of A (32 TM rows) and TN column
 // blocks of B (32 TN columns).  Wide tiles: TM = 4, TN = 4 (or 2 for the
@@ -968,7 +967,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmArgs p) {
 template <int TN, int OUT>
 __device__ __forceinline__ void mx8_tile(const GemmArgs& p, uint8_t* smem, int64_t m0, int64_t n0, int kt0, int kt1,
                                          float* Cz) {
-  constexpr int TM = 2, NW = 8, WM = 4, WN = 2;
+  constexpr int TM = 2, NW = 8, WN = 2;           // 4 x 2 waves
   constexpr int LA = 4, LB = TN;                 // code loads (8 rows each) per wave per stage: A 32 rows, B 8 TN rows
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63, h = l >> 5;
@@ -1137,9 +1136,25 @@ __device__ __forceinline__ v2h e4m3_pair(int word) {
 }
 
 // A stage holds 8 NVFP4 blocks per row.  Lane group g owns blocks 4g..4g+3
-// (32 contiguous bytes); at step u it feeds half (u & 1) of block 4g + u/2 to
-// the 32x32x16 fp16 MFMA.  A and B use the same assignment, so every step
-// pairs equal contraction indices.
+// (32 contiguous bytes); at step u (0..7) it feeds half (u & 1) of block
+// 4g + u/2 to the 32x32x16 fp16 MFMA.  A and B use the same assignment, so
+// every step pairs equal contraction indices.
+//
+// Schedule of a stage: all its code chunks and scale words are read from LDS
+// first, step 0's fragments are dequantized, then each step's 16 MFMAs run
+// with the next step's dequantization (64 VALU instructions) interleaved one
+// MFMA, four VALU: an MFMA keeps the matrix pipe busy for 8 passes while the
+// wave issues the independent VALU work behind it.  (Left to itself the
+// compiler bunches the conversions ahead of the MFMAs and the two serialize.)
+__device__ __forceinline__ void nv_sched_step(bool with_valu) {
+#pragma unroll
+  for (int q = 0; q < 16; q++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // one MFMA
+    if (with_valu) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int OUT>
 __global__ void __launch_bounds__(256, 1) gemm_nv_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * STAGE_BYTES];
@@ -1166,39 +1181,49 @@ __global__ void __launch_bounds__(256, 1) gemm_nv_kernel(GemmArgs p) {
     const uint8_t* B = st + A_BYTES;
     const uint8_t* SA = st + A_BYTES + B_BYTES;
     const uint8_t* SB = SA + SA_BYTES;
-    // the lane's four block scales per row, once per stage
+    // the stage's code chunks (half h = blocks 4g + 2h, +1) and the lane's
+    // four block scales per row
+    v4i ca[2][4], cb[2][4];
+    int sa[4], sb[4];
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      sa[t] = *(const int*)(SA + (ra0 + 32 * t) * 8 + 4 * g);
+      sb[t] = *(const int*)(SB + (rb0 + 32 * t) * 8 + 4 * g);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+#pragma unroll
+      for (int t = 0; t < 4; t++) {
+        ca[h][t] = *(const v4i*)(A + (ra0 + 32 * t) * ROWB + (h ? offc1 : offc0));
+        cb[h][t] = *(const v4i*)(B + (rb0 + 32 * t) * ROWB + (h ? offc1 : offc0));
+      }
     v2h fa[4][4], fb[4][4];
 #pragma unroll
     for (int t = 0; t < 4; t++) {
-      const int sa = *(const int*)(SA + (ra0 + 32 * t) * 8 + 4 * g);
-      const int sb = *(const int*)(SB + (rb0 + 32 * t) * 8 + 4 * g);
-      fa[t][0] = e4m3_pair<0>(sa); fa[t][1] = e4m3_pair<1>(sa); fa[t][2] = e4m3_pair<2>(sa); fa[t][3] = e4m3_pair<3>(sa);
-      fb[t][0] = e4m3_pair<0>(sb); fb[t][1] = e4m3_pair<1>(sb); fb[t][2] = e4m3_pair<2>(sb); fb[t][3] = e4m3_pair<3>(sb);
+      fa[t][0] = e4m3_pair<0>(sa[t]); fa[t][1] = e4m3_pair<1>(sa[t]); fa[t][2] = e4m3_pair<2>(sa[t]); fa[t][3] = e4m3_pair<3>(sa[t]);
+      fb[t][0] = e4m3_pair<0>(sb[t]); fb[t][1] = e4m3_pair<1>(sb[t]); fb[t][2] = e4m3_pair<2>(sb[t]); fb[t][3] = e4m3_pair<3>(sb[t]);
     }
-#pragma unroll
-    for (int half = 0; half < 2; half++) {        // 16-byte chunk: blocks 4g + 2 half, +1
-      const int offc = half ? offc1 : offc0;
-      v4i ca[4], cb[4];
+    // step u: word u & 3 of half u >> 2, block 2 (u >> 2) + ((u & 3) >> 1)
+    v8h af[2][4], bf[2][4];
+    auto dequant = [&](int u, v8h (&xa)[4], v8h (&xb)[4]) {
+      const int h = u >> 2, wd = u & 3, blk = 2 * h + (wd >> 1);
 #pragma unroll
       for (int t = 0; t < 4; t++) {
-        ca[t] = *(const v4i*)(A + (ra0 + 32 * t) * ROWB + offc);
-        cb[t] = *(const v4i*)(B + (rb0 + 32 * t) * ROWB + offc);
+        xa[t] = nv_dequant8((uint32_t)ca[h][t][wd], fa[t][blk]);
+        xb[t] = nv_dequant8((uint32_t)cb[h][t][wd], fb[t][blk]);
       }
+    };
+    dequant(0, af[0], bf[0]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < 4; u++) {                // word u of the chunk = half (u & 1) of block 2 half + u/2
-        const int blk = 2 * half + (u >> 1);
-        v8h af[4], bf[4];
+    for (int u = 0; u < 8; u++) {
+      if (u < 7) dequant(u + 1, af[(u + 1) & 1], bf[(u + 1) & 1]);
 #pragma unroll
-        for (int t = 0; t < 4; t++) {
-          af[t] = nv_dequant8((uint32_t)ca[t][u], fa[t][blk]);
-          bf[t] = nv_dequant8((uint32_t)cb[t][u], fb[t][blk]);
-        }
+      for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-          for (int j = 0; j < 4; j++)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-      }
+        for (int j = 0; j < 4; j++)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[u & 1][i], bf[u & 1][j], acc[i][j], 0, 0, 0);
+      nv_sched_step(u < 7);
     }
   });
   float* Cz = p.C + (int64_t)z * p.split_stride;

@@ -22,12 +22,12 @@ def test_more_than_one_gpu_is_refused():
 
 def _traffic_file(tmp_path, digest, nbytes=123456.0):
     p = tmp_path / "traffic.txt"
-    p.write_text("header line\n" + json.dumps({"bytes_per_launch": nbytes, "gemm_source_sha256_16": digest}))
+    p.write_text("header line\n" + json.dumps({"bytes_per_launch": nbytes, "gemm_isa_sha256_16": digest}))
     return str(p)
 
 
 def test_traffic_only_for_the_measured_gemm_source(tmp_path):
-    assert bench.gemm_traffic(_traffic_file(tmp_path, bench.source_digest())) == 123456.0
+    assert bench.gemm_traffic(_traffic_file(tmp_path, bench.kernel_digest(compile_if_stale=True))) == 123456.0
     assert bench.gemm_traffic(_traffic_file(tmp_path, "0" * 16)) is None
     assert bench.gemm_traffic(str(tmp_path / "missing.txt")) is None
     bad = tmp_path / "bad.txt"
@@ -36,8 +36,9 @@ def test_traffic_only_for_the_measured_gemm_source(tmp_path):
 
 
 def test_committed_traffic_matches_the_gemm_source():
-    """The committed PMC summary was taken on the current GEMM source, so the
-    benchmark reports its traffic figure."""
+    """The committed PMC summary was taken on the current headline GEMM kernel
+    (same gfx950 assembly), so the benchmark reports its traffic figure."""
+    bench.kernel_digest(compile_if_stale=True)
     path = os.path.join(ROOT, "profiles", "gemm_mx_headline_traffic.txt")
     assert bench.gemm_traffic(path) is not None
 

@@ -40,10 +40,19 @@ def test_noalloc_matches_quantize_on_two_calls(fmt, rnd, had, axis):
         assert _same(got, ref), (fmt, rnd, had, axis, R, C)
 
 
+SCRATCH_BYTES = 1 << 20   # the library's static scratch (262144 partials)
+
+
 def test_noalloc_refuses_inputs_past_the_scratch():
     mx = need_gpu()
-    # 2^20 x 2^13 NVFP4 elements need 4 MiB of partials: refused before launch
-    out = mx.MxTensorStruct(1, 0, 2 ** 20, 2 ** 13, 0x100000, 0x100000, 0x100000)
-    status = mx.lib.mxfp4_quantize_noalloc(ctypes.c_void_p(0x100000), 2 ** 20, 2 ** 13, 2 ** 13, 1, 0, 0, 1, 0,
+    # 2^20 x 2^13 NVFP4 elements need 2 MiB of partials: refused before any
+    # launch.  The pointers are not device memory, so the call is made only
+    # once the size query confirms the refusal.
+    R, C = 2 ** 20, 2 ** 13
+    need = mx.mxfp4_quantize_workspace_bytes("nv", R, C)
+    if need <= SCRATCH_BYTES:
+        pytest.fail(f"{R}x{C} needs {need} bytes of partials, within the scratch: not a refusal case")
+    out = mx.MxTensorStruct(1, 0, R, C, 0x100000, 0x100000, 0x100000)
+    status = mx.lib.mxfp4_quantize_noalloc(ctypes.c_void_p(0x100000), R, C, C, 1, 0, 0, 1, 0,
                                            ctypes.byref(out), None)
     assert status == -4
