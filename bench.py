@@ -377,7 +377,8 @@ class ClockStamps:
                 "sclk_mhz_per_xcd": [round(float(np.median(per_xcd[x])), 1) for x in sorted(per_xcd)],
                 "compute_units_paired": int(len(vals)),
                 "wall_s": round(wall, 6) if wall is not None else None,
-                "source": "s_memtime / s_memrealtime of each compute unit, stamped before and after the timed steps"}
+                "source": "s_memtime / s_memrealtime of each compute unit, stamped before and after the timed steps",
+                "note": "a register-only MFMA probe puts this counter about 10% below the MFMA clock"}
 
 
 def cpu_model():
