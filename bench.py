@@ -719,8 +719,14 @@ def sweep(args):
     if args.sweep == "-":
         print(text)
     else:
+        # an existing file keeps its description above the table
+        head = ""
+        if os.path.exists(args.sweep):
+            old = open(args.sweep).read()
+            if lines[0] in old:
+                head = old[:old.index(lines[0])]
         with open(args.sweep, "w") as f:
-            f.write(text)
+            f.write(head + text)
         print(text)
 
 
