@@ -363,6 +363,9 @@ __global__ void __launch_bounds__(256) grid_block_kernel(MseArgs a, float alpha)
 
 hipError_t launch_quantize_grid(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int hadamard, int axis,
                                 float alpha, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  // the row and tiled transposing quantizers take every input they can (they
+  // differ from the plain quantizer only in the scale byte)
+  if (launch_quantize_grid_fast(x, R, C, ldx, hadamard, axis, alpha, codes, scales, stream)) return hipGetLastError();
   const int64_t rows = axis == 1 ? R : C, K = axis == 1 ? C : R;
   MseArgs a{};
   a.x = x;

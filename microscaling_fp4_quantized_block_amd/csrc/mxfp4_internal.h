@@ -63,6 +63,12 @@ hipError_t launch_gemm_nv(const uint8_t* a_codes, const uint8_t* a_scales, const
 void launch_tensor_scale(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int hadamard, int axis,
                          float* tensor_scale, uint32_t* partials, hipStream_t s);
 
+// MXFP4 round-to-nearest with a fixed grid scale through the row / tiled
+// transposing quantizers; false (nothing launched) when the input takes
+// neither (an unaligned transposed input).
+bool launch_quantize_grid_fast(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int hadamard, int axis,
+                               float alpha, uint8_t* codes, uint8_t* scales, hipStream_t s);
+
 // Round-to-nearest quantization with MSE-fitted scales (mse.hip).
 size_t quantize_mse_workspace_bytes(int fmt, int hadamard, int64_t R, int64_t C, int axis);
 hipError_t launch_quantize_mse(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int fmt, int hadamard,

@@ -157,6 +157,21 @@ __device__ __forceinline__ void block_scale(uint32_t amax_bits, float st, uint32
   }
 }
 
+// MXFP4 with a fixed grid scale alpha: the exponent is chosen for
+// RN(alpha * absmax) (an overflowed product takes e = 127); a block holding a
+// non-finite element keeps the NaN scale byte.  alpha = 1 gives block_scale.
+__device__ __forceinline__ void grid_block_scale(uint32_t amax_bits, float alpha, uint32_t& byte, float& mul,
+                                                 bool& nonfinite) {
+  nonfinite = amax_bits >= 0x7F800000u;
+  if (nonfinite) {
+    byte = 0xFFu;
+  } else {
+    const uint32_t sb = __float_as_uint(alpha * __uint_as_float(amax_bits));
+    byte = sb >= 0x7F800000u ? 254u : mx_scale_byte_from_f32bits(sb);
+  }
+  mul = mx_inv_scale(byte);
+}
+
 // ---------------------------------------------------------------------------
 // Tensor amax pass (NVFP4): largest finite |y| over the tensor, y the input
 // or its block rotation.  Each workgroup writes one partial (binary32 bits;
@@ -277,6 +292,7 @@ struct RowArgs {
   uint64_t seed;
   const float* st;        // NVFP4 tensor scale (device), written by the finalize kernel
   double* parts;          // STATS: 3 binary64 sums per workgroup of the launch
+  float alpha;            // GRID: the fixed grid scale
 };
 
 // LOAD bit 0: element loads (the input is not 16-byte aligned), else 16-byte
@@ -284,7 +300,8 @@ struct RowArgs {
 // division; else the slice is contiguous.
 // STATS: also the signal and noise sums of the operand (noise_accum8; blocks
 // with a NaN scale byte counted as left out), one triple per workgroup.
-template <int FMT, int RND, bool HAD, int LOAD, bool STATS = false>
+// GRID: MXFP4 round-to-nearest with the fixed grid scale a.alpha.
+template <int FMT, int RND, bool HAD, int LOAD, bool STATS = false, bool GRID = false>
 __global__ void __launch_bounds__(256) quant_rows_kernel(RowArgs a) {
   constexpr int LPB = (FMT == FMT_MX) ? 4 : 2;   // lanes per scale block
   constexpr int U = kRowChunksPerWG / 256;
@@ -339,7 +356,8 @@ __global__ void __launch_bounds__(256) quant_rows_kernel(RowArgs a) {
     uint32_t byte;
     float mul;
     bool nonfinite;
-    block_scale<FMT>(amax_bits, st, byte, mul, nonfinite);
+    if constexpr (GRID) grid_block_scale(amax_bits, a.alpha, byte, mul, nonfinite);
+    else block_scale<FMT>(amax_bits, st, byte, mul, nonfinite);
     uint32_t rw[4] = {0, 0, 0, 0};
     if (RND == RND_SR && !nonfinite) {
       const uint64_t g = a.tbase + t;      // = output index / 8
@@ -377,9 +395,10 @@ struct ColArgs {
   uint64_t seed;
   const float* st;
   double* parts;          // STATS (tile kernel): 3 binary64 sums per workgroup of the launch
+  float alpha;            // GRID (tile kernel): the fixed grid scale
 };
 
-template <int FMT, int RND, bool HAD, bool STATS = false>
+template <int FMT, int RND, bool HAD, bool STATS = false, bool GRID = false>
 __global__ void __launch_bounds__(256) quant_cols_tile_kernel(ColArgs a) {
   constexpr int BS = (FMT == FMT_MX) ? 32 : 16;
   __shared__ __attribute__((aligned(16))) uint16_t tile[256 * 64];   // 32 KB
@@ -437,7 +456,8 @@ __global__ void __launch_bounds__(256) quant_cols_tile_kernel(ColArgs a) {
       uint32_t byte;
       float mul;
       bool nonfinite;
-      block_scale<FMT>(m, st, byte, mul, nonfinite);
+      if constexpr (GRID) grid_block_scale(m, a.alpha, byte, mul, nonfinite);
+      else block_scale<FMT>(m, st, byte, mul, nonfinite);
 #pragma unroll
       for (int j2 = 0; j2 < BS / 8; j2++) {
         const int e0 = b * BS + j2 * 8;
@@ -590,22 +610,23 @@ static int grid_for(int64_t work_items, int per_block, int64_t cap) {
 
 // Each launcher returns the number of workgroups it launched (the STATS
 // partial triples it wrote); with launch = false it only counts them.
-template <int FMT, int RND, bool HAD, bool STATS>
+template <int FMT, int RND, bool HAD, bool STATS, bool GRID = false>
 static int64_t launch_rows(const RowArgs& a, int load, bool launch, hipStream_t s) {
   const int grid = (int)(((uint64_t)a.total + kRowChunksPerWG - 1) / kRowChunksPerWG);
   if (!launch) return grid;
   switch (load) {
-    case 0: hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, 0, STATS>), dim3(grid), dim3(256), 0, s, a); break;
-    case 1: hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, 1, STATS>), dim3(grid), dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, 2, STATS>), dim3(grid), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, 3, STATS>), dim3(grid), dim3(256), 0, s, a); break;
+    case 0: hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, 0, STATS, GRID>), dim3(grid), dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, 1, STATS, GRID>), dim3(grid), dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, 2, STATS, GRID>), dim3(grid), dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((quant_rows_kernel<FMT, RND, HAD, 3, STATS, GRID>), dim3(grid), dim3(256), 0, s, a); break;
   }
   return grid;
 }
 
 // STATS only with the tiled kernel (the caller sends the other inputs
 // through quantize, then the separate noise pass).
-template <int FMT, int RND, bool HAD, bool STATS>
+// GRID only with the tiled kernel (the caller checks).
+template <int FMT, int RND, bool HAD, bool STATS, bool GRID = false>
 static int64_t launch_cols(ColArgs a, bool tiled, bool vec, bool launch, hipStream_t s) {
   // grid.y is limited to 65535: larger inputs go in slabs of rows
   const int64_t rows_per = tiled ? 256 : 128;
@@ -617,9 +638,11 @@ static int64_t launch_cols(ColArgs a, bool tiled, bool vec, bool launch, hipStre
     const int64_t cols_per = tiled ? 64 : 128;
     dim3 grid((unsigned)((a.C + cols_per - 1) / cols_per), (unsigned)((nr + rows_per - 1) / rows_per));
     if (launch) {
-      if (tiled) hipLaunchKernelGGL((quant_cols_tile_kernel<FMT, RND, HAD, STATS>), grid, dim3(256), 0, s, a);
-      else if (vec) hipLaunchKernelGGL((quant_cols_kernel<FMT, RND, HAD, true>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((quant_cols_kernel<FMT, RND, HAD, false>), grid, dim3(256), 0, s, a);
+      if (tiled) hipLaunchKernelGGL((quant_cols_tile_kernel<FMT, RND, HAD, STATS, GRID>), grid, dim3(256), 0, s, a);
+      else if constexpr (!GRID) {
+        if (vec) hipLaunchKernelGGL((quant_cols_kernel<FMT, RND, HAD, true>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((quant_cols_kernel<FMT, RND, HAD, false>), grid, dim3(256), 0, s, a);
+      }
     }
     const int64_t wgs = (int64_t)grid.x * grid.y;
     n += wgs;
@@ -631,10 +654,10 @@ static int64_t launch_cols(ColArgs a, bool tiled, bool vec, bool launch, hipStre
 // Chunk ranges of one launch stay below 2^31 so the kernels index in 32 bits.
 constexpr uint64_t kSliceChunks = (uint64_t)1 << 30;
 
-template <int FMT, int RND, bool HAD, bool STATS>
+template <int FMT, int RND, bool HAD, bool STATS, bool GRID = false>
 static int64_t launch_rows_sliced(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, bool aligned16,
                                   uint64_t seed, uint8_t* codes, uint8_t* scales, const float* st, double* parts,
-                                  bool launch, hipStream_t s) {
+                                  bool launch, hipStream_t s, float alpha = 1.0f) {
   constexpr int LPB = (FMT == FMT_MX) ? 4 : 2;
   const uint64_t cpr = (uint64_t)C / 8;
   RowArgs a{};
@@ -642,9 +665,10 @@ static int64_t launch_rows_sliced(const uint16_t* x, int64_t R, int64_t C, int64
   a.seed = seed;
   a.st = st;
   a.parts = parts;
+  a.alpha = alpha;
   int64_t n = 0;
   auto go = [&](int load) {
-    const int64_t g = launch_rows<FMT, RND, HAD, STATS>(a, load, launch, s);
+    const int64_t g = launch_rows<FMT, RND, HAD, STATS, GRID>(a, load, launch, s);
     n += g;
     if (STATS && a.parts) a.parts += 3 * g;   // (null when only counting)
   };
@@ -688,7 +712,7 @@ static int64_t launch_one(int axis, const uint16_t* x, int64_t R, int64_t C, int
   const bool aligned16 = (((uintptr_t)x & 15u) == 0) && (ldx % 8 == 0);
   if (axis == 1)
     return launch_rows_sliced<FMT, RND, HAD, STATS>(x, R, C, ldx, aligned16, seed, codes, scales, st, parts, true, s);
-  ColArgs ca{x, R, C, ldx, 0, codes, scales, seed, st, parts};
+  ColArgs ca{x, R, C, ldx, 0, codes, scales, seed, st, parts, 1.0f};
   const bool tiled = aligned16 && (C % 8 == 0);
   const bool vec = (((uintptr_t)x & 3u) == 0) && (ldx % 2 == 0);
   return launch_cols<FMT, RND, HAD, STATS>(ca, tiled, vec, true, s);
@@ -739,6 +763,30 @@ void launch_tensor_scale(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, i
     }
   }
   hipLaunchKernelGGL(amax_finalize_kernel, dim3(1), dim3(1024), 0, s, partials, nparts, tensor_scale);
+}
+
+// MXFP4 with a fixed grid scale through the row and tiled transposing
+// quantizers (the block kernel of mse.hip covers the rest); false when the
+// input takes neither.
+template <bool HAD>
+static bool launch_grid_fast_t(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int axis, float alpha,
+                               uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  const bool aligned16 = (((uintptr_t)x & 15u) == 0) && (ldx % 8 == 0);
+  if (axis == 1) {
+    launch_rows_sliced<FMT_MX, RND_RTN, HAD, false, true>(x, R, C, ldx, aligned16, 0, codes, scales, nullptr,
+                                                          nullptr, true, s, alpha);
+    return true;
+  }
+  if (!(aligned16 && C % 8 == 0)) return false;
+  ColArgs ca{x, R, C, ldx, 0, codes, scales, 0, nullptr, nullptr, alpha};
+  launch_cols<FMT_MX, RND_RTN, HAD, false, true>(ca, true, true, true, s);
+  return true;
+}
+
+bool launch_quantize_grid_fast(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int hadamard, int axis,
+                               float alpha, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  if (hadamard) return launch_grid_fast_t<true>(x, R, C, ldx, axis, alpha, codes, scales, s);
+  return launch_grid_fast_t<false>(x, R, C, ldx, axis, alpha, codes, scales, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -904,7 +952,7 @@ int64_t quantize_noise_parts(int fmt, int hadamard, int64_t R, int64_t C, int ax
                                                                       nullptr, nullptr, nullptr, false, nullptr);
     n = a > b ? a : b;
   } else {
-    ColArgs ca{nullptr, R, C, C, 0, nullptr, nullptr, 0, nullptr, nullptr};
+    ColArgs ca{nullptr, R, C, C, 0, nullptr, nullptr, 0, nullptr, nullptr, 1.0f};
     const int64_t a = launch_cols<FMT_MX, RND_RTN, false, true>(ca, true, true, false, nullptr);
     const int64_t b = (int64_t)(noise_workspace_bytes(fmt, hadamard, C, R) / (3 * sizeof(double)));
     n = a > b ? a : b;

@@ -30,3 +30,24 @@ def test_grid_full_size_weight(oracle_mod):
     say("grid full size", W.shape)
     q = q_to_host(mx.mxfp4_quantize_grid(to_device_bf16(W), 0.75, True, 1))
     assert_codes_equal(q, oracle_mod.quantize_grid(W, 0.75, True, 1), "grid config 3 W_down")
+
+
+@pytest.mark.parametrize("axis", [1, 0])
+def test_grid_unaligned_and_overflowing_blocks(oracle_mod, axis):
+    """An input view one element off 16-byte alignment (the transposing path
+    then takes the block kernel, the row path its element loads), and blocks
+    whose alpha * absmax overflows binary32 (scale byte 254)."""
+    mx = need_gpu()
+    import torch
+    X = workloads.small_t_bf16((96, 128), 3.0, seed=141).copy()
+    X[3, 0:32] = 0x7F7F            # the largest finite bf16: 1.5 * absmax overflows
+    X[40:72, 5] = 0xFF7F           # a column block of the same magnitude (axis 0)
+    full = np.zeros((96, 128 + 8), dtype=np.uint16)
+    full[:, 1:129] = X
+    xt = torch.from_numpy(full.view(np.int16)).view(torch.bfloat16).cuda()[:, 1:129]
+    for alpha in (1.5, 0.75):
+        say("grid unaligned", axis, alpha)
+        q = q_to_host(mx.mxfp4_quantize_grid(xt, alpha, False, axis))
+        assert_codes_equal(q, oracle_mod.quantize_grid(X, alpha, False, axis), f"grid unaligned {axis} {alpha}")
+    if axis == 1:
+        assert 254 in q_to_host(mx.mxfp4_quantize_grid(xt, 1.5, False, axis))[1]
