@@ -69,6 +69,12 @@ void launch_tensor_scale(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, i
 bool launch_quantize_grid_fast(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int hadamard, int axis,
                                float alpha, uint8_t* codes, uint8_t* scales, hipStream_t s);
 
+// MXFP4 round-to-nearest with MSE-fitted block scales, transposed (axis 0),
+// through the tiled transposing quantizer; false (nothing launched) when the
+// input is not that kernel's (axis 1, or unaligned).
+bool launch_quantize_mse_mx_fast(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int hadamard, int axis,
+                                 uint8_t* codes, uint8_t* scales, hipStream_t s);
+
 // Round-to-nearest quantization with MSE-fitted scales (mse.hip).
 size_t quantize_mse_workspace_bytes(int fmt, int hadamard, int64_t R, int64_t C, int axis);
 hipError_t launch_quantize_mse(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int fmt, int hadamard,

@@ -28,6 +28,7 @@
 // STATS instantiations of the row and tiled kernels also add the signal and
 // quantization-noise sums of the operand (mxfp4_quantize_noise).
 #include "fp4_device.h"
+#include "mse_device.h"
 #include "mxfp4_internal.h"
 
 namespace mxfp4 {
@@ -398,7 +399,9 @@ struct ColArgs {
   float alpha;            // GRID (tile kernel): the fixed grid scale
 };
 
-template <int FMT, int RND, bool HAD, bool STATS = false, bool GRID = false>
+// GRID: MXFP4 with the fixed grid scale a.alpha.  MSE: MXFP4 with the
+// MSE-fitted block scale (mse_block of mse_device.h on the lane's block).
+template <int FMT, int RND, bool HAD, bool STATS = false, bool GRID = false, bool MSE = false>
 __global__ void __launch_bounds__(256) quant_cols_tile_kernel(ColArgs a) {
   constexpr int BS = (FMT == FMT_MX) ? 32 : 16;
   __shared__ __attribute__((aligned(16))) uint16_t tile[256 * 64];   // 32 KB
@@ -448,6 +451,10 @@ __global__ void __launch_bounds__(256) quant_cols_tile_kernel(ColArgs a) {
 #pragma unroll
     for (int j = 0; j < 32; j++) y[j] = __uint_as_float((uint32_t)tile[(64 * w + 32 * h + j) * 64 + l] << 16);
     if (HAD) fwht32_inlane(y);
+    if constexpr (MSE) {             // MXFP4: the half is one block, the lane holds it
+      sbyte[h][0] = mse_block<FMT_MX, 32>(y, 1.0f, out[h]);
+      continue;
+    }
 #pragma unroll
     for (int b = 0; b < 32 / BS; b++) {
       uint32_t m = 0;
@@ -625,8 +632,8 @@ static int64_t launch_rows(const RowArgs& a, int load, bool launch, hipStream_t 
 
 // STATS only with the tiled kernel (the caller sends the other inputs
 // through quantize, then the separate noise pass).
-// GRID only with the tiled kernel (the caller checks).
-template <int FMT, int RND, bool HAD, bool STATS, bool GRID = false>
+// GRID and MSE only with the tiled kernel (the caller checks).
+template <int FMT, int RND, bool HAD, bool STATS, bool GRID = false, bool MSE = false>
 static int64_t launch_cols(ColArgs a, bool tiled, bool vec, bool launch, hipStream_t s) {
   // grid.y is limited to 65535: larger inputs go in slabs of rows
   const int64_t rows_per = tiled ? 256 : 128;
@@ -638,8 +645,8 @@ static int64_t launch_cols(ColArgs a, bool tiled, bool vec, bool launch, hipStre
     const int64_t cols_per = tiled ? 64 : 128;
     dim3 grid((unsigned)((a.C + cols_per - 1) / cols_per), (unsigned)((nr + rows_per - 1) / rows_per));
     if (launch) {
-      if (tiled) hipLaunchKernelGGL((quant_cols_tile_kernel<FMT, RND, HAD, STATS, GRID>), grid, dim3(256), 0, s, a);
-      else if constexpr (!GRID) {
+      if (tiled) hipLaunchKernelGGL((quant_cols_tile_kernel<FMT, RND, HAD, STATS, GRID, MSE>), grid, dim3(256), 0, s, a);
+      else if constexpr (!GRID && !MSE) {
         if (vec) hipLaunchKernelGGL((quant_cols_kernel<FMT, RND, HAD, true>), grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL((quant_cols_kernel<FMT, RND, HAD, false>), grid, dim3(256), 0, s, a);
       }
@@ -787,6 +794,29 @@ bool launch_quantize_grid_fast(const uint16_t* x, int64_t R, int64_t C, int64_t 
                                float alpha, uint8_t* codes, uint8_t* scales, hipStream_t s) {
   if (hadamard) return launch_grid_fast_t<true>(x, R, C, ldx, axis, alpha, codes, scales, s);
   return launch_grid_fast_t<false>(x, R, C, ldx, axis, alpha, codes, scales, s);
+}
+
+// MXFP4 with MSE-fitted block scales, transposed (axis 0), through the tiled
+// transposing quantizer: the block kernel of mse.hip reads a column block
+// element by element, the tile kernel stages it through LDS with full-line
+// loads (same block step, same bits).  Along rows the block kernel already
+// reads whole lines and is bound by its binary64 arithmetic: a quad-of-lanes
+// version in the row quantizer measured the same 44 us on a config-3 weight.
+// False when the input is not the tiled kernel's.
+template <bool HAD>
+static bool launch_mse_fast_t(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int axis, uint8_t* codes,
+                              uint8_t* scales, hipStream_t s) {
+  const bool aligned16 = (((uintptr_t)x & 15u) == 0) && (ldx % 8 == 0);
+  if (axis == 1 || !(aligned16 && C % 8 == 0)) return false;
+  ColArgs ca{x, R, C, ldx, 0, codes, scales, 0, nullptr, nullptr, 1.0f};
+  launch_cols<FMT_MX, RND_RTN, HAD, false, false, true>(ca, true, true, true, s);
+  return true;
+}
+
+bool launch_quantize_mse_mx_fast(const uint16_t* x, int64_t R, int64_t C, int64_t ldx, int hadamard, int axis,
+                                 uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  if (hadamard) return launch_mse_fast_t<true>(x, R, C, ldx, axis, codes, scales, s);
+  return launch_mse_fast_t<false>(x, R, C, ldx, axis, codes, scales, s);
 }
 
 // ---------------------------------------------------------------------------
