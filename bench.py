@@ -641,8 +641,9 @@ def sweep(args):
                              "GB/s", "hbm", gbps_f / PEAK_HBM_GBPS))
                 del st, ws, qf, fws
         if cfg == 3:
-            # decode with the activation quantization fused into the GEMM,
-            # against the two launches it replaces (quantize, then GEMM)
+            # the decode linear layer through mxfp4_quantize_gemm (for these
+            # shapes: the activations quantized into the workspace, then the
+            # decode GEMM), against the same two calls made separately
             for gname, xname, wname in (("decode up", "x_dec_up", "W_up"), ("decode down", "x_dec_down", "W_down")):
                 x, qw, qx = tens[xname], qs[(wname, "rtn", 1)], qs[(xname, "rtn", 1)]
                 Mg, Kg = x.shape
@@ -661,7 +662,7 @@ def sweep(args):
                     mx.mxfp4_quantize(x, fmt, "rtn", had, 1, 7, out=qx)
                     mx.mxfp4_gemm(qx, qw, out=C, workspace=gws)
                 t_2 = timed(two, False)
-                for label, t in (("fused", t_f), ("two launches", t_2)):
+                for label, t in (("quantize_gemm", t_f), ("quantize, then gemm", t_2)):
                     rows.append((cfg, "quantize+gemm", f"{gname} ({label})", f"{Mg}x{Ng}x{Kg}", t * 1e6,
                                  flops / t / 1e12, "TFLOP/s", bound, bound_t / t))
                 del C, ws, gws

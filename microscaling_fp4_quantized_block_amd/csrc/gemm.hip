@@ -1110,6 +1110,210 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_fused_kernel(GemmArgs p) {
   mx_tile<TM, 2, 1, OUT, true, HAD>(p, smem, 0, (int64_t)blockIdx.x * 256, kt0, kt1, Cz);
 }
 
+// Decode-shaped MXFP4 GEMM (M <= 32 activation rows against a long weight):
+// the weights stream from HBM once, so the kernel is built for bytes in
+// flight rather than MFMA rate.  A workgroup owns 16 output columns (weight
+// rows) over the whole contraction; its NW waves take contiguous ranges of
+// rounds (four 128-wide steps each), and the per-wave sums are added in LDS in
+// wave order: no split-K workspace and no second launch.
+//
+// One step is v_mfma_scale_f32_16x16x128_f8f6f4 with the weights as the
+// first operand: lane l holds block 4s + l / 16 of weight row n0 + l % 16
+// (16 code bytes) and that block's scale byte, and the same block of
+// activation row 16t + l % 16 (TMR = 1 or 2 tiles of 16 rows); the output
+// lane l holds is C[16t + l % 16][n0 + 4 (l / 16) + v], v = 0..3.
+//
+// That operand layout gives each row only 64 bytes per load instruction,
+// and half-line loads stream at about half the rate of whole 128-byte lines
+// (measured on the configuration-3 decode shapes), so codes travel through
+// LDS: each wave owns R slots of one step pair (16 weight rows and 16 TMR
+// activation rows, 128 bytes each) filled by buffer->LDS loads of whole
+// lines (8 rows x 128 bytes per instruction, chunk c of row q stored at
+// position c ^ ((q >> 1) & 7), which keeps the fragment reads free of bank
+// conflicts), and reads its fragments back from its own slots, so no barrier
+// is needed.  Scale bytes come straight to registers, 16 bytes (one round)
+// per lane and operand.  Rows past M or N read as zeros through the buffer
+// resources and are not stored; code chunks past K are loaded as zeros and
+// the scale bytes of steps past K are cleared, so those products vanish.
+constexpr uint32_t kOutOfRange = 0x80000000u;   // a buffer offset past every operand the kernel reads
+#ifndef MXFP4_DECODE_NW
+#define MXFP4_DECODE_NW 4     // waves per workgroup, each on its own range of the contraction
+#endif
+
+// TMR activation tiles and TN weight tiles of 16 rows (16 TN output columns
+// per workgroup); R slots per wave (R / 2 rounds in flight).
+template <int TMR, int TN, int R>
+struct DecodeShape {
+  static constexpr int ROWS = 16 * (TN + TMR);    // slot rows: 16 TN weight rows, then 16 TMR activation rows
+  static constexpr int SLOT = ROWS * 128;
+  static constexpr int LDS = MXFP4_DECODE_NW * R * SLOT;
+};
+
+template <int TMR, int TN, int R, int OUT>
+__global__ void __launch_bounds__(64 * MXFP4_DECODE_NW) gemm_mx_decode_kernel(GemmArgs p) {
+  static_assert(OUT == OUT_F32 || OUT == OUT_BF16, "the decode kernel writes C directly");
+  static_assert(R % 2 == 0 && R >= 2, "slots come in rounds of two");
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  typedef DecodeShape<TMR, TN, R> Shape;
+  constexpr int NW = MXFP4_DECODE_NW;
+  constexpr int SLOT = Shape::SLOT;
+  constexpr int NDMA = Shape::ROWS / 8;         // buffer->LDS loads per slot
+  constexpr int NB = 2 * TN;                    // the first NB of them move weight rows
+  constexpr int RQ = R / 2;                     // rounds in flight
+  constexpr int VM_ROUND = 2 * NDMA + TN + TMR; // vector memory operations issued per round
+  static_assert(NW * TMR * TN * 64 * 16 <= Shape::LDS, "the wave sums reuse the slots");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Shape::LDS];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63, r = l & 15, g = l >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * (16 * TN);
+  const int64_t krow = p.K / 2, srow = p.K / 32;
+  const int steps = (int)(p.K / 128);
+  const int rounds = (steps + 3) >> 2;
+  const int c0 = (int)((int64_t)rounds * w / NW), c1 = (int)((int64_t)rounds * (w + 1) / NW);
+  const int64_t nb = p.N - n0 < 16 * TN ? p.N - n0 : 16 * TN;
+  const __amdgpu_buffer_rsrc_t bc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.b + n0 * krow), (short)0, (int)(nb * krow), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t bs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.bs + n0 * srow), (short)0, (int)(nb * srow), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t ac =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.a, (short)0, (int)(p.M * krow), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t as =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.as, (short)0, (int)(p.M * srow), kRsrcWord3);
+  uint8_t* const ring = smem + w * (R * SLOT);
+
+  // buffer->LDS load h of a slot moves slot rows 8h .. 8h + 7; lane l fills
+  // position l & 7 of row q = 8h + (l >> 3) with global chunk ch[h & 1] of it
+  // (the swizzle (q >> 1) & 7 depends on h & 1 only)
+  uint32_t ch[2], rowoff[NDMA];
+#pragma unroll
+  for (int e = 0; e < 2; e++) ch[e] = (uint32_t)((l & 7) ^ ((4 * e + (l >> 4)) & 7));
+#pragma unroll
+  for (int h = 0; h < NDMA; h++) {
+    const int q = 8 * h + (l >> 3);              // slot row
+    rowoff[h] = (uint32_t)((h < NB ? q : q - 16 * TN) * krow);   // row within its operand
+  }
+  // fragment position of step u (0, 1) of a slot in this lane's rows (all
+  // fragment rows are 16 apart, so they share the swizzle of row r)
+  const uint32_t pos0 = (uint32_t)(16 * (g ^ ((r >> 1) & 7)));
+  const uint32_t pos1 = (uint32_t)(16 * ((4 + g) ^ ((r >> 1) & 7)));
+  const uint32_t sq = (uint32_t)(r * srow), sq16 = (uint32_t)(16 * srow);
+  const int shift = 8 * g;
+
+  v4f acc[TMR][TN];
+#pragma unroll
+  for (int t = 0; t < TMR; t++)
+#pragma unroll
+    for (int j = 0; j < TN; j++) acc[t][j] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+  v4i bsc[RQ][TN], asc[RQ][TMR];
+
+  // round c into slots 2k, 2k + 1 and scale registers k; rounds past the
+  // wave's range read zeros (so their products vanish)
+  auto issue = [&](int k, int c) {
+    const bool live = c < c1;
+#pragma unroll
+    for (int e = 0; e < 2; e++) {
+      const int pair = 2 * c + e;
+      uint8_t* sl = ring + (2 * k + e) * SLOT;
+#pragma unroll
+      for (int h = 0; h < NDMA; h++) {
+        const uint32_t chunk = ch[h & 1];
+        const bool in = live && 2 * pair + (int)(chunk >> 2) < steps;
+        const uint32_t off = rowoff[h] + 16u * chunk + 128u * (uint32_t)pair;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(h < NB ? bc : ac, (lds_void*)(sl + h * 1024), 16,
+                                                 in ? off : kOutOfRange, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TN; j++)
+      bsc[k][j] = __builtin_amdgcn_raw_buffer_load_b128(bs, live ? sq + j * sq16 + 16u * (uint32_t)c : kOutOfRange,
+                                                        0, 0);
+#pragma unroll
+    for (int t = 0; t < TMR; t++)
+      asc[k][t] = __builtin_amdgcn_raw_buffer_load_b128(as, live ? sq + t * sq16 + 16u * (uint32_t)c : kOutOfRange,
+                                                        0, 0);
+  };
+#pragma unroll
+  for (int k = 0; k < RQ; k++) {
+    issue(k, c0 + k);
+    __builtin_amdgcn_sched_barrier(0);   // round order, as in the loop
+  }
+  for (int base = c0; base < c1; base += RQ) {
+#pragma unroll
+    for (int k = 0; k < RQ; k++) {
+      const int c = base + k;
+      wait_cnt<(RQ - 1) * VM_ROUND, 15>();       // this round's slots have landed
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const uint8_t* sl = ring + (2 * k + (u >> 1)) * SLOT;
+        const uint32_t pos = (u & 1) ? pos1 : pos0;
+        v4i fb[TN], fa[TMR];
+#pragma unroll
+        for (int j = 0; j < TN; j++) fb[j] = *(const v4i*)(sl + (16 * j + r) * 128 + pos);
+#pragma unroll
+        for (int t = 0; t < TMR; t++) fa[t] = *(const v4i*)(sl + (16 * TN + 16 * t + r) * 128 + pos);
+        // steps past K: scale byte 0 (their codes are zero), never a NaN byte from the next row
+        const bool ok = 4 * c + u < steps;
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+          const int sb = ok ? (int)((uint32_t)bsc[k][j][u] >> shift) : 0;
+          const v8i b8 = __builtin_shufflevector(fb[j], fb[j], 0, 1, 2, 3, -1, -1, -1, -1);
+#pragma unroll
+          for (int t = 0; t < TMR; t++) {
+            const int sa = ok ? (int)((uint32_t)asc[k][t][u] >> shift) : 0;
+            const v8i a8 = __builtin_shufflevector(fa[t], fa[t], 0, 1, 2, 3, -1, -1, -1, -1);
+            acc[t][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b8, a8, acc[t][j], 4, 4, 0, sb, 0, sa);
+          }
+        }
+      }
+      wait_cnt<63, 0>();                          // the slots' reads are done before they are refilled
+      asm volatile("" ::: "memory");
+      issue(k, c + RQ);
+      // keep the next round's scale shifts behind its own wait (the
+      // scheduler would hoist them here, waiting for every load in flight)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wait_cnt<0, 0>();   // nothing may still write LDS when the workgroup exits
+
+  // wave sums in wave order: ((w0 + w1) + w2) + ..., through the slots once
+  // every wave is done reading them
+  __syncthreads();
+  v4f(*red)[TMR][TN][64] = (v4f(*)[TMR][TN][64])smem;
+#pragma unroll
+  for (int t = 0; t < TMR; t++)
+#pragma unroll
+    for (int j = 0; j < TN; j++) red[w][t][j][l] = acc[t][j];
+  __syncthreads();
+  if (w != 0) return;
+  typedef typename std::conditional<OUT == OUT_BF16, __bf16, float>::type T;
+#pragma unroll
+  for (int t = 0; t < TMR; t++) {
+    const int64_t m = 16 * t + r;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < TN; j++) {
+      v4f s = red[0][t][j][l];
+#pragma unroll
+      for (int q = 1; q < NW; q++) s += red[q][t][j][l];
+      const int64_t n = n0 + 16 * j + 4 * g;
+      T* dst = (T*)p.C + m * p.ldc + n;
+      if (n + 4 <= p.N && (((uintptr_t)dst) & (4 * sizeof(T) - 1)) == 0) {
+        if constexpr (OUT == OUT_BF16) {
+          typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+          *(bf16x4_t*)dst = (bf16x4_t){(__bf16)s[0], (__bf16)s[1], (__bf16)s[2], (__bf16)s[3]};
+        } else {
+          __builtin_nontemporal_store(s, (v4f*)dst);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; v++)
+          if (n + v < p.N) dst[v] = (T)s[v];
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // NVFP4
 // ---------------------------------------------------------------------------
@@ -1284,6 +1488,13 @@ GemmPlan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
   pl.k_tiles = (K + (mx ? MX_BK : BK) - 1) / (mx ? MX_BK : BK);
   pl.narrow_tm = 0;
   pl.waves8 = 0;
+  pl.decode = 0;
+  if (mx && M <= 32 && N >= MXFP4_DECODE_MIN_N) {
+    // decode shapes: 16-column workgroups over the whole contraction
+    pl.decode = M <= 16 ? 1 : 2;
+    pl.splits = 1;
+    return pl;
+  }
   if (mx && M <= 128) {
     // narrow tiles (32 TM x 256), split along K (in stage pairs) into at most
     // one workgroup per compute unit, each split at least two pairs long
@@ -1329,11 +1540,52 @@ static int compute_units() {
   return cache[dev];
 }
 
+// Decode launch: one workgroup per 16 TN weight rows.  Two weight tiles per
+// workgroup halve the activation bytes each weight byte brings through L2
+// when that still leaves at least 256 workgroups; contractions of at most two
+// rounds per wave take R = 2 (more workgroups resident, one round in flight
+// each), longer ones the most slots that fit.
+template <int TMR, int TN, int R, int OUT>
+static void launch_decode_kernel(const GemmArgs& p, hipStream_t stream) {
+  static_assert(DecodeShape<TMR, TN, R>::LDS <= 160 * 1024, "LDS");
+  const dim3 grid((unsigned)((p.N + 16 * TN - 1) / (16 * TN)));
+  hipLaunchKernelGGL((gemm_mx_decode_kernel<TMR, TN, R, OUT>), grid, dim3(64 * MXFP4_DECODE_NW), 0, stream, p);
+}
+
+#ifndef MXFP4_DECODE_R11
+#define MXFP4_DECODE_R11 4
+#endif
+template <int OUT>
+static void launch_decode(const GemmArgs& p, const GemmPlan& plan, hipStream_t stream) {
+  const int64_t rounds = (p.K / 128 + 3) / 4;
+  const bool short_k = rounds <= 2 * MXFP4_DECODE_NW;
+  const bool tn2 = p.N >= MXFP4_DECODE_TN2_MIN_N;
+  if (plan.decode == 1) {
+    if (tn2) {
+      if (short_k) launch_decode_kernel<1, 2, 2, OUT>(p, stream);
+      else launch_decode_kernel<1, 2, 4, OUT>(p, stream);
+    } else {
+      if (short_k) launch_decode_kernel<1, 1, 2, OUT>(p, stream);
+      else launch_decode_kernel<1, 1, MXFP4_DECODE_R11, OUT>(p, stream);
+    }
+  } else {
+    if (tn2) {
+      if (short_k) launch_decode_kernel<2, 2, 2, OUT>(p, stream);
+      else launch_decode_kernel<2, 2, 4, OUT>(p, stream);
+    } else {
+      if (short_k) launch_decode_kernel<2, 1, 2, OUT>(p, stream);
+      else launch_decode_kernel<2, 1, 4, OUT>(p, stream);
+    }
+  }
+}
+
 template <int OUT>
 static void launch_gemm_kernel(bool nv, const GemmArgs& p, const GemmPlan& plan, int fused_had, dim3 grid,
                                dim3 ngrid, hipStream_t stream) {
   if (nv) {
     if constexpr (OUT != OUT_MXQ) hipLaunchKernelGGL(gemm_nv_kernel<OUT>, grid, dim3(256), 0, stream, p);
+  } else if (plan.decode) {
+    if constexpr (OUT == OUT_F32 || OUT == OUT_BF16) launch_decode<OUT>(p, plan, stream);
   } else if (plan.narrow_tm && fused_had >= 0) {
     // fused plans have 32-row tiles (fused_plan_ok)
     if (fused_had) hipLaunchKernelGGL((gemm_mx_fused_kernel<1, true, OUT>), ngrid, dim3(256), 0, stream, p);
@@ -1370,7 +1622,7 @@ static hipError_t launch_gemm_common(bool nv, GemmArgs p, void* C, int64_t ldc, 
   }
   p.rem = 0;
   const int64_t tiles = (int64_t)p.ntm * p.ntn;
-  if (!nv && plan.splits == 1 && !plan.narrow_tm) {
+  if (!nv && plan.splits == 1 && !plan.narrow_tm && !plan.decode) {
     const int64_t cus = compute_units();
     if (tiles > cus && tiles % cus != 0) p.rem = (int)(tiles % cus);
   }

@@ -303,7 +303,7 @@ static size_t align16_bytes(size_t n) { return (n + 15) & ~(size_t)15; }
 
 static size_t gemm_quantize_ws(const mxfp4_tensor* A, const mxfp4_tensor* B, bool* fused) {
   const mxfp4::GemmPlan pl = mxfp4::plan_gemm(A->fmt, A->rows, B->rows, A->k);
-  *fused = A->fmt == MXFP4_FMT_MX && pl.splits == 1;
+  *fused = A->fmt == MXFP4_FMT_MX && pl.splits == 1 && !pl.decode;
   if (*fused) return 0;
   const size_t gemm_ws = pl.splits > 1 ? (size_t)pl.splits * (size_t)A->rows * (size_t)B->rows * sizeof(float) : 0;
   return align16_bytes((size_t)A->rows * (size_t)B->rows * 2) + gemm_ws;

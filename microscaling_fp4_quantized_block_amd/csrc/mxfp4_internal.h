@@ -30,7 +30,16 @@ struct GemmPlan {
   int64_t k_tiles;     // contraction tiles of the kernel's K step
   int narrow_tm;       // MXFP4 with M <= 128: rows per narrow tile / 32 (1, 2 or 4); 0 = wide tiles
   int waves8;          // MXFP4 wide tiles with at most four stages: the 8-wave kernel
+  int decode;          // MXFP4 with M <= 32 against a long weight: gemm_mx_decode_kernel with 16-row A tiles (1 or 2)
 };
+// weights of at least this many rows take the decode kernel when M <= 32
+#ifndef MXFP4_DECODE_MIN_N
+#define MXFP4_DECODE_MIN_N 2048
+#endif
+// and from this many, two 16-row weight tiles per workgroup
+#ifndef MXFP4_DECODE_TN2_MIN_N
+#define MXFP4_DECODE_TN2_MIN_N 8192
+#endif
 GemmPlan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K);
 
 // C: fp32, or bf16 (round to nearest even from the fp32 result) when c_bf16.

@@ -54,7 +54,20 @@ def assert_codes_equal(got, want, what=""):
 
 
 def assert_gemm_within(Cg: np.ndarray, Co: np.ndarray, So: np.ndarray, what="", tol=1e-5):
-    err = np.abs(Cg.astype(np.float64) - Co)
+    # NaN and infinite results must sit where the oracle has them (a bare
+    # |difference| comparison would let NaN through)
+    Cg = Cg.astype(np.float64)
+    ng, no = np.isnan(Cg), np.isnan(Co)
+    if not np.array_equal(ng, no):
+        i = np.argwhere(ng != no)[0]
+        raise AssertionError(f"{what}: NaN positions differ; first {i.tolist()}: gpu {Cg[tuple(i)]!r} "
+                             f"oracle {Co[tuple(i)]!r}")
+    inf = np.isinf(Cg) | np.isinf(Co)
+    if not np.array_equal(Cg[inf], Co[inf]):
+        raise AssertionError(f"{what}: infinite results differ from the oracle's")
+    special = ng | inf
+    Cg, Co, So = np.where(special, 0.0, Cg), np.where(special, 0.0, Co), np.where(special, 0.0, So)
+    err = np.abs(Cg - Co)
     bound = tol * So
     bad = err > bound
     if bad.any():

@@ -253,24 +253,27 @@ def test_quantize_gemm_rejects_bad_arguments(mx):
     assert qgemm(mx, C=None) == INVALID
     assert qgemm(mx, B=desc(mx, rows=64, codes=FAKE + 8)) == INVALID    # weight codes must be 16-byte aligned
     assert qgemm(mx, M=0) == OK                                          # empty output: no-op
-    # a decode shape with a split contraction needs its workspace
+    # a decode shape needs its workspace (the quantized activations)
     B = desc(mx, rows=14336, k=4096)
     assert qgemm(mx, M=16, K=4096, ldx=4096, B=B, ldc=14336) == WORKSPACE
 
 
 def test_quantize_gemm_workspace_bytes(mx):
-    # decode 16 x 14336 x 4096: fused into the narrow GEMM (56 column tiles,
-    # 8 stage pairs -> 4 splits of 2 pairs); only the split partial sums
-    assert qgemm_ws(mx, 16, 4096, 0, desc(mx, rows=14336, k=4096)) == (OK, 4 * 16 * 14336 * 4)
-    assert qgemm_ws(mx, 16, 4096, 1, desc(mx, had=1, rows=14336, k=4096)) == (OK, 4 * 16 * 14336 * 4)
+    # decode 16 x 14336 x 4096 and 16 x 4096 x 14336 (at most 32 rows against
+    # at least 2048 weight rows): quantized into the workspace (codes and
+    # scales, 16-byte padded), then the decode GEMM, which needs no workspace
+    assert qgemm_ws(mx, 16, 4096, 0, desc(mx, rows=14336, k=4096)) == (OK, 16 * 2048 + 16 * 128)
+    assert qgemm_ws(mx, 16, 4096, 1, desc(mx, had=1, rows=14336, k=4096)) == (OK, 16 * 2048 + 16 * 128)
+    assert qgemm_ws(mx, 16, 14336, 1, desc(mx, had=1, rows=4096, k=14336)) == (OK, 16 * 7168 + 16 * 448)
     # wide activations: quantized codes and scales (16-byte padded), no split
     assert qgemm_ws(mx, 300, 1024, 0, desc(mx, rows=512, k=1024)) == (OK, 300 * 512 + 300 * 32)
     # a narrow plan whose splits are too long for LDS (128 rows -> 4 stages
     # per split at most; 256 column tiles leave one split of 32 stages): two
     # steps, codes + scales, no split partials
     assert qgemm_ws(mx, 128, 8192, 0, desc(mx, rows=65536, k=8192)) == (OK, 128 * 4096 + 128 * 256)
-    # 16 column tiles over 28 stage pairs: 14 splits of 2 pairs, fused
-    assert qgemm_ws(mx, 16, 14336, 1, desc(mx, had=1, rows=4096, k=14336)) == (OK, 14 * 16 * 4096 * 4)
+    # 16 rows against 1024 weight rows: fused into the narrow GEMM, 4 column
+    # tiles over 16 stage pairs -> 8 splits of 2 pairs; only the split partial sums
+    assert qgemm_ws(mx, 16, 8192, 1, desc(mx, had=1, rows=1024, k=8192)) == (OK, 8 * 16 * 1024 * 4)
     assert qgemm_ws(mx, 16, 4096, 0, desc(mx, fmt=1, rows=64, k=4096))[0] == MISMATCH
 
 

@@ -1,11 +1,12 @@
 """GPU parity of the online-activation-quantization GEMM (mxfp4_quantize_gemm):
 its result must equal mxfp4_quantize followed by mxfp4_gemm bit for bit (same
 codes, same scale bytes, same products in the same order), and the oracle
-within 1e-5 * sum|ab|.  Covers the fused narrow path (M <= 32, with and
-without the block Hadamard, ragged M and N, contractions ending mid-stage,
-long split contractions, unaligned and padded inputs, NaN blocks) and the
-two-step path (33 .. 128 rows on narrow tiles, wide activations, a narrow
-plan too long for LDS)."""
+within 1e-5 * sum|ab|.  Covers the fused narrow path (M <= 32 against fewer
+than 2048 weight rows, with and without the block Hadamard, ragged M and N,
+contractions ending mid-stage, long split contractions, unaligned and padded
+inputs, NaN blocks) and the two-step path (decode shapes into the decode
+GEMM, 33 .. 128 rows on narrow tiles, wide activations, a narrow plan too
+long for LDS)."""
 import numpy as np
 import pytest
 import torch
@@ -96,7 +97,8 @@ def test_quantize_gemm_config3_decode():
         W = workloads.make_tensor(3, wname)
         say("quantize_gemm config3", xname, X.shape, W.shape)
         qw = mx.mxfp4_quantize(to_device_bf16(W), "mx", "rtn", True, 1, 0)
-        assert mx.mxfp4_quantize_gemm_workspace_bytes(X.shape[0], X.shape[1], True, qw) > 0   # split along K
+        # quantized into the workspace, then the decode GEMM
+        assert mx.mxfp4_quantize_gemm_workspace_bytes(X.shape[0], X.shape[1], True, qw) == 16 * X.shape[1] * 17 // 32
         Cf, Cu = _both(mx, to_device_bf16(X), qw, True)
         assert np.array_equal(_bits(Cf), _bits(Cu)), xname
 
