@@ -235,7 +235,13 @@ def summarize_quant(fetch_dir, write_dir, trace_dir, out_md):
 def summarize_stats(stats_csv, out_md):
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
+    head = ""
+    if os.path.exists(out_md):   # keep an existing file's description above the table
+        with open(out_md) as f:
+            text = f.read()
+        head = text[:text.index("| kernel |")] if "| kernel |" in text else text
     with open(out_md, "w") as f:
+        f.write(head)
         f.write("| kernel | calls | average us | min us | max us | share % |\n|---|---|---|---|---|---|\n")
         for r in rows:
             f.write("| %s | %s | %.1f | %.1f | %.1f | %.1f |\n" % (

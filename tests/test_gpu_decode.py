@@ -28,8 +28,13 @@ def _pair(mx, oracle_mod, A, B, had=False):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 2048, 128), (16, 2064, 256), (5, 2056, 1152), (17, 2050, 384),
-                                   (32, 4096, 640), (24, 3000, 4224), (16, 2048, 13 * 128)])
+                                   (32, 4096, 640), (24, 3000, 4224), (16, 2048, 13 * 128), (16, 3000, 8192),
+                                   (16, 8200, 4224), (20, 8192, 512), (32, 8224, 4096), (30, 8208, 4608)])
 def test_decode_gemm_full_check(oracle_mod, M, N, K):
+    """One and two activation tiles, one and two weight tiles per workgroup
+    (from 8192 weight rows; 8200 and 8208 leave a workgroup with a partial or
+    missing second tile), short contractions (one round of loads in flight)
+    and long ones, step counts that leave the last round partial."""
     mx = need_gpu()
     A = workloads.small_t_bf16((M, K), 3.0, seed=51, outlier_frac=0.02)
     B = workloads.small_normal_bf16((N, K), 0.02, seed=52)
