@@ -155,6 +155,9 @@ mxfp4_status mxfp4_gemm_workspace_bytes(const mxfp4_tensor *A, const mxfp4_tenso
  * 2^24 (UNSUPPORTED_SHAPE otherwise); fmt, k and hadamard of A and B must agree
  * (FORMAT_MISMATCH).  A->codes and B->codes must be 16-byte aligned and the
  * scales 4-byte aligned (INVALID_ARG otherwise).
+ * MXFP4 with at most 32 rows of A against at least 2048 rows of B (decode)
+ * streams B once through a kernel of its own, with the contraction split
+ * inside each workgroup: no workspace.
  * workspace: device, 4-byte aligned (WORKSPACE otherwise), at least
  *    mxfp4_gemm_workspace_bytes (NULL if 0); with 16-byte alignment, a
  *    16-byte aligned C and N and ldc multiples of 4, the split-K reduction
@@ -194,8 +197,8 @@ mxfp4_status mxfp4_gemm_quantize_workspace_bytes(const mxfp4_tensor *A, const mx
  * so out is already in its contraction-major layout.  For MXFP4 operands
  * without a K split, the GEMM kernel's epilogue encodes C in registers and
  * writes only codes and scales (0.53 bytes per output instead of 4);
- * otherwise (NVFP4 operands, split contractions) the bf16 C goes through the
- * workspace.  Operands as for mxfp4_gemm; N = B->rows must be a multiple of
+ * otherwise (NVFP4 operands, split contractions, decode shapes) the bf16 C
+ * goes through the workspace.  Operands as for mxfp4_gemm; N = B->rows must be a multiple of
  * 32 (UNSUPPORTED_SHAPE).  out: MXFP4 descriptor [A->rows, B->rows] with
  * out->hadamard == hadamard, codes 16-byte aligned (INVALID_ARG otherwise).
  * workspace: device, 16-byte aligned, at least
@@ -218,13 +221,15 @@ mxfp4_status mxfp4_quantize_gemm_workspace_bytes(int64_t M, int64_t K, int hadam
  * FP4 GEMM kernels):
  *   C[M, N] = Q(x) * B^T,  Q = mxfp4_quantize(x, MXFP4, RTN, hadamard, axis 1),
  * bit for bit the result of mxfp4_quantize followed by mxfp4_gemm on the same
- * input.  For decode-shaped activations (M <= 32) each GEMM workgroup
- * quantizes the activation rows of its own contraction range in LDS, so the
- * activations never go through memory as codes and the call is one GEMM
- * launch (plus the split-K reduction); otherwise (more rows, whose repeated
- * quantization in every column-tile workgroup would cost more than one
- * quantizer pass, and the rare plans whose contraction split is too long for
- * LDS) x is quantized into the workspace first.
+ * input.  For up to 32 activation rows against fewer than 2048 weight rows
+ * each GEMM workgroup quantizes the activation rows of its own contraction
+ * range in LDS, so the activations never go through memory as codes and the
+ * call is one GEMM launch (plus the split-K reduction); otherwise x is
+ * quantized into the workspace first: decode shapes (at least 2048 weight
+ * rows), where the decode GEMM after a quantizer pass is faster than that
+ * fused kernel, more rows, whose repeated quantization in every column-tile
+ * workgroup would cost more than one quantizer pass, and the rare plans whose
+ * contraction split is too long for LDS.
  * x: device, bf16 bit patterns [M, K], row-major, leading dimension ldx >= K.
  * B: the pre-quantized weights [N, K] (MXFP4, B->k == K and B->hadamard ==
  *    hadamard, else FORMAT_MISMATCH); B->codes 16-byte and B->scales 4-byte
