@@ -155,9 +155,10 @@ mxfp4_status mxfp4_gemm_workspace_bytes(const mxfp4_tensor *A, const mxfp4_tenso
  * 2^24 (UNSUPPORTED_SHAPE otherwise); fmt, k and hadamard of A and B must agree
  * (FORMAT_MISMATCH).  A->codes and B->codes must be 16-byte aligned and the
  * scales 4-byte aligned (INVALID_ARG otherwise).
- * MXFP4 with at most 32 rows of A against at least 2048 rows of B (decode)
- * streams B once through a kernel of its own, with the contraction split
- * inside each workgroup: no workspace.
+ * MXFP4 with at most 128 rows of A (decode and small batches) against at
+ * least 2048 rows of B, or with few operand bytes per 16 rows of B, streams
+ * B once through a kernel of its own, with the contraction split inside each
+ * workgroup: no workspace.
  * workspace: device, 4-byte aligned (WORKSPACE otherwise), at least
  *    mxfp4_gemm_workspace_bytes (NULL if 0); with 16-byte alignment, a
  *    16-byte aligned C and N and ldc multiples of 4, the split-K reduction
@@ -221,15 +222,16 @@ mxfp4_status mxfp4_quantize_gemm_workspace_bytes(int64_t M, int64_t K, int hadam
  * FP4 GEMM kernels):
  *   C[M, N] = Q(x) * B^T,  Q = mxfp4_quantize(x, MXFP4, RTN, hadamard, axis 1),
  * bit for bit the result of mxfp4_quantize followed by mxfp4_gemm on the same
- * input.  For up to 32 activation rows against fewer than 2048 weight rows
- * each GEMM workgroup quantizes the activation rows of its own contraction
- * range in LDS, so the activations never go through memory as codes and the
- * call is one GEMM launch (plus the split-K reduction); otherwise x is
- * quantized into the workspace first: decode shapes (at least 2048 weight
- * rows), where the decode GEMM after a quantizer pass is faster than that
- * fused kernel, more rows, whose repeated quantization in every column-tile
- * workgroup would cost more than one quantizer pass, and the rare plans whose
- * contraction split is too long for LDS.
+ * input.  Where the GEMM takes the narrow kernel with up to 32 activation
+ * rows (long contractions against short weights), each GEMM workgroup
+ * quantizes the activation rows of its own contraction range in LDS, so the
+ * activations never go through memory as codes and the call is one GEMM
+ * launch (plus the split-K reduction); otherwise x is quantized into the
+ * workspace first: the decode kernel's shapes, where that kernel after a
+ * quantizer pass is faster than the fused one, more rows, whose repeated
+ * quantization in every column-tile workgroup would cost more than one
+ * quantizer pass, and the rare plans whose contraction split is too long for
+ * LDS.
  * x: device, bf16 bit patterns [M, K], row-major, leading dimension ldx >= K.
  * B: the pre-quantized weights [N, K] (MXFP4, B->k == K and B->hadamard ==
  *    hadamard, else FORMAT_MISMATCH); B->codes 16-byte and B->scales 4-byte

@@ -1110,7 +1110,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_fused_kernel(GemmArgs p) {
   mx_tile<TM, 2, 1, OUT, true, HAD>(p, smem, 0, (int64_t)blockIdx.x * 256, kt0, kt1, Cz);
 }
 
-// Decode-shaped MXFP4 GEMM (M <= 32 activation rows against a long weight):
+// Decode-shaped MXFP4 GEMM (up to 128 activation rows against the weights):
 // the weights stream from HBM once, so the kernel is built for bytes in
 // flight rather than MFMA rate.  A workgroup owns 16 output columns (weight
 // rows) over the whole contraction; its NW waves take contiguous ranges of
@@ -1120,7 +1120,7 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_fused_kernel(GemmArgs p) {
 // One step is v_mfma_scale_f32_16x16x128_f8f6f4 with the weights as the
 // first operand: lane l holds block 4s + l / 16 of weight row n0 + l % 16
 // (16 code bytes) and that block's scale byte, and the same block of
-// activation row 16t + l % 16 (TMR = 1 or 2 tiles of 16 rows); the output
+// activation row 16t + l % 16 (TMR = 1 .. 8 tiles of 16 rows); the output
 // lane l holds is C[16t + l % 16][n0 + 4 (l / 16) + v], v = 0..3.
 //
 // That operand layout gives each row only 64 bytes per load instruction,
@@ -1489,9 +1489,15 @@ GemmPlan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
   pl.narrow_tm = 0;
   pl.waves8 = 0;
   pl.decode = 0;
-  if (mx && M <= 32 && N >= MXFP4_DECODE_MIN_N) {
-    // decode shapes: 16-column workgroups over the whole contraction
-    pl.decode = M <= 16 ? 1 : 2;
+  // decode shapes: 16-column workgroups over the whole contraction, when
+  // there are enough of them or each one's operand bytes ((M + 16) K / 2) stay
+  // small (measured against the narrow kernel: better on every shape with at
+  // least 2048 weight rows up to 128 activation rows, and on shorter weights
+  // up to ~0.5 MB per workgroup; 128 x 512 x 16384, 1.2 MB per workgroup
+  // over 32 workgroups, is 28 % slower)
+  if (mx && M <= MXFP4_DECODE_MAX_M &&
+      (N >= MXFP4_DECODE_MIN_N || (M + 16) * (K / 2) <= MXFP4_DECODE_WG_BYTES)) {
+    pl.decode = (int)((M + 15) / 16);
     pl.splits = 1;
     return pl;
   }
@@ -1544,7 +1550,7 @@ static int compute_units() {
 // workgroup halve the activation bytes each weight byte brings through L2
 // when that still leaves at least 256 workgroups; contractions of at most two
 // rounds per wave take R = 2 (more workgroups resident, one round in flight
-// each), longer ones the most slots that fit.
+// each), longer ones four slots where they fit in LDS.
 template <int TMR, int TN, int R, int OUT>
 static void launch_decode_kernel(const GemmArgs& p, hipStream_t stream) {
   static_assert(DecodeShape<TMR, TN, R>::LDS <= 160 * 1024, "LDS");
@@ -1555,27 +1561,42 @@ static void launch_decode_kernel(const GemmArgs& p, hipStream_t stream) {
 #ifndef MXFP4_DECODE_R11
 #define MXFP4_DECODE_R11 4
 #endif
+template <int TMR, int OUT>
+static void launch_decode_tmr(const GemmArgs& p, bool tn2, bool short_k, hipStream_t stream) {
+  constexpr int LDS_MAX = 160 * 1024;
+  if (tn2) {
+    if constexpr (DecodeShape<TMR, 2, 4>::LDS <= LDS_MAX) {
+      if (!short_k) return launch_decode_kernel<TMR, 2, 4, OUT>(p, stream);
+    }
+    launch_decode_kernel<TMR, 2, 2, OUT>(p, stream);
+  } else {
+    constexpr int RL = TMR == 1 ? MXFP4_DECODE_R11 : 4;
+    if constexpr (DecodeShape<TMR, 1, RL>::LDS <= LDS_MAX) {
+      if (!short_k) return launch_decode_kernel<TMR, 1, RL, OUT>(p, stream);
+    }
+    launch_decode_kernel<TMR, 1, 2, OUT>(p, stream);
+  }
+}
+
 template <int OUT>
 static void launch_decode(const GemmArgs& p, const GemmPlan& plan, hipStream_t stream) {
   const int64_t rounds = (p.K / 128 + 3) / 4;
   const bool short_k = rounds <= 2 * MXFP4_DECODE_NW;
   const bool tn2 = p.N >= MXFP4_DECODE_TN2_MIN_N;
-  if (plan.decode == 1) {
-    if (tn2) {
-      if (short_k) launch_decode_kernel<1, 2, 2, OUT>(p, stream);
-      else launch_decode_kernel<1, 2, 4, OUT>(p, stream);
-    } else {
-      if (short_k) launch_decode_kernel<1, 1, 2, OUT>(p, stream);
-      else launch_decode_kernel<1, 1, MXFP4_DECODE_R11, OUT>(p, stream);
-    }
-  } else {
-    if (tn2) {
-      if (short_k) launch_decode_kernel<2, 2, 2, OUT>(p, stream);
-      else launch_decode_kernel<2, 2, 4, OUT>(p, stream);
-    } else {
-      if (short_k) launch_decode_kernel<2, 1, 2, OUT>(p, stream);
-      else launch_decode_kernel<2, 1, 4, OUT>(p, stream);
-    }
+  switch (plan.decode) {
+    case 1: launch_decode_tmr<1, OUT>(p, tn2, short_k, stream); break;
+    case 2: launch_decode_tmr<2, OUT>(p, tn2, short_k, stream); break;
+#if MXFP4_DECODE_MAX_M > 32
+    case 3: launch_decode_tmr<3, OUT>(p, tn2, short_k, stream); break;
+    case 4: launch_decode_tmr<4, OUT>(p, tn2, short_k, stream); break;
+#endif
+#if MXFP4_DECODE_MAX_M > 64
+    case 5: launch_decode_tmr<5, OUT>(p, tn2, short_k, stream); break;
+    case 6: launch_decode_tmr<6, OUT>(p, tn2, short_k, stream); break;
+    case 7: launch_decode_tmr<7, OUT>(p, tn2, short_k, stream); break;
+    case 8: launch_decode_tmr<8, OUT>(p, tn2, short_k, stream); break;
+#endif
+    default: break;
   }
 }
 

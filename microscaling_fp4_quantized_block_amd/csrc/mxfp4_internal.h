@@ -30,11 +30,19 @@ struct GemmPlan {
   int64_t k_tiles;     // contraction tiles of the kernel's K step
   int narrow_tm;       // MXFP4 with M <= 128: rows per narrow tile / 32 (1, 2 or 4); 0 = wide tiles
   int waves8;          // MXFP4 wide tiles with at most four stages: the 8-wave kernel
-  int decode;          // MXFP4 with M <= 32 against a long weight: gemm_mx_decode_kernel with 16-row A tiles (1 or 2)
+  int decode;          // MXFP4 with few rows against a long weight: gemm_mx_decode_kernel with this many 16-row A tiles
 };
-// weights of at least this many rows take the decode kernel when M <= 32
+// MXFP4 with at most MXFP4_DECODE_MAX_M activation rows takes the decode
+// kernel against weights of at least MXFP4_DECODE_MIN_N rows, or when a
+// workgroup's operand bytes stay within MXFP4_DECODE_WG_BYTES
 #ifndef MXFP4_DECODE_MIN_N
 #define MXFP4_DECODE_MIN_N 2048
+#endif
+#ifndef MXFP4_DECODE_MAX_M
+#define MXFP4_DECODE_MAX_M 128
+#endif
+#ifndef MXFP4_DECODE_WG_BYTES
+#define MXFP4_DECODE_WG_BYTES (512 * 1024)
 #endif
 // and from this many, two 16-row weight tiles per workgroup
 #ifndef MXFP4_DECODE_TN2_MIN_N

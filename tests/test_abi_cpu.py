@@ -196,8 +196,9 @@ def test_gemm_bf16_rejects_bad_arguments(mx):
     assert g(a, b, C=FAKE + 1) == INVALID                          # bf16 C must be 2-byte aligned
     assert g(desc(mx, codes=FAKE + 8), b) == INVALID
     assert g(desc(mx, rows=0), b) == OK
-    # a split plan still needs its FP32 partial-sum workspace
-    A, B = desc(mx, rows=64, k=8192), desc(mx, rows=96, k=8192)
+    # a split plan still needs its FP32 partial-sum workspace (64 rows against
+    # 96 over K = 32768: past the decode kernel's bytes per workgroup)
+    A, B = desc(mx, rows=64, k=32768), desc(mx, rows=96, k=32768)
     assert mx.lib.mxfp4_gemm_bf16(ctypes.byref(A), ctypes.byref(B), FAKE + 2, 96, None, 0, None) == WORKSPACE
 
 
@@ -208,16 +209,22 @@ def test_gemm_fp32_output_alignment(mx):
 
 def test_gemm_workspace_query_matches_split_plan(mx):
     b = ctypes.c_size_t()
-    # 64 x 96 outputs over a long contraction: split along K, fp32 partials
+    # 64 x 96 outputs over a long contraction (80 x 16384 operand bytes per
+    # decode workgroup, past its limit): the narrow kernel split along K
+    # into 32 ranges, fp32 partials
+    A, B = desc(mx, rows=64, k=32768), desc(mx, rows=96, k=32768)
+    assert mx.lib.mxfp4_gemm_workspace_bytes(ctypes.byref(A), ctypes.byref(B), ctypes.byref(b)) == OK
+    assert b.value == 32 * 64 * 96 * 4
+    # the same rows over K = 8192 take the decode kernel: no workspace
     A, B = desc(mx, rows=64, k=8192), desc(mx, rows=96, k=8192)
     assert mx.lib.mxfp4_gemm_workspace_bytes(ctypes.byref(A), ctypes.byref(B), ctypes.byref(b)) == OK
-    assert b.value > 0 and b.value % (64 * 96 * 4) == 0
+    assert b.value == 0
     # a large output needs no split
     A, B = desc(mx, rows=4096, k=8192), desc(mx, rows=14336, k=8192)
     assert mx.lib.mxfp4_gemm_workspace_bytes(ctypes.byref(A), ctypes.byref(B), ctypes.byref(b)) == OK
     assert b.value == 0
     # the split GEMM rejects a missing workspace before launching
-    A, B = desc(mx, rows=64, k=8192), desc(mx, rows=96, k=8192)
+    A, B = desc(mx, rows=64, k=32768), desc(mx, rows=96, k=32768)
     assert mx.lib.mxfp4_gemm(ctypes.byref(A), ctypes.byref(B), FAKE, 96, None, 0, None) == WORKSPACE
 
 
@@ -259,21 +266,29 @@ def test_quantize_gemm_rejects_bad_arguments(mx):
 
 
 def test_quantize_gemm_workspace_bytes(mx):
-    # decode 16 x 14336 x 4096 and 16 x 4096 x 14336 (at most 32 rows against
-    # at least 2048 weight rows): quantized into the workspace (codes and
-    # scales, 16-byte padded), then the decode GEMM, which needs no workspace
+    # decode 16 x 14336 x 4096 and 16 x 4096 x 14336 (decode plans): quantized
+    # into the workspace (codes and scales, 16-byte padded), then the decode
+    # GEMM, which needs no workspace
     assert qgemm_ws(mx, 16, 4096, 0, desc(mx, rows=14336, k=4096)) == (OK, 16 * 2048 + 16 * 128)
     assert qgemm_ws(mx, 16, 4096, 1, desc(mx, had=1, rows=14336, k=4096)) == (OK, 16 * 2048 + 16 * 128)
     assert qgemm_ws(mx, 16, 14336, 1, desc(mx, had=1, rows=4096, k=14336)) == (OK, 16 * 7168 + 16 * 448)
     # wide activations: quantized codes and scales (16-byte padded), no split
     assert qgemm_ws(mx, 300, 1024, 0, desc(mx, rows=512, k=1024)) == (OK, 300 * 512 + 300 * 32)
-    # a narrow plan whose splits are too long for LDS (128 rows -> 4 stages
-    # per split at most; 256 column tiles leave one split of 32 stages): two
-    # steps, codes + scales, no split partials
+    # 128 rows against 65536 weight rows: the decode GEMM too
     assert qgemm_ws(mx, 128, 8192, 0, desc(mx, rows=65536, k=8192)) == (OK, 128 * 4096 + 128 * 256)
-    # 16 rows against 1024 weight rows: fused into the narrow GEMM, 4 column
-    # tiles over 16 stage pairs -> 8 splits of 2 pairs; only the split partial sums
-    assert qgemm_ws(mx, 16, 8192, 1, desc(mx, had=1, rows=1024, k=8192)) == (OK, 8 * 16 * 1024 * 4)
+    # 100 rows against 1024 weight rows over K = 16384 (past the decode
+    # kernel's bytes per workgroup): the narrow plan with 128-row tiles, 16
+    # splits, not fused (the fused kernel takes 32-row tiles): codes, scales
+    # and the split partials
+    assert qgemm_ws(mx, 100, 16384, 0, desc(mx, rows=1024, k=16384)) == (
+        OK, 100 * 8192 + 100 * 512 + 16 * 100 * 1024 * 4)
+    # 16 rows against 1024 weight rows over K = 65536 (32 x 32768 operand
+    # bytes per decode workgroup, past its limit): fused into the narrow GEMM,
+    # 4 column tiles over 128 stage pairs -> 32 splits of 4 pairs; only the
+    # split partial sums
+    assert qgemm_ws(mx, 16, 65536, 1, desc(mx, had=1, rows=1024, k=65536)) == (OK, 32 * 16 * 1024 * 4)
+    # the same against K = 8192: the decode GEMM after quantizing into the workspace
+    assert qgemm_ws(mx, 16, 8192, 1, desc(mx, had=1, rows=1024, k=8192)) == (OK, 16 * 4096 + 16 * 256)
     assert qgemm_ws(mx, 16, 4096, 0, desc(mx, fmt=1, rows=64, k=4096))[0] == MISMATCH
 
 

@@ -1,11 +1,12 @@
-"""GPU parity of the decode-shaped MXFP4 GEMM (at most 32 activation rows
-against a weight of at least 2048 rows: 16-column workgroups over the whole
-contraction, the waves' partial sums added in LDS in wave order).  Every
-element against the binary64 oracle within 1e-5 * sum|ab|: one and two
-16-row activation tiles, ragged weight rows, step counts that do not divide
-evenly among the waves, contractions of a single step; fp32 and bf16 C into
-strided and misaligned outputs (same bits as the contiguous call, nothing
-outside the view written); NaN scale bytes; no workspace."""
+"""GPU parity of the decode-shaped MXFP4 GEMM (up to 128 activation rows
+against a weight of at least 2048 rows, or with few operand bytes per
+workgroup: 16-column workgroups over the whole contraction, the waves'
+partial sums added in LDS in wave order).  Every element against the binary64
+oracle within 1e-5 * sum|ab|: one to eight 16-row activation tiles, ragged
+weight rows, step counts that do not divide evenly among the waves,
+contractions of a single step; fp32 and bf16 C into strided and misaligned
+outputs (same bits as the contiguous call, nothing outside the view
+written); NaN scale bytes; no workspace."""
 import numpy as np
 import pytest
 import torch
@@ -29,12 +30,16 @@ def _pair(mx, oracle_mod, A, B, had=False):
 
 @pytest.mark.parametrize("M,N,K", [(1, 2048, 128), (16, 2064, 256), (5, 2056, 1152), (17, 2050, 384),
                                    (32, 4096, 640), (24, 3000, 4224), (16, 2048, 13 * 128), (16, 3000, 8192),
-                                   (16, 8200, 4224), (20, 8192, 512), (32, 8224, 4096), (30, 8208, 4608)])
+                                   (16, 8200, 4224), (20, 8192, 512), (32, 8224, 4096), (30, 8208, 4608),
+                                   (33, 2048, 256), (48, 300, 1152), (64, 8200, 4224), (80, 2050, 640),
+                                   (100, 4096, 4224), (128, 8192, 512), (128, 300, 2048), (97, 96, 128)])
 def test_decode_gemm_full_check(oracle_mod, M, N, K):
-    """One and two activation tiles, one and two weight tiles per workgroup
-    (from 8192 weight rows; 8200 and 8208 leave a workgroup with a partial or
-    missing second tile), short contractions (one round of loads in flight)
-    and long ones, step counts that leave the last round partial."""
+    """One to eight activation tiles (partial last tiles), one and two weight
+    tiles per workgroup (from 8192 weight rows; 8200 and 8208 leave a
+    workgroup with a partial or missing second tile), weights shorter than
+    2048 rows, short contractions (one round of loads in flight) and long
+    ones (fewer slots where the activation tiles fill LDS), step counts that
+    leave the last round partial."""
     mx = need_gpu()
     A = workloads.small_t_bf16((M, K), 3.0, seed=51, outlier_frac=0.02)
     B = workloads.small_normal_bf16((N, K), 0.02, seed=52)

@@ -1,12 +1,12 @@
 """GPU parity of the online-activation-quantization GEMM (mxfp4_quantize_gemm):
 its result must equal mxfp4_quantize followed by mxfp4_gemm bit for bit (same
 codes, same scale bytes, same products in the same order), and the oracle
-within 1e-5 * sum|ab|.  Covers the fused narrow path (M <= 32 against fewer
-than 2048 weight rows, with and without the block Hadamard, ragged M and N,
-contractions ending mid-stage, long split contractions, unaligned and padded
-inputs, NaN blocks) and the two-step path (decode shapes into the decode
-GEMM, 33 .. 128 rows on narrow tiles, wide activations, a narrow plan too
-long for LDS)."""
+within 1e-5 * sum|ab|.  Covers the two-step path into the decode GEMM (up to
+128 rows: with and without the block Hadamard, ragged M and N, contractions
+ending mid-stage, unaligned and padded inputs, NaN blocks, configuration 3
+decode), the fused narrow path (up to 32 rows on a narrow plan: long
+contractions against short weights, split along K) and the other two-step
+cases (more rows on narrow tiles, wide activations)."""
 import numpy as np
 import pytest
 import torch
@@ -33,7 +33,8 @@ def _both(mx, x, qw, had):
 @pytest.mark.parametrize("had", [False, True])
 @pytest.mark.parametrize("M,N,K", [(1, 300, 256), (16, 256, 1024), (17, 529, 384), (32, 512, 2048),
                                    (5, 96, 8192), (31, 7000, 4096), (33, 640, 1024), (64, 96, 8192),
-                                   (100, 256, 640), (128, 160, 512), (129, 200, 256), (300, 272, 384)])
+                                   (100, 256, 640), (128, 160, 512), (129, 200, 256), (300, 272, 384),
+                                   (16, 256, 65536), (7, 300, 65536)])
 def test_quantize_gemm_matches_two_step_and_oracle(oracle_mod, had, M, N, K):
     """Every element of C: bit-identical to the two-step path, and within the
     oracle's tolerance (128 < M takes the two-step path itself)."""
@@ -103,13 +104,13 @@ def test_quantize_gemm_config3_decode():
         assert np.array_equal(_bits(Cf), _bits(Cu)), xname
 
 
-def test_quantize_gemm_narrow_plan_too_long_for_lds():
-    """65 rows (128-row blocks, at most 4 stages of activations in LDS) against
-    65536 weight rows: 256 column tiles leave one split of 16 stages, so the
-    call quantizes into the workspace and runs the GEMM; the result is still
-    the two-step one."""
+def test_quantize_gemm_narrow_plan_not_fused():
+    """65 rows against 1024 weight rows over K = 16384 (past the decode
+    kernel's bytes per workgroup): a narrow plan with 128-row tiles, which the
+    fused kernel (32-row tiles) does not take, so the call quantizes into the
+    workspace and runs the split GEMM; the result is still the two-step one."""
     mx = need_gpu()
-    M, N, K = 65, 65536, 4096
+    M, N, K = 65, 1024, 16384
     g = torch.Generator(device="cuda")
     g.manual_seed(47)
     x = (torch.randn((M, K), generator=g, device="cuda") * 2.0).to(torch.bfloat16)
@@ -118,6 +119,7 @@ def test_quantize_gemm_narrow_plan_too_long_for_lds():
     qw = mx.mxfp4_quantize(w, "mx", "rtn", False, 1, 0)
     del w
     need = mx.mxfp4_quantize_gemm_workspace_bytes(M, K, False, qw)
-    assert need == M * K // 2 + ((M * K // 32 + 15) // 16) * 16
+    ws_gemm = mx.mxfp4_gemm_workspace_bytes(mx.empty_qtensor("mx", M, K, False, "cuda"), qw)
+    assert ws_gemm > 0 and need == M * K // 2 + ((M * K // 32 + 15) // 16) * 16 + ws_gemm
     Cf, Cu = _both(mx, x, qw, False)
     assert np.array_equal(_bits(Cf), _bits(Cu))

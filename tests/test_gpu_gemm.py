@@ -24,12 +24,16 @@ def _quant_pair(mx, oracle_mod, A_bits, B_bits, fmt, had=False, rnd="rtn", axis_
 
 @pytest.mark.parametrize("fmt", ["mx", "nv"])
 @pytest.mark.parametrize("M,N,K", [(256, 256, 1024), (300, 200, 384), (17, 529, 256), (512, 768, 2048),
-                                   (64, 96, 8192), (1, 1, 128), (128, 160, 640), (64, 64, 4224)])
+                                   (64, 96, 8192), (1, 1, 128), (128, 160, 640), (64, 64, 4224),
+                                   (64, 96, 32768), (100, 64, 12672)])
 def test_gemm_small_full_check(oracle_mod, fmt, M, N, K):
     """Several tiles with ragged edges, short contractions, contractions that
-    end half way into a 256-wide stage (384, 640, 128, 4224), split-K cases
-    (64 x 96 x 8192; 64 x 64 x 4224 with an odd stage count) and a 1 x 1
-    output; every element checked."""
+    end half way into a 256-wide stage (384, 640, 128, 4224, 12672), a 1 x 1
+    output; MXFP4 rows up to 128 take the decode kernel (64 x 96 x 8192 and
+    the other small ones), and the narrow kernel split along K where a decode
+    workgroup's operands would pass its limit (64 x 96 x 32768; 100 x 64 x
+    12672 with an odd stage count in the last split); NVFP4 splits the wide
+    kernel (64 x 96 x 8192 and the long ones); every element checked."""
     mx = need_gpu()
     A = workloads.small_t_bf16((M, K), 3.0, seed=31, outlier_frac=0.02)
     B = workloads.small_normal_bf16((N, K), 0.02, seed=32)
@@ -206,13 +210,13 @@ def test_gemm_config4_wgrad_split_k(oracle_mod):
     _sampled_check(mx, oracle_mod, qa, qb, oa, ob, "mx", "config4 wgrad fc2", nsample=16)
 
 
-@pytest.mark.parametrize("fmt,M,N,K", [("mx", 300, 300, 16384), ("mx", 40, 260, 16384), ("mx", 300, 300, 4096),
+@pytest.mark.parametrize("fmt,M,N,K", [("mx", 300, 300, 16384), ("mx", 40, 260, 32768), ("mx", 300, 300, 4096),
                                        ("nv", 200, 260, 8192)])
 def test_splitk_reduction_load_widths_agree(oracle_mod, fmt, M, N, K):
     """The split-K reduction adds the partials in split order whether it reads
     them four outputs at a time (contiguous, 16-byte aligned C, more than four
-    splits: 16 here, wide and narrow tiles, NVFP4) or one at a time (C at an odd
-    row stride and a 4-byte offset; 4 splits): the same bits, fp32 and bf16 C,
+    splits: 16 or 32 here, wide and narrow tiles, NVFP4) or one at a time (C at
+    an odd row stride and a 4-byte offset; 4 splits): the same bits, fp32 and bf16 C,
     and the oracle within tolerance on sampled rows."""
     mx = need_gpu()
     A = workloads.small_normal_bf16((M, K), 1.0, seed=41)

@@ -3,9 +3,9 @@ MXFP4 for the next layer): bit for bit the same codes and scale bytes as
 mxfp4_gemm_bf16 followed by mxfp4_quantize (round to nearest, along rows,
 block Hadamard when asked), and the same as the oracle's quantizer on the
 GPU's bf16 C (the GEMM itself is checked against the binary64 oracle by the
-GEMM tests).  Covers the fused epilogue (MXFP4, no K split: ragged tiles, the
-256 x 128 half tiles, narrow tiles) and the two-step path (split K, NVFP4
-operands)."""
+GEMM tests).  Covers the fused epilogue (MXFP4 wide tiles, no K split: ragged
+tiles, the 256 x 128 half tiles) and the two-step path (the decode kernel's
+shapes, split K, NVFP4 operands)."""
 import numpy as np
 import pytest
 import torch
