@@ -32,7 +32,10 @@
 // Workgroup ids are remapped so that tiles running at the same time on one XCD
 // (which owns one L2) share A and B panels.  Long contractions with few
 // output tiles are split along K; the partial sums land in the workspace and a
-// second kernel adds them in a fixed order.
+// second kernel adds them in a fixed order.  Up to 128 activation rows take
+// the decode kernel instead (16-column workgroups over the whole contraction,
+// 16x16x128 scaled MFMA), and where its workgroups would hold too many
+// operand bytes, the narrow kernel (32-row tiles, split along K).
 #include <type_traits>
 
 #include "fp4_device.h"
@@ -1074,10 +1077,11 @@ __global__ void __launch_bounds__(512, 1) gemm_mx8_kernel(GemmArgs p) {
   }
 }
 
-// Narrow MXFP4 GEMM (M <= 32 TM <= 128: decode-shaped activations against
-// weights): 32 TM x 256 tiles, the four waves side by side along N, so no MFMA
-// work is spent on rows past M; these shapes stream the weights from HBM and
-// are split along K for enough workgroups.  Grid: (N tiles, splits).
+// Narrow MXFP4 GEMM (M <= 32 TM <= 128 where the decode kernel is not taken:
+// long contractions against short weights): 32 TM x 256 tiles, the four waves
+// side by side along N, so no MFMA work is spent on rows past M; these shapes
+// stream the weights from HBM and are split along K for enough workgroups.
+// Grid: (N tiles, splits).
 template <int TM, int OUT>
 __global__ void __launch_bounds__(256, 1) gemm_mx_narrow_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[MX_LDS];
