@@ -1525,12 +1525,19 @@ GemmPlan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
   const int64_t min_units = mx ? 2 : 4;        // at least 4 stages of 256 / 128 per split
   int splits = 1;
   // fewer output tiles than compute units: split the contraction so that
-  // about one wave of workgroups fills the chip
+  // about one wave of workgroups fills the chip ...
   const int64_t cus = 256;
   if (tiles < cus && units >= 2 * min_units) {
     int64_t s = cus / tiles;
     if (s > units / min_units) s = units / min_units;
     if (s > 32) s = 32;
+    // ... while the time a split saves, (1 - 1/s) of a tile's contraction at
+    // the MFMA rate one wave per SIMD reaches, exceeds what it adds: the fp32
+    // partials written and read back (8 s bytes per output at ~5 TB/s) and the
+    // reduction's launch (measured: 8192 x 1024 x 2048 took 46.5 us in two
+    // splits and 20.1 us whole, 4096 x 2048 x 4096 53.2 and 30.0 us)
+    const double t_k = (double)K * (mx ? 5.2e-9 : 2.1e-8);
+    while (s > 1 && t_k * (1.0 - 1.0 / (double)s) <= (double)M * (double)N * 8.0 * (double)s / 5.0e12 + 3.0e-6) s--;
     if (s > 1) splits = (int)s;
   }
   pl.splits = splits;
