@@ -1534,10 +1534,12 @@ GemmPlan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
     // ... while the time a split saves, (1 - 1/s) of a tile's contraction at
     // the MFMA rate one wave per SIMD reaches, exceeds what it adds: the fp32
     // partials written and read back (8 s bytes per output at ~5 TB/s) and the
-    // reduction's launch (measured: 8192 x 1024 x 2048 took 46.5 us in two
-    // splits and 20.1 us whole, 4096 x 2048 x 4096 53.2 and 30.0 us)
+    // reduction's launch, ~4 us (measured: 8192 x 1024 x 2048 took 46.5 us in
+    // two splits and 20.1 us whole, 4096 x 2048 x 4096 53.2 and 30.0 us,
+    // 2048 x 1024 x 4096 31.5 in three and 27.8 whole; 1024 x 1024 x 8192
+    // 29.7 in eight and 45.1 whole)
     const double t_k = (double)K * (mx ? 5.2e-9 : 2.1e-8);
-    while (s > 1 && t_k * (1.0 - 1.0 / (double)s) <= (double)M * (double)N * 8.0 * (double)s / 5.0e12 + 3.0e-6) s--;
+    while (s > 1 && t_k * (1.0 - 1.0 / (double)s) <= (double)M * (double)N * 8.0 * (double)s / 5.0e12 + 4.0e-6) s--;
     if (s > 1) splits = (int)s;
   }
   pl.splits = splits;
