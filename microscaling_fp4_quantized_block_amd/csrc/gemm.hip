@@ -902,7 +902,10 @@ __device__ __forceinline__ void mx_tile(const GemmArgs& p, uint8_t* smem, int64_
 // tiles divide evenly or a split is used): the R remainder tiles are cut into
 // two 256 x 128 halves, one run by the first workgroups and one by the last,
 // so every compute unit ends at the same time, and the C stores of the two
-// groups of compute units fall at alternating times.  (Four phases, with
+// groups of compute units fall at alternating times.  With at most half as
+// many tiles as compute units, R = T: every tile runs as two halves on two
+// compute units (measured: 256 x 14336 x 4096 29.3 -> 22.4 us, 4096 x 1024 x
+// 4096 28.0 -> 20.2 us).  (Four phases, with
 // quarter and three-quarter pieces, measured ~10 % slower.)  Within each range, consecutive workgroup ids go to consecutive XCDs, so the
 // ids one XCD runs are gathered into a contiguous run of tiles, walked in
 // groups of GROUP_M tile rows.
@@ -1538,8 +1541,12 @@ GemmPlan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
     // two splits and 20.1 us whole, 4096 x 2048 x 4096 53.2 and 30.0 us,
     // 2048 x 1024 x 4096 31.5 in three and 27.8 whole; 1024 x 1024 x 8192
     // 29.7 in eight and 45.1 whole)
+    // (unsplit MXFP4 launches of at most half as many tiles as compute units
+    // run every tile as two 256 x 128 halves, so they take about half a
+    // tile's contraction time)
     const double t_k = (double)K * (mx ? 5.2e-9 : 2.1e-8);
-    while (s > 1 && t_k * (1.0 - 1.0 / (double)s) <= (double)M * (double)N * 8.0 * (double)s / 5.0e12 + 4.0e-6) s--;
+    const double whole = (mx && tiles * 2 <= cus) ? 0.5 : 1.0;
+    while (s > 1 && t_k * (whole - 1.0 / (double)s) <= (double)M * (double)N * 8.0 * (double)s / 5.0e12 + 4.0e-6) s--;
     if (s > 1) splits = (int)s;
   }
   pl.splits = splits;
@@ -1659,6 +1666,7 @@ static hipError_t launch_gemm_common(bool nv, GemmArgs p, void* C, int64_t ldc, 
   if (!nv && plan.splits == 1 && !plan.narrow_tm && !plan.decode) {
     const int64_t cus = compute_units();
     if (tiles > cus && tiles % cus != 0) p.rem = (int)(tiles % cus);
+    else if (tiles * 2 <= cus) p.rem = (int)tiles;   // few tiles: every one as two 256 x 128 halves
   }
   dim3 grid((unsigned)(tiles + p.rem), (unsigned)plan.splits);
   dim3 ngrid((unsigned)((p.N + 255) / 256), (unsigned)plan.splits);
