@@ -384,7 +384,50 @@ class ClockStamps:
                 "compute_units_paired": int(len(vals)),
                 "wall_s": round(wall, 6) if wall is not None else None,
                 "source": "s_memtime / s_memrealtime of each compute unit, stamped before and after the timed steps",
-                "note": "a register-only MFMA probe puts this counter about 10% below the MFMA clock"}
+                "note": "s_memtime advances once per shader clock (the MFMA ceiling run counts 32 ticks per "
+                        "32-cycle scaled FP4 MFMA)"}
+
+
+def mfma_ceiling(device, launches=6, iters=30000):
+    """The scaled FP4 MFMA rate the chip sustains with no memory traffic, on
+    pseudo-random operands (libmxclock.so's ceiling kernel: one workgroup of
+    four waves per compute unit, 16 independent accumulators per wave).  Run
+    after the timed steps, back to back for ~60 ms; the last launches are
+    timed with events, and the kernel's own s_memtime / s_memrealtime stamps
+    give the clock during them and the counter ticks per MFMA."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "microscaling_fp4_quantized_block_amd", "libmxclock.so"))
+    lib.mxclock_mfma_ceiling.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mxclock_mfma_ceiling.restype = ctypes.c_int
+    lib.mxclock_ceiling_mfmas_per_iter.restype = ctypes.c_longlong
+    lib.mxclock_wall_rate_khz.restype = ctypes.c_int
+    stamps = torch.zeros(lib.mxclock_ceiling_stamp_slots(), dtype=torch.int64, device=device)
+    sink = torch.zeros(lib.mxclock_ceiling_sink_slots(), dtype=torch.float32, device=device)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    timed = 2
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for i in range(launches):
+        if i == launches - timed:
+            ev[0].record()
+        if lib.mxclock_mfma_ceiling(iters, ctypes.c_void_p(stamps.data_ptr()), ctypes.c_void_p(sink.data_ptr()),
+                                    stream) != 0:
+            raise RuntimeError("MFMA ceiling launch failed")
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / timed
+    mfmas = lib.mxclock_ceiling_mfmas_per_iter() * iters
+    tflops = mfmas * 2.0 * 32 * 32 * 64 / (ms * 1e-3) / 1e12
+    st = stamps.cpu().numpy().view(np.uint64).reshape(-1, 2).astype(np.float64)
+    rate_khz = lib.mxclock_wall_rate_khz()
+    mhz = float(np.median(st[:, 0] / st[:, 1] * rate_khz / 1e3)) if rate_khz else None
+    ticks = float(np.median(st[:, 0])) / (16.0 * iters)   # per wave: 16 MFMAs per iteration
+    return {"tflops": round(tflops, 1), "frac_of_fp4_peak": round(tflops / PEAK_FP4_TFLOPS, 4),
+            "sclk_mhz": round(mhz, 1) if mhz else None, "ticks_per_mfma": round(ticks, 2),
+            "ms_per_launch": round(ms, 3),
+            "what": "scaled FP4 MFMA 32x32x64 alone on pseudo-random codes, one workgroup of four waves per "
+                    "compute unit, no memory traffic; run after the timed steps; the clock it holds is set by "
+                    "the power of random operands"}
 
 
 def cpu_model():
@@ -835,6 +878,7 @@ def main():
     torch.cuda.synchronize()
     qa_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in part_events]))
     qb_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in part_events]))
+    ceiling = mfma_ceiling(dev)
 
     flops = 2.0 * M * N * K
     gemm_tflops = flops / (g_ms * 1e-3) / 1e12
@@ -859,7 +903,8 @@ def main():
                    "step": "quantize A + quantize B + FP4 GEMM", "parallelism": "none (1 GPU)"},
         "components": {
             "gemm": {"ms": round(g_ms, 4), "tflops": round(gemm_tflops, 1),
-                     "frac_of_fp4_peak": round(gemm_tflops / PEAK_FP4_TFLOPS, 4)},
+                     "frac_of_fp4_peak": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
+                     "frac_of_mfma_ceiling": round(gemm_tflops / ceiling["tflops"], 4)},
             "quantize_A": {"ms": round(qa_ms, 4), "gbps": round(qa_gbps, 1),
                            "frac_of_hbm_peak": round(qa_gbps / PEAK_HBM_GBPS, 4)},
             "quantize_B": {"ms": round(qb_ms, 4), "gbps": round(qb_gbps, 1),
@@ -869,6 +914,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP4_TFLOPS, 4),
                      "traffic": traffic},
         "clock": clock.summary(),
+        "mfma_ceiling": ceiling,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()

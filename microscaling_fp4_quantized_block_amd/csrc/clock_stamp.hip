@@ -9,6 +9,17 @@
 // after the timed steps, give the average shader clock over the steps of
 // every compute unit that ran a workgroup of both: d(memtime) / d(realtime)
 // times the real-time counter's rate (hipDeviceAttributeWallClockRate).
+//
+// The MFMA ceiling kernel measures the rate the chip sustains for the scaled
+// FP4 MFMA alone (v_mfma_scale_f32_32x32x64_f8f6f4, FP4 operands, unit scales)
+// on pseudo-random codes, with no memory traffic: one workgroup of four waves
+// per compute unit (its LDS request leaves room for no second one), each wave
+// cycling 16 independent accumulators over 4 x 4 operand registers, the
+// register pattern of the 256 x 256 GEMM tile.  The power drawn by random
+// operands sets the clock, so this is the practical compute ceiling of the
+// FP4 GEMM on this part, next to the nominal dense peak at 2.4 GHz.  Each
+// workgroup also stamps s_memtime and s_memrealtime around its loop, which
+// gives the clock during the run and the counter ticks per MFMA.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,7 +39,74 @@ __global__ void __launch_bounds__(64) clock_stamp_kernel(uint64_t* out) {
   out[3 * blockIdx.x + 2] = r;
 }
 
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int kCeilGroups = 256;                 // one per compute unit
+constexpr int kCeilLds = 96 * 1024;              // more than half of a compute unit's LDS
+
+__global__ void __launch_bounds__(256) mfma_ceiling_kernel(int iters, uint64_t* stamps, float* sink) {
+  extern __shared__ char lds[];
+  const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
+  v4i fa[4], fb[4];
+  for (int i = 0; i < 4; i++)
+    for (int k = 0; k < 4; k++) {
+      // two rounds of an integer hash: every nibble an arbitrary E2M1 code
+      uint32_t h = gid * 2654435761u + (uint32_t)(4 * i + k) * 40503u + 0x9e3779b9u;
+      h ^= h >> 15; h *= 0x2c1b3c6du; h ^= h >> 12; h *= 0x297a2d39u; h ^= h >> 15;
+      uint32_t g = h * 0x27d4eb2du + 0x165667b1u;
+      g ^= g >> 15; g *= 0x2c1b3c6du; g ^= g >> 12;
+      fa[i][k] = (int)h;
+      fb[i][k] = (int)g;
+    }
+  v16f acc[4][4];
+  for (int i = 0; i < 4; i++)
+    for (int j = 0; j < 4; j++) acc[i][j] = (v16f){};
+  const int unit = 0x7f7f7f7f;                   // E8M0 scale 1.0 in every byte
+  const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; it++) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const v8i a = __builtin_shufflevector(fa[i], fa[i], 0, 1, 2, 3, -1, -1, -1, -1);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const v8i b = __builtin_shufflevector(fb[j], fb[j], 0, 1, 2, 3, -1, -1, -1, -1);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 4, 4, 0, unit, 0, unit);
+      }
+    }
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  float s = 0.f;
+  for (int i = 0; i < 4; i++)
+    for (int j = 0; j < 4; j++)
+      for (int k = 0; k < 16; k++) s += acc[i][j][k];
+  sink[gid] = s;                                 // keeps every MFMA live
+  if (threadIdx.x == 0) {
+    stamps[2 * blockIdx.x] = t1 - t0;
+    stamps[2 * blockIdx.x + 1] = r1 - r0;
+  }
+  if (s == 1.2345f) lds[threadIdx.x] = 1;        // the LDS request stays in the kernel
+}
+
 extern "C" {
+
+// Sizes of the ceiling run's buffers: uint64 stamp slots and float sink slots.
+int mxclock_ceiling_stamp_slots(void) { return 2 * kCeilGroups; }
+int mxclock_ceiling_sink_slots(void) { return 256 * kCeilGroups; }
+// Scaled FP4 MFMAs (32x32x64) one launch issues, per iteration.
+long long mxclock_ceiling_mfmas_per_iter(void) { return (long long)kCeilGroups * 4 * 16; }
+
+// stamps, sink: device buffers of the sizes above.  Per workgroup, stamps
+// receives the s_memtime and s_memrealtime differences over its loop.
+int mxclock_mfma_ceiling(int iters, uint64_t* stamps, float* sink, hipStream_t stream) {
+  if (!stamps || !sink || iters <= 0) return -1;
+  if (hipFuncSetAttribute((const void*)mfma_ceiling_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kCeilLds) !=
+      hipSuccess)
+    return -5;
+  hipLaunchKernelGGL(mfma_ceiling_kernel, dim3(kCeilGroups), dim3(256), kCeilLds, stream, iters, stamps, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 
 // Number of uint64 slots one stamp writes.
 int mxclock_stamp_slots(void) { return 3 * kStampGroups; }
