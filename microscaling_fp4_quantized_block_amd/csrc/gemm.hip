@@ -1535,7 +1535,7 @@ GemmPlan plan_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
     if (s > units / min_units) s = units / min_units;
     if (s > 32) s = 32;
     // ... while the time a split saves, (1 - 1/s) of a tile's contraction at
-    // the MFMA rate one wave per SIMD reaches, exceeds what it adds: the fp32
+    // the kernel's measured MFMA rate, exceeds what it adds: the fp32
     // partials written and read back (8 s bytes per output at ~5 TB/s) and the
     // reduction's launch, ~4 us (measured: 8192 x 1024 x 2048 took 46.5 us in
     // two splits and 20.1 us whole, 4096 x 2048 x 4096 53.2 and 30.0 us,
