@@ -388,17 +388,19 @@ class ClockStamps:
                         "32-cycle scaled FP4 MFMA)"}
 
 
-def mfma_ceiling(device, launches=6, iters=30000):
-    """The scaled FP4 MFMA rate the chip sustains with no memory traffic, on
-    pseudo-random operands (libmxclock.so's ceiling kernel: one workgroup of
-    four waves per compute unit, 16 independent accumulators per wave).  Run
-    after the timed steps, back to back for ~60 ms; the last launches are
-    timed with events, and the kernel's own s_memtime / s_memrealtime stamps
-    give the clock during them and the counter ticks per MFMA."""
+def mfma_ceiling(device, kind=0, launches=6, iters=30000):
+    """The MFMA rate the chip sustains with no memory traffic, on pseudo-random
+    operands (libmxclock.so's ceiling kernel: one workgroup of four waves per
+    compute unit, 16 independent accumulators per wave).  kind 0: the scaled
+    FP4 32x32x64 MFMA of the MXFP4 GEMM; kind 1: the fp16 32x32x16 MFMA of the
+    NVFP4 GEMM.  Run back to back for ~60 ms; the last launches are timed with
+    events, and the kernel's own s_memtime / s_memrealtime stamps give the
+    clock during them and the counter ticks per MFMA."""
     import ctypes
     import torch
     lib = ctypes.CDLL(os.path.join(ROOT, "microscaling_fp4_quantized_block_amd", "libmxclock.so"))
-    lib.mxclock_mfma_ceiling.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mxclock_mfma_ceiling.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p]
     lib.mxclock_mfma_ceiling.restype = ctypes.c_int
     lib.mxclock_ceiling_mfmas_per_iter.restype = ctypes.c_longlong
     lib.mxclock_wall_rate_khz.restype = ctypes.c_int
@@ -410,24 +412,27 @@ def mfma_ceiling(device, launches=6, iters=30000):
     for i in range(launches):
         if i == launches - timed:
             ev[0].record()
-        if lib.mxclock_mfma_ceiling(iters, ctypes.c_void_p(stamps.data_ptr()), ctypes.c_void_p(sink.data_ptr()),
-                                    stream) != 0:
+        if lib.mxclock_mfma_ceiling(kind, iters, ctypes.c_void_p(stamps.data_ptr()),
+                                    ctypes.c_void_p(sink.data_ptr()), stream) != 0:
             raise RuntimeError("MFMA ceiling launch failed")
     ev[1].record()
     torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[1]) / timed
     mfmas = lib.mxclock_ceiling_mfmas_per_iter() * iters
-    tflops = mfmas * 2.0 * 32 * 32 * 64 / (ms * 1e-3) / 1e12
+    flop_per_mfma = 2.0 * 32 * 32 * (64 if kind == 0 else 16)
+    peak = PEAK_FP4_TFLOPS if kind == 0 else PEAK_FP16_TFLOPS
+    tflops = mfmas * flop_per_mfma / (ms * 1e-3) / 1e12
     st = stamps.cpu().numpy().view(np.uint64).reshape(-1, 2).astype(np.float64)
     rate_khz = lib.mxclock_wall_rate_khz()
     mhz = float(np.median(st[:, 0] / st[:, 1] * rate_khz / 1e3)) if rate_khz else None
     ticks = float(np.median(st[:, 0])) / (16.0 * iters)   # per wave: 16 MFMAs per iteration
-    return {"tflops": round(tflops, 1), "frac_of_fp4_peak": round(tflops / PEAK_FP4_TFLOPS, 4),
+    what = ("scaled FP4 MFMA 32x32x64 alone on pseudo-random codes" if kind == 0 else
+            "fp16 MFMA 32x32x16 alone on random fp16 values")
+    return {"tflops": round(tflops, 1), "frac_of_nominal_peak": round(tflops / peak, 4),
             "sclk_mhz": round(mhz, 1) if mhz else None, "ticks_per_mfma": round(ticks, 2),
             "ms_per_launch": round(ms, 3),
-            "what": "scaled FP4 MFMA 32x32x64 alone on pseudo-random codes, one workgroup of four waves per "
-                    "compute unit, no memory traffic; run after the timed steps; the clock it holds is set by "
-                    "the power of random operands"}
+            "what": what + ", one workgroup of four waves per compute unit, no memory traffic; the clock it "
+                           "holds is set by the power of random operands"}
 
 
 def cpu_model():
@@ -597,6 +602,11 @@ def sweep(args):
         return replay_time(graph_of(fn))
 
     rows = []
+
+    def add_row(r):
+        rows.append(r)
+        print("[sweep] " + " | ".join(str(v) for v in r[:5]), file=sys.stderr, flush=True)
+
     wanted = [int(c) for c in args.sweep_configs.split(",")]
     for cfg, (calls, gemms) in sweep_plan().items():
         if cfg not in wanted:
@@ -621,7 +631,7 @@ def sweep(args):
             qs[(name, rnd, axis)] = q
             nbytes = R * Cc * (2.0 + 0.5 + 1.0 / bs) + (4 if fmt == "nv" else 0)
             gbps = nbytes / t / 1e9
-            rows.append((cfg, "quantize", f"{name} {rnd} axis{axis}" + (" H" if had else ""), f"{R}x{Cc}",
+            add_row((cfg, "quantize", f"{name} {rnd} axis{axis}" + (" H" if had else ""), f"{R}x{Cc}",
                          t * 1e6, gbps, "GB/s", "hbm", gbps / PEAK_HBM_GBPS))
         for (gname, ca, cb) in gemms:
             qa, qb = qs[ca], qs[cb]
@@ -636,7 +646,7 @@ def sweep(args):
             bound_t = max(flops / (peak * 1e12), nbytes / (PEAK_HBM_GBPS * 1e9))
             bound = "mfma" if flops / (peak * 1e12) >= nbytes / (PEAK_HBM_GBPS * 1e9) else "hbm"
             tf = flops / t / 1e12
-            rows.append((cfg, "gemm", gname, f"{Mg}x{Ng}x{Kg}", t * 1e6, tf, "TFLOP/s",
+            add_row((cfg, "gemm", gname, f"{Mg}x{Ng}x{Kg}", t * 1e6, tf, "TFLOP/s",
                          bound + ("-fp16" if fmt == "nv" and bound == "mfma" else ""), bound_t / t))
             if cfg in (0, 3):
                 # the same GEMM writing bf16 (inference consumers): 2 bytes per output
@@ -645,7 +655,7 @@ def sweep(args):
                 nbytes_b = nbytes - 2.0 * Mg * Ng
                 bound_tb = max(flops / (peak * 1e12), nbytes_b / (PEAK_HBM_GBPS * 1e9))
                 bound_b = "mfma" if flops / (peak * 1e12) >= nbytes_b / (PEAK_HBM_GBPS * 1e9) else "hbm"
-                rows.append((cfg, "gemm_bf16", gname, f"{Mg}x{Ng}x{Kg}", tb * 1e6, flops / tb / 1e12, "TFLOP/s",
+                add_row((cfg, "gemm_bf16", gname, f"{Mg}x{Ng}x{Kg}", tb * 1e6, flops / tb / 1e12, "TFLOP/s",
                              bound_b, bound_tb / tb))
                 del Cb
             del C, ws
@@ -660,7 +670,7 @@ def sweep(args):
                 t = timed(lambda: mx.mxfp4_quantize_mse(x, fmt, had, 1, 2, out=q, workspace=ws), True)
                 nbytes = R * Cc * (2.0 + 0.5 + 1.0 / bs) + (4 if fmt == "nv" else 0)
                 gbps = nbytes / t / 1e9
-                rows.append((cfg, "quantize_mse", f"{name} rtn axis1" + (" H" if had else "") + (" 2 rounds" if fmt == "nv" else ""),
+                add_row((cfg, "quantize_mse", f"{name} rtn axis1" + (" H" if had else "") + (" 2 rounds" if fmt == "nv" else ""),
                              f"{R}x{Cc}", t * 1e6, gbps, "GB/s", "hbm", gbps / PEAK_HBM_GBPS))
                 del q, ws
         if cfg in (4, 5):
@@ -676,7 +686,7 @@ def sweep(args):
                 R, Cc = x.shape
                 nbytes = R * Cc * (2.0 + 0.5 + 1.0 / bs)
                 gbps = nbytes / t / 1e9
-                rows.append((cfg, "noise", f"{name} {rnd} axis{axis}", f"{R}x{Cc}", t * 1e6, gbps, "GB/s", "hbm",
+                add_row((cfg, "noise", f"{name} {rnd} axis{axis}", f"{R}x{Cc}", t * 1e6, gbps, "GB/s", "hbm",
                              gbps / PEAK_HBM_GBPS))
                 # the same sums computed while quantizing (one pass; bytes:
                 # the quantizer's, input once + codes and scales written)
@@ -686,7 +696,7 @@ def sweep(args):
                 tf = timed(lambda: mx.mxfp4_quantize_noise(x, fmt, rnd, had, axis, 5, out=qf, stats=st,
                                                            workspace=fws), True)
                 gbps_f = R * Cc * (2.0 + 0.5 + 1.0 / bs) / tf / 1e9
-                rows.append((cfg, "quantize+noise", f"{name} {rnd} axis{axis} (fused)", f"{R}x{Cc}", tf * 1e6, gbps_f,
+                add_row((cfg, "quantize+noise", f"{name} {rnd} axis{axis} (fused)", f"{R}x{Cc}", tf * 1e6, gbps_f,
                              "GB/s", "hbm", gbps_f / PEAK_HBM_GBPS))
                 del st, ws, qf, fws
         if cfg == 3:
@@ -712,7 +722,7 @@ def sweep(args):
                     mx.mxfp4_gemm(qx, qw, out=C, workspace=gws)
                 t_2 = timed(two, False)
                 for label, t in (("quantize_gemm", t_f), ("quantize, then gemm", t_2)):
-                    rows.append((cfg, "quantize+gemm", f"{gname} ({label})", f"{Mg}x{Ng}x{Kg}", t * 1e6,
+                    add_row((cfg, "quantize+gemm", f"{gname} ({label})", f"{Mg}x{Ng}x{Kg}", t * 1e6,
                                  flops / t / 1e12, "TFLOP/s", bound, bound_t / t))
                 del C, ws, gws
             # prefill up with its output quantized (rotated) for the down
@@ -733,7 +743,7 @@ def sweep(args):
             nbytes = (Mg + Ng) * Kg * (0.5 + 1.0 / 32) + Mg * Ng * (0.5 + 1.0 / 32)
             bound_t = max(flops / (PEAK_FP4_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBPS * 1e9))
             for label, t in (("epilogue", t_f), ("bf16 GEMM + quantize", t_2)):
-                rows.append((cfg, "gemm+quantize C", f"prefill up, C quantized with H ({label})", f"{Mg}x{Ng}x{Kg}",
+                add_row((cfg, "gemm+quantize C", f"prefill up, C quantized with H ({label})", f"{Mg}x{Ng}x{Kg}",
                              t * 1e6, flops / t / 1e12, "TFLOP/s", "mfma", bound_t / t))
             del qo, Cb, gws
             # the weights with a fixed grid scale (alpha = 0.75, rotated)
@@ -743,7 +753,7 @@ def sweep(args):
                 q = mx.empty_qtensor("mx", R, Cc, True, dev)
                 t = timed(lambda: mx.mxfp4_quantize_grid(x, 0.75, True, 1, out=q), True)
                 gbps = R * Cc * (2.0 + 0.5 + 1.0 / 32) / t / 1e9
-                rows.append((cfg, "quantize_grid", f"{name} alpha 0.75 H", f"{R}x{Cc}", t * 1e6, gbps, "GB/s", "hbm",
+                add_row((cfg, "quantize_grid", f"{name} alpha 0.75 H", f"{R}x{Cc}", t * 1e6, gbps, "GB/s", "hbm",
                              gbps / PEAK_HBM_GBPS))
                 del q
         if cfg == 4:
@@ -756,7 +766,7 @@ def sweep(args):
                 q = mx.empty_qtensor("mx", R, Cc, False, dev)
                 t = timed(lambda: mx.mxfp4_qema_quantize(w, m, 0.999, False, out=q), True)
                 gbps = R * Cc * (2.0 + 4.0 + 4.0 + 0.5 + 1.0 / 32) / t / 1e9
-                rows.append((cfg, "qema", f"{name} beta 0.999", f"{R}x{Cc}", t * 1e6, gbps, "GB/s", "hbm",
+                add_row((cfg, "qema", f"{name} beta 0.999", f"{R}x{Cc}", t * 1e6, gbps, "GB/s", "hbm",
                              gbps / PEAK_HBM_GBPS))
                 del m, q
         del tens, qs
@@ -765,6 +775,16 @@ def sweep(args):
              "|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
         lines.append("| %d | %s | %s | %s | %.1f | %.0f | %s | %s | %.3f |" % r)
+    # the compute ceilings the chip holds on random operands, measured right
+    # after the sweep (the GEMM rows' mfma fractions are against the nominal peaks)
+    lines += ["", "MFMA ceilings on random operands, measured right after the rows above "
+              "(`mfma_ceiling` in bench.py; no memory traffic):", "",
+              "| MFMA | TFLOP/s | frac of nominal peak | clock MHz | s_memtime ticks per MFMA |",
+              "|---|---|---|---|---|"]
+    for kind, name in ((0, "scaled FP4 32x32x64 (MXFP4 GEMM)"), (1, "fp16 32x32x16 (NVFP4 GEMM)")):
+        c = mfma_ceiling(dev, kind)
+        lines.append("| %s | %.0f | %.3f | %.0f | %.2f |" % (name, c["tflops"], c["frac_of_nominal_peak"],
+                                                             c["sclk_mhz"] or 0.0, c["ticks_per_mfma"]))
     text = "\n".join(lines) + "\n"
     if args.sweep == "-":
         print(text)

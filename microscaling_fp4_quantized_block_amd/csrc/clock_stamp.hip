@@ -12,7 +12,8 @@
 //
 // The MFMA ceiling kernel measures the rate the chip sustains for the scaled
 // FP4 MFMA alone (v_mfma_scale_f32_32x32x64_f8f6f4, FP4 operands, unit scales)
-// on pseudo-random codes, with no memory traffic: one workgroup of four waves
+// on pseudo-random codes, or for the fp16 MFMA of the NVFP4 GEMM on random
+// fp16 values, with no memory traffic: one workgroup of four waves
 // per compute unit (its LDS request leaves room for no second one), each wave
 // cycling 16 independent accumulators over 4 x 4 operand registers, the
 // register pattern of the 256 x 256 GEMM tile.  The power drawn by random
@@ -42,21 +43,34 @@ __global__ void __launch_bounds__(64) clock_stamp_kernel(uint64_t* out) {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int kCeilGroups = 256;                 // one per compute unit
 constexpr int kCeilLds = 96 * 1024;              // more than half of a compute unit's LDS
 
+// Two rounds of an integer hash of (workgroup, thread, register index).
+__device__ __forceinline__ uint32_t ceil_hash(uint32_t gid, uint32_t idx, uint32_t salt) {
+  uint32_t h = gid * 2654435761u + idx * 40503u + salt;
+  h ^= h >> 15; h *= 0x2c1b3c6du; h ^= h >> 12; h *= 0x297a2d39u; h ^= h >> 15;
+  return h;
+}
+
+// KIND 0: the scaled FP4 MFMA (32x32x64, every nibble an arbitrary E2M1
+// code, unit E8M0 scales).  KIND 1: the fp16 MFMA (32x32x16) that the NVFP4
+// GEMM runs on, every operand a random fp16 in [1, 2) with a random sign, so
+// that products and sums stay finite.
+template <int KIND>
 __global__ void __launch_bounds__(256) mfma_ceiling_kernel(int iters, uint64_t* stamps, float* sink) {
   extern __shared__ char lds[];
   const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
   v4i fa[4], fb[4];
   for (int i = 0; i < 4; i++)
     for (int k = 0; k < 4; k++) {
-      // two rounds of an integer hash: every nibble an arbitrary E2M1 code
-      uint32_t h = gid * 2654435761u + (uint32_t)(4 * i + k) * 40503u + 0x9e3779b9u;
-      h ^= h >> 15; h *= 0x2c1b3c6du; h ^= h >> 12; h *= 0x297a2d39u; h ^= h >> 15;
-      uint32_t g = h * 0x27d4eb2du + 0x165667b1u;
-      g ^= g >> 15; g *= 0x2c1b3c6du; g ^= g >> 12;
+      uint32_t h = ceil_hash(gid, 4 * i + k, 0x9e3779b9u), g = ceil_hash(gid, 4 * i + k, 0x165667b1u);
+      if (KIND == 1) {   // two fp16 per word: sign, exponent 15 (2^0), random 10-bit mantissa
+        h = (h & 0x83FF83FFu) | 0x3C003C00u;
+        g = (g & 0x83FF83FFu) | 0x3C003C00u;
+      }
       fa[i][k] = (int)h;
       fb[i][k] = (int)g;
     }
@@ -68,11 +82,16 @@ __global__ void __launch_bounds__(256) mfma_ceiling_kernel(int iters, uint64_t* 
   for (int it = 0; it < iters; it++) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const v8i a = __builtin_shufflevector(fa[i], fa[i], 0, 1, 2, 3, -1, -1, -1, -1);
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        const v8i b = __builtin_shufflevector(fb[j], fb[j], 0, 1, 2, 3, -1, -1, -1, -1);
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 4, 4, 0, unit, 0, unit);
+        if constexpr (KIND == 0) {
+          const v8i a = __builtin_shufflevector(fa[i], fa[i], 0, 1, 2, 3, -1, -1, -1, -1);
+          const v8i b = __builtin_shufflevector(fb[j], fb[j], 0, 1, 2, 3, -1, -1, -1, -1);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 4, 4, 0, unit, 0, unit);
+        } else {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, fa[i]),
+                                                             __builtin_bit_cast(v8h, fb[j]), acc[i][j], 0, 0, 0);
+        }
       }
     }
   }
@@ -89,6 +108,16 @@ __global__ void __launch_bounds__(256) mfma_ceiling_kernel(int iters, uint64_t* 
   if (s == 1.2345f) lds[threadIdx.x] = 1;        // the LDS request stays in the kernel
 }
 
+template <int KIND>
+static int launch_ceiling(int iters, uint64_t* stamps, float* sink, hipStream_t stream) {
+  if (!stamps || !sink || iters <= 0) return -1;
+  if (hipFuncSetAttribute((const void*)mfma_ceiling_kernel<KIND>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kCeilLds) != hipSuccess)
+    return -5;
+  hipLaunchKernelGGL(mfma_ceiling_kernel<KIND>, dim3(kCeilGroups), dim3(256), kCeilLds, stream, iters, stamps, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
 extern "C" {
 
 // Sizes of the ceiling run's buffers: uint64 stamp slots and float sink slots.
@@ -99,13 +128,12 @@ long long mxclock_ceiling_mfmas_per_iter(void) { return (long long)kCeilGroups *
 
 // stamps, sink: device buffers of the sizes above.  Per workgroup, stamps
 // receives the s_memtime and s_memrealtime differences over its loop.
-int mxclock_mfma_ceiling(int iters, uint64_t* stamps, float* sink, hipStream_t stream) {
-  if (!stamps || !sink || iters <= 0) return -1;
-  if (hipFuncSetAttribute((const void*)mfma_ceiling_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kCeilLds) !=
-      hipSuccess)
-    return -5;
-  hipLaunchKernelGGL(mfma_ceiling_kernel, dim3(kCeilGroups), dim3(256), kCeilLds, stream, iters, stamps, sink);
-  return hipGetLastError() == hipSuccess ? 0 : -5;
+// kind 0: scaled FP4 32x32x64 (FLOP per MFMA 2 * 32 * 32 * 64); kind 1: fp16
+// 32x32x16 (2 * 32 * 32 * 16).
+int mxclock_mfma_ceiling(int kind, int iters, uint64_t* stamps, float* sink, hipStream_t stream) {
+  if (kind == 0) return launch_ceiling<0>(iters, stamps, sink, stream);
+  if (kind == 1) return launch_ceiling<1>(iters, stamps, sink, stream);
+  return -1;
 }
 
 // Number of uint64 slots one stamp writes.

@@ -103,3 +103,16 @@ def test_sweep_plan_covers_every_configuration():
     for cfg in (4, 5):
         kinds = {g[0].split()[-1] for g in plan[cfg][1]}
         assert kinds == {"fwd", "dgrad", "wgrad"}
+
+
+def test_clock_library_exports_what_bench_calls():
+    """libmxclock.so (the benchmark's clock stamps and MFMA ceiling run) loads
+    on the CPU and exports every function bench.py calls."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "microscaling_fp4_quantized_block_amd", "libmxclock.so"))
+    for name in ("mxclock_stamp", "mxclock_stamp_slots", "mxclock_wall_rate_khz", "mxclock_mfma_ceiling",
+                 "mxclock_ceiling_stamp_slots", "mxclock_ceiling_sink_slots", "mxclock_ceiling_mfmas_per_iter"):
+        assert hasattr(lib, name), name
+    lib.mxclock_ceiling_mfmas_per_iter.restype = ctypes.c_longlong
+    assert lib.mxclock_ceiling_mfmas_per_iter() == 256 * 4 * 16
+    assert lib.mxclock_ceiling_stamp_slots() == 512
