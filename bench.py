@@ -499,6 +499,69 @@ def _training_gemms(triples):
     return calls, gemms
 
 
+class GraphTimer:
+    """GPU time of one call from HIP graphs of `inner` back-to-back calls
+    (replays cost no Python, ctypes or event time per call): the graph is
+    replayed back to back for ~30 ms first (from idle the clock needs ~10 ms
+    of load to settle), then the median of `reps` timed replays, per call.
+    With evict_first, each call is preceded by a 512 MiB write that evicts the
+    MALL, and that write's own time (timed the same way) is subtracted."""
+
+    inner = 8
+
+    def __init__(self, device, reps):
+        import torch
+        self.torch = torch
+        self.reps = reps
+        self.evict = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=device)
+        self.t_evict = self.replay_time(self.graph_of(lambda: self.evict.fill_(1.0)))
+
+    def graph_of(self, fn):
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(self.inner):
+                fn()
+        torch.cuda.synchronize()
+        return g
+
+    def replay_time(self, g):
+        torch = self.torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        for _ in range(min(5000, int(30.0 / max(e0.elapsed_time(e1), 1e-3)) + 1)):
+            g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for i in range(self.reps + 2):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts)) * 1e-3 / self.inner
+
+    def timed(self, fn, evict_first):
+        """Seconds per call of fn."""
+        if evict_first:
+            def both():
+                self.evict.fill_(1.0)
+                fn()
+            return max(self.replay_time(self.graph_of(both)) - self.t_evict, 1e-7)
+        return self.replay_time(self.graph_of(fn))
+
+
 def sweep_plan():
     plan = {}
     c = [("X", "rtn", 1), ("W", "rtn", 1)]
@@ -528,7 +591,6 @@ def sweep(args):
     import workloads
     import microscaling_fp4_quantized_block_amd as mx
     dev = torch.device("cuda", 0)
-    evict = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
     gen = torch.Generator(device=dev)
 
     def draw(cfg, name):
@@ -547,59 +609,8 @@ def sweep(args):
                 x[:, ch] *= kw.get("outlier_scale", 50.0)
         return x.to(torch.bfloat16)
 
-    inner = 8
-
-    def graph_of(fn):
-        """`inner` back-to-back calls of fn captured into one HIP graph
-        (replays cost no Python or ctypes time per call)."""
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            fn()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(inner):
-                fn()
-        torch.cuda.synchronize()
-        return g
-
-    def replay_time(g):
-        # from idle the clock needs ~10 ms of load to settle: replay the graph
-        # back to back for about 30 ms before timing it
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        for _ in range(min(5000, int(30.0 / max(e0.elapsed_time(e1), 1e-3)) + 1)):
-            g.replay()
-        torch.cuda.synchronize()
-        ts = []
-        for i in range(args.sweep_reps + 2):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            if i >= 2:
-                ts.append(e0.elapsed_time(e1))
-        return float(np.median(ts)) * 1e-3 / inner
-
-    g_evict = graph_of(lambda: evict.fill_(1.0))
-    t_evict = replay_time(g_evict)
-
-    def timed(fn, evict_first):
-        """GPU time of one call: graphs of back-to-back calls (each after a
-        512 MiB MALL eviction, whose own time is subtracted, for quantizer
-        calls)."""
-        if evict_first:
-            def both():
-                evict.fill_(1.0)
-                fn()
-            return max(replay_time(graph_of(both)) - t_evict, 1e-7)
-        return replay_time(graph_of(fn))
+    gt = GraphTimer(dev, args.sweep_reps)
+    timed = gt.timed
 
     rows = []
 
@@ -858,25 +869,20 @@ def main():
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     # ev: events recorded on the launch stream (torch's current stream, which
-    # the binding passes to the library) around the GEMM, and with `parts`
-    # also around each quantizer call
-    def step(ev=None, parts=False):
-        if parts:
-            ev[0].record()
+    # the binding passes to the library) around the GEMM
+    def step(ev=None):
         mx.mxfp4_quantize(A, "mx", "rtn", False, 1, 0, out=qa)
-        if parts:
-            ev[1].record()
         mx.mxfp4_quantize(B, "mx", "rtn", False, 1, 0, out=qb)
         if ev is not None:
-            ev[2].record()
+            ev[0].record()
         mx.mxfp4_gemm(qa, qb, out=C, workspace=ws)
         if ev is not None:
-            ev[3].record()
+            ev[1].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    new_events = lambda: [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    new_events = lambda: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     events = new_events()
     clock = ClockStamps(dev)
     torch.cuda.synchronize()
@@ -888,16 +894,15 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    g_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
-    # the quantizer components: the same steps again after the timed region,
-    # with events between the calls (each event pair adds a few microseconds
-    # to a step, so the timed steps carry only the GEMM's)
-    part_events = new_events()
-    for i in range(args.steps):
-        step(part_events[i], parts=True)
-    torch.cuda.synchronize()
-    qa_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in part_events]))
-    qb_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in part_events]))
+    g_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    # the quantizer components, after the timed region: each call timed as in
+    # the sweep (HIP graphs of 8 back-to-back calls, each after a 512 MiB write
+    # that evicts the MALL as the step's GEMM does, that write's time
+    # subtracted), so no event or launch gap is counted in a kernel's rate
+    gt = GraphTimer(dev, 10)
+    qa_ms = 1e3 * gt.timed(lambda: mx.mxfp4_quantize(A, "mx", "rtn", False, 1, 0, out=qa), True)
+    qb_ms = 1e3 * gt.timed(lambda: mx.mxfp4_quantize(B, "mx", "rtn", False, 1, 0, out=qb), True)
+    del gt
     ceiling = mfma_ceiling(dev)
 
     flops = 2.0 * M * N * K
